@@ -1,0 +1,322 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test fixes one part of the oracle by something independent of its code:
+a brute-force evaluation of the definition on tiny inputs, a library routine
+(torch's scaled_dot_product_attention, torch's float8 cast), closed forms and
+special cases with a known answer, and the numbers the pages print.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_synth import make_inputs, oracle_args
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _rand_case(rng, H=4, L=37, d_c=32, d_nope=24, d_r=16, d_v=20):
+    """Random float64 case with every width distinct, so a transposed or
+    swapped operand cannot pass silently on shape alone."""
+    return dict(
+        c_kv=rng.standard_normal((L, d_c)),
+        k_rope=rng.standard_normal((L, d_r)),
+        q_nope=rng.standard_normal((H, d_nope)),
+        q_rope=rng.standard_normal((H, d_r)),
+        w_uk=rng.standard_normal((H, d_nope, d_c)) / math.sqrt(d_c),
+        w_uv=rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c),
+        sm_scale=1.0 / math.sqrt(d_nope + d_r),
+    )
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(np.ravel(a - b)) / np.linalg.norm(np.ravel(b)))
+
+
+# --- P1: absorbed and non-absorbed forms agree --------------------------------
+
+def test_absorbed_equals_nonabsorbed_tiny_workload():
+    inp = make_inputs("tiny")
+    a = oracle_args(inp)
+    c_kv, k_rope = oracle.gather_rows(a["cache"], 0, int(inp.seq_lens[0]))
+    o1, l1 = oracle.attend_nonabsorbed(c_kv, k_rope, a["q_nope"][0], a["q_rope"][0],
+                                       a["w_uk"], a["w_uv"], a["sm_scale"])
+    o2, l2, _ = oracle.attend_absorbed(c_kv, k_rope, a["q_nope"][0], a["q_rope"][0],
+                                       a["w_uk"], a["w_uv"], a["sm_scale"])
+    assert _rel(o1, o2) <= 1e-5
+    assert _rel(o1, o2) <= 1e-12          # holds far below the required 1e-5
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_absorbed_equals_nonabsorbed_dsv2_shapes():
+    inp = make_inputs("dsv2_b32_l4096", batch=1, seq_lens=[77])
+    a = oracle_args(inp)
+    c_kv, k_rope = oracle.gather_rows(a["cache"], 0, 77)
+    o1, l1 = oracle.attend_nonabsorbed(c_kv, k_rope, a["q_nope"][0], a["q_rope"][0],
+                                       a["w_uk"], a["w_uv"], a["sm_scale"])
+    o2, l2, _ = oracle.attend_absorbed(c_kv, k_rope, a["q_nope"][0], a["q_rope"][0],
+                                       a["w_uk"], a["w_uv"], a["sm_scale"])
+    assert _rel(o1, o2) <= 1e-12
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+# --- P2: brute force from the definition, pure Python ------------------------
+
+def _brute_force(case):
+    """Attention evaluated straight from the definition with Python floats:
+    k_{j,h}[i] = sum_c W_UK[h][i][c] c_j[c], then [k; k^R]; v likewise with
+    W_UV and no rotary part; p_j = exp(s_j) / sum exp(s_i) without any max
+    subtraction; o = sum_j p_j v_j; lse = log sum exp(s_i)."""
+    c_kv = case["c_kv"].tolist()
+    k_rope = case["k_rope"].tolist()
+    w_uk = case["w_uk"].tolist()
+    w_uv = case["w_uv"].tolist()
+    L = len(c_kv)
+    out, lses = [], []
+    for h in range(len(w_uk)):
+        q = case["q_nope"][h].tolist() + case["q_rope"][h].tolist()
+        scores, values = [], []
+        for j in range(L):
+            k = [math.fsum(w_uk[h][i][c] * c_kv[j][c] for c in range(len(c_kv[j])))
+                 for i in range(len(w_uk[h]))] + k_rope[j]
+            v = [math.fsum(w_uv[h][i][c] * c_kv[j][c] for c in range(len(c_kv[j])))
+                 for i in range(len(w_uv[h]))]
+            scores.append(case["sm_scale"] * math.fsum(a * b for a, b in zip(q, k)))
+            values.append(v)
+        e = [math.exp(s) for s in scores]
+        z = math.fsum(e)
+        out.append([math.fsum(e[j] / z * values[j][i] for j in range(L))
+                    for i in range(len(values[0]))])
+        lses.append(math.log(z))
+    return np.array(out), np.array(lses)
+
+
+def test_oracle_matches_brute_force_definition():
+    case = _rand_case(np.random.default_rng(11))
+    o_bf, l_bf = _brute_force(case)
+    o, l = oracle.attend_nonabsorbed(**case)
+    np.testing.assert_allclose(o, o_bf, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l, l_bf, rtol=1e-13, atol=0)
+    # the softmax weights sum to one: recover them from a constant value row
+    case1 = dict(case)
+    case1["w_uv"] = np.zeros_like(case["w_uv"])
+    assert np.all(oracle.attend_nonabsorbed(**case1)[0] == 0)
+
+
+# --- P3: per-head attention equals a library routine ---------------------------
+
+def test_oracle_matches_torch_sdpa():
+    case = _rand_case(np.random.default_rng(5), H=3, L=53)
+    o, lse = oracle.attend_nonabsorbed(**case)
+    c = torch.from_numpy(case["c_kv"])
+    for h in range(3):
+        kc = c @ torch.from_numpy(case["w_uk"][h]).T              # [L, d_nope]
+        k = torch.cat([kc, torch.from_numpy(case["k_rope"])], 1)  # [L, d_nope + d_r]
+        v = c @ torch.from_numpy(case["w_uv"][h]).T               # [L, d_v]
+        q = torch.cat([torch.from_numpy(case["q_nope"][h]), torch.from_numpy(case["q_rope"][h])])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[None, None, None], k[None, None], v[None, None], scale=case["sm_scale"])
+        np.testing.assert_allclose(o[h], ref[0, 0, 0].numpy(), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[h], torch.logsumexp(case["sm_scale"] * (k @ q), 0).item(),
+                                   rtol=1e-14, atol=0)
+
+
+# --- P4: closed forms printed on the pages -------------------------------------
+
+def test_closed_forms_match_printed_numbers():
+    items = {it["name"]: it for it in json.load(open(GOLDEN))["items"]}
+    it = items["mla_cache_elements_per_token_per_layer"]
+    assert oracle.cache_elements_per_token(**it["inputs"]) == it["value"]
+    it = items["mha_elements_per_token_per_layer"]
+    assert oracle.mha_elements_per_token(**it["inputs"]) == it["value"]
+    it = items["gqa_equivalent_groups"]
+    d_h = it["inputs"]["d_h"]
+    g = oracle.gqa_equivalent_groups(it["inputs"]["d_c_over_d_h"] * d_h,
+                                     int(it["inputs"]["d_rope_over_d_h"] * d_h), d_h)
+    assert g == it["value"]
+    it = items["kv_cache_reduction_vs_deepseek_67b_percent"]
+    x = it["inputs"]
+    red = oracle.kv_reduction_vs_gqa_model(512, 64, x["mla_layers"], x["mla_bits"],
+                                           x["gqa_groups"], x["d_h"], x["gqa_layers"],
+                                           x["gqa_bits"])
+    assert round(100 * red, it["rounding"]) == it["value"]
+    # the same ratio without the cache quantisation is far from the printed value
+    red16 = oracle.kv_reduction_vs_gqa_model(512, 64, 60, 16, 8, 128, 95, 16)
+    assert abs(100 * red16 - 82.2) < 0.05
+
+
+def test_bf16_row_bytes():
+    # 576 bf16 elements per token: 1152 bytes; the fp8 layout keeps 512 one-byte
+    # codes, a 64-wide bf16 rotary key and one fp32 scale: 644 bytes.
+    assert oracle.cache_elements_per_token(512, 64) * 2 == 1152
+    inp = make_inputs("fp8_b128_l8192", batch=1, seq_lens=[3])
+    assert inp.cache_bytes() == 3 * 644
+
+
+# --- P5-P7: special cases with a closed-form answer -----------------------------
+
+def test_single_token_returns_projected_latent():
+    case = _rand_case(np.random.default_rng(1), L=1)
+    o, lse = oracle.attend_nonabsorbed(**case)
+    for h in range(case["w_uv"].shape[0]):
+        np.testing.assert_allclose(o[h], case["w_uv"][h] @ case["c_kv"][0], rtol=1e-13, atol=1e-15)
+        s0 = case["sm_scale"] * (np.dot(case["w_uk"][h] @ case["c_kv"][0], case["q_nope"][h])
+                                 + np.dot(case["k_rope"][0], case["q_rope"][h]))
+        assert abs(lse[h] - s0) <= 1e-13 * max(1.0, abs(s0))
+
+
+def test_zero_query_is_uniform_average():
+    case = _rand_case(np.random.default_rng(2), L=29)
+    case["q_nope"][:] = 0
+    case["q_rope"][:] = 0
+    o, lse = oracle.attend_nonabsorbed(**case)
+    mean_c = case["c_kv"].mean(axis=0)
+    for h in range(o.shape[0]):
+        np.testing.assert_allclose(o[h], case["w_uv"][h] @ mean_c, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(29), rtol=1e-14)
+
+
+def test_identical_rows_give_that_row():
+    case = _rand_case(np.random.default_rng(3), L=17)
+    case["c_kv"][:] = case["c_kv"][4]
+    case["k_rope"][:] = case["k_rope"][4]
+    o, lse = oracle.attend_nonabsorbed(**case)
+    for h in range(o.shape[0]):
+        np.testing.assert_allclose(o[h], case["w_uv"][h] @ case["c_kv"][0], rtol=1e-12, atol=1e-14)
+
+
+def test_very_large_scale_selects_argmax_row():
+    case = _rand_case(np.random.default_rng(4), L=23)
+    case["sm_scale"] = 1e4
+    o, _ = oracle.attend_nonabsorbed(**case)
+    for h in range(o.shape[0]):
+        s = (case["c_kv"] @ (case["w_uk"][h].T @ case["q_nope"][h])
+             + case["k_rope"] @ case["q_rope"][h])
+        j = int(np.argmax(s))
+        np.testing.assert_allclose(o[h], case["w_uv"][h] @ case["c_kv"][j], rtol=1e-9, atol=1e-12)
+
+
+def test_empty_cache():
+    case = _rand_case(np.random.default_rng(4), L=0)
+    o, lse = oracle.attend_nonabsorbed(**case)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# --- P8: token order does not matter (pins the paged gather) ----------------------
+
+def test_permutation_invariance():
+    case = _rand_case(np.random.default_rng(6), L=41)
+    o, lse = oracle.attend_nonabsorbed(**case)
+    perm = np.random.default_rng(7).permutation(41)
+    case["c_kv"] = case["c_kv"][perm]
+    case["k_rope"] = case["k_rope"][perm]
+    o2, lse2 = oracle.attend_nonabsorbed(**case)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-14)
+
+
+def test_paged_and_contiguous_layouts_agree():
+    lens = [130, 64, 1, 77]
+    a = oracle_args(make_inputs("dsv2_b32_l4096", batch=4, seq_lens=lens, pad_fill=float("nan")))
+    p = oracle_args(make_inputs("dsv2_b32_l4096", batch=4, seq_lens=lens, layout="paged",
+                                page_size=64, pad_fill=float("nan")))
+    assert p["cache"]["block_table"].shape == (4, 3)
+    o1, l1 = oracle.decode(**a)
+    o2, l2 = oracle.decode(**p)
+    assert np.all(np.isfinite(o1))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_token_rows_paged_mapping():
+    bt = np.array([[5, 2, 7], [0, 1, 3]], dtype=np.int32)
+    rows = oracle.mla.token_rows(0, 10, block_table=bt, page_size=4)
+    assert rows.tolist() == [20, 21, 22, 23, 8, 9, 10, 11, 28, 29]
+    rows = oracle.mla.token_rows(1, 3, seq_stride=100)
+    assert rows.tolist() == [100, 101, 102]
+
+
+# --- P9: split-KV with log-sum-exp merge equals the unsplit result ---------------
+
+@pytest.mark.parametrize("bounds", [[0, 60], [0, 1, 60], [0, 13, 13, 40, 60], [0, 30, 60, 60]])
+def test_split_merge_invariance(bounds):
+    case = _rand_case(np.random.default_rng(8), L=60)
+    o, lse = oracle.attend_nonabsorbed(**case)
+    o2, lse2 = oracle.attend_split(bounds=bounds, **case)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13)
+
+
+def test_merge_of_only_empty_parts():
+    o, lse = oracle.lse_merge(np.zeros((3, 2, 5)), np.full((3, 2), -np.inf))
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# --- P10: e4m3 codec ----------------------------------------------------------
+
+def test_e4m3_table_against_definition_values():
+    t = oracle.e4m3_table()
+    assert t[0x7E] == 448.0                # largest finite
+    assert t[0x08] == 2.0 ** -6            # smallest normal
+    assert t[0x01] == 2.0 ** -9            # smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9        # largest subnormal
+    assert t[0x38] == 1.0
+    assert t[0x3C] == 1.5
+    assert t[0xB8] == -1.0
+    assert t[0x80] == 0.0 and math.copysign(1.0, t[0x80]) == -1.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.sum(np.isnan(t)) == 2
+
+
+def test_e4m3_decode_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.decode_e4m3(np.arange(256))
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e4m3_encode_matches_torch_cast():
+    t = oracle.e4m3_table()
+    finite = t[np.isfinite(t)]
+    mids = (np.sort(finite)[1:] + np.sort(finite)[:-1]) / 2      # exact ties
+    x = np.concatenate([np.linspace(-448, 448, 100001), finite, mids,
+                        mids * (1 + 1e-6), mids * (1 - 1e-6), [0.0, -0.0, 1e-30, -1e-30]])
+    # torch rounds a float64 source to float32 before the fp8 cast, so compare
+    # on float32 inputs, which is what the cache quantiser feeds it.
+    x = x.astype(np.float32)
+    got = oracle.encode_e4m3(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, ref)
+    # saturation beyond the range (torch's cast does not saturate; clamp first)
+    assert oracle.encode_e4m3(np.array([1e6, -500.0])).tolist() == [0x7E, 0xFE]
+
+
+def test_e4m3_quantised_cache_matches_codec():
+    inp = make_inputs("fp8_b128_l8192", batch=1, seq_lens=[40])
+    codes = inp.codes.numpy()
+    scale = inp.scale.numpy().astype(np.float64)
+    c = inp.rows[:40, :512].double().numpy()
+    # the quantiser divides in float32
+    y = (inp.rows[:40, :512].float() / inp.scale[:40, None]).double().numpy()
+    np.testing.assert_array_equal(oracle.encode_e4m3(y), codes[:40])
+    assert np.all((codes[:40] & 0x7F).max(axis=1) == 0x7E)   # the absmax element -> 448
+    deq = oracle.decode_e4m3(codes[:40]) * scale[:40, None]
+    # e4m3 keeps 3 mantissa bits: relative error at most 2^-4 for normals
+    big = np.abs(c) > 2.0 ** -6 * scale[:40, None]
+    assert np.all(np.abs(deq - c)[big] <= 2.0 ** -4 * np.abs(c)[big])
+
+
+# --- softmax scales of the workloads ---------------------------------------------
+
+def test_workload_softmax_scales():
+    assert make_inputs("tiny").sm_scale == pytest.approx(1 / math.sqrt(48), rel=1e-15)
+    assert make_inputs("dsv2_b32_l4096", batch=1, seq_lens=[2]).sm_scale == \
+        pytest.approx(1 / math.sqrt(192), rel=1e-15)
+    long = make_inputs("long_b4_l131072", batch=1, seq_lens=[2]).sm_scale
+    assert long == pytest.approx(0.0987910, abs=5e-8)
