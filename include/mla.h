@@ -1,0 +1,186 @@
+/*
+ * libmla — Multi-head Latent Attention (MLA) decode over a latent KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is MLA as defined in the DeepSeek-V2 paper (Chinese translation
+ * of the paper), section 2.1:
+ *   - 2.1.2 low-rank key-value joint compression: each cached token keeps one
+ *     latent c_KV of width d_c instead of per-head keys and values; keys and
+ *     values are the up-projections W_UK c_KV and W_UV c_KV, and at inference
+ *     W_UK can be folded into the query side and W_UV into the output side;
+ *   - 2.1.3 decoupled RoPE: a rotary key k^R of width d_h^R, shared by all
+ *     heads, is cached beside c_KV; a head's score is [q^C; q^R]·[k^C; k^R].
+ * With both foldings a decode step for one layer is, per sequence b and head h:
+ *   q_lat[b,h]  = [ W_UK[h]^T q_nope[b,h] ; q_rope[b,h] ]          (absorb)
+ *   s_j         = sm_scale * q_lat[b,h] · row_j,  row_j = [c_KV_j ; k^R_j]
+ *   o_lat[b,h]  = sum_j softmax(s)_j c_KV_j,  lse = log sum_j exp(s_j)  (decode)
+ *   o[b,h]      = W_UV[h] o_lat[b,h]                              (out-proj)
+ * Long caches may be cut into splits whose normalised partial results are
+ * merged by log-sum-exp (combine).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller; the
+ *     library allocates nothing and keeps no state except a thread-local copy
+ *     of the last HIP error. Pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on
+ *     it and the call returns without synchronising.
+ *   - Arguments are validated on the host before anything is enqueued. On any
+ *     failure nothing is enqueued and a negative mla_status is returned; the
+ *     library never aborts and never throws across this boundary.
+ *   - Layouts are dense row-major with the last index fastest.
+ *   - Supported head shapes (H, d_latent, d_rope, d_nope, d_v) and dtypes:
+ *       (128, 512, 64, 128, 128): MLA_BF16 tensors, cache MLA_BF16 or MLA_FP8_E4M3
+ *       (4, 32, 16, 32, 32):      MLA_F32 everywhere
+ *     Anything else returns MLA_ERR_UNSUPPORTED.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mla_status;
+#define MLA_OK               0
+#define MLA_ERR_NULL        (-1)  /* a required pointer is NULL                     */
+#define MLA_ERR_SHAPE       (-2)  /* a size is negative, zero where it must not be,
+                                     or inconsistent with another                 */
+#define MLA_ERR_DTYPE       (-3)  /* unknown dtype or unsupported dtype combination */
+#define MLA_ERR_UNSUPPORTED (-4)  /* head shape outside the compiled set           */
+#define MLA_ERR_ALIGN       (-5)  /* a pointer or stride breaks 16-byte alignment   */
+#define MLA_ERR_HIP         (-6)  /* a HIP call failed; see mla_last_hip_error()    */
+
+#define MLA_F32       0
+#define MLA_BF16      1
+#define MLA_FP8_E4M3  2   /* OCP e4m3 ("e4m3fn"): bias 7, max 448, no infinities */
+
+typedef void* mla_stream;   /* a hipStream_t */
+
+typedef struct {
+  int32_t num_heads;   /* H                                  */
+  int32_t d_latent;    /* d_c: width of c_KV                 */
+  int32_t d_rope;      /* d_h^R: width of the rotary key     */
+  int32_t d_nope;      /* per-head width of q^C and k^C      */
+  int32_t d_v;         /* per-head width of v^C              */
+} mla_dims;
+
+/*
+ * The latent cache of one layer (DeepSeek-V2 paper, section 2.1.3: one
+ * (d_c + d_h^R)-element row per cached token).
+ *
+ * Token j of sequence b lives in physical row r(b, j):
+ *   contiguous (page_size == 0): r = b * seq_stride + j
+ *   paged      (page_size  > 0): r = block_table[b * max_pages_per_seq + j / page_size]
+ *                                    * page_size + j % page_size
+ * dtype MLA_BF16 / MLA_F32: `latent` holds rows of d_latent + d_rope elements,
+ *   c_KV first then k^R, consecutive rows `row_stride` elements apart.
+ * dtype MLA_FP8_E4M3: `latent` holds rows of d_latent e4m3 codes (`row_stride`
+ *   bytes apart); `rope` holds bf16 rows of d_rope elements (`rope_stride`
+ *   elements apart); `scale` holds one fp32 per row; c_KV = code * scale.
+ * Only rows of tokens j < seq_lens[b] are read; padding rows and the unused
+ * tail of a sequence's last page may hold anything (NaN included).
+ * page_size must be a power of two; block-table entries past a sequence's
+ * last page are never read.
+ */
+typedef struct {
+  int32_t dtype;
+  const void* latent;
+  const void* rope;                /* fp8 only, else NULL                 */
+  const float* scale;              /* fp8 only, else NULL                 */
+  int64_t row_stride;              /* elements (bytes for fp8 codes)      */
+  int64_t rope_stride;             /* fp8 only: elements                  */
+  int32_t page_size;               /* 0 = contiguous                      */
+  int64_t seq_stride;              /* contiguous only: rows per sequence  */
+  const int32_t* block_table;      /* paged only: [batch, max_pages_per_seq] */
+  int32_t max_pages_per_seq;       /* paged only                          */
+} mla_kv_cache;
+
+/*
+ * Absorb W_UK into the query (DeepSeek-V2 paper, section 2.1.2, final
+ * sentences on absorption; concatenation with the rotary query from 2.1.3).
+ *   q_nope [B, H, d_nope], q_rope [B, H, d_rope] (RoPE already applied),
+ *   w_uk   [H, d_nope, d_latent] (the (d_nope * H) x d_latent matrix W_UK with
+ *          its rows grouped by head),
+ *   q_lat  [B, H, d_latent + d_rope] (output):
+ *          q_lat[b,h,:d_latent] = sum_n q_nope[b,h,n] * w_uk[h,n,:],
+ *          q_lat[b,h,d_latent:] = q_rope[b,h,:].
+ * dtype: MLA_BF16 (bf16 in and out, fp32 accumulation) or MLA_F32.
+ * batch == 0 is a no-op.
+ */
+mla_status mla_absorb_q(const mla_dims* dims, int32_t batch,
+                        const void* q_nope, const void* q_rope, const void* w_uk,
+                        void* q_lat, int32_t dtype, mla_stream stream);
+
+/*
+ * Attention of one query token per sequence over the latent cache, absorbed
+ * form (DeepSeek-V2 paper, sections 2.1.2-2.1.3); softmax in fp32.
+ *   q_lat    [B, H, d_latent + d_rope], bf16 for a bf16/fp8 cache, f32 for f32.
+ *   seq_lens [B] int32 device array; a length outside [0, max_seq_len] is
+ *            clamped to that range.
+ *   sm_scale multiplies q_lat·row before the softmax (1/sqrt(d_nope + d_rope)
+ *            times any length-extension factor).
+ *   num_splits S >= 1 cuts the token range [0, max_seq_len) into S chunks
+ *            of mla_split_chunk(max_seq_len, S) tokens; each (b, split) is
+ *            computed independently.
+ *   S == 1: out [B, H, d_latent] in out_dtype (MLA_BF16 or MLA_F32),
+ *           lse [B, H] f32 (natural log).
+ *   S  > 1: out [B, S, H, d_latent] f32 partials, each normalised over its
+ *           own chunk; lse [B, S, H] f32. Merge them with mla_combine.
+ * A sequence (or chunk) with no tokens yields out = 0 and lse = -inf.
+ */
+mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat,
+                      const mla_kv_cache* cache, const int32_t* seq_lens,
+                      int32_t max_seq_len, float sm_scale, int32_t num_splits,
+                      void* out, float* lse, int32_t out_dtype, mla_stream stream);
+
+/*
+ * Log-sum-exp merge of split partials (the split-KV pass of mla_decode):
+ *   lse[b,h] = log sum_s exp(lse_part[b,s,h]),
+ *   out[b,h] = sum_s exp(lse_part[b,s,h] - lse[b,h]) * o_part[b,s,h,:].
+ * Parts with lse = -inf contribute nothing; if all do, out = 0, lse = -inf.
+ *   o_part [B, S, H, d_latent] f32, lse_part [B, S, H] f32,
+ *   out [B, H, d_latent] in out_dtype (MLA_BF16 or MLA_F32), lse [B, H] f32
+ *   (lse may be NULL when not wanted).
+ */
+mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t num_splits,
+                       const float* o_part, const float* lse_part, void* out,
+                       float* lse, int32_t out_dtype, mla_stream stream);
+
+/*
+ * Apply W_UV on the output side (DeepSeek-V2 paper, section 2.1.2: W_UV
+ * absorbed into the output projection).
+ *   o_lat [B, H, d_latent] in o_dtype (MLA_BF16 or MLA_F32),
+ *   w_uv  [H, d_v, d_latent] in w_dtype (the (d_v * H) x d_latent matrix W_UV
+ *         with its rows grouped by head),
+ *   out   [B, H, d_v] in out_dtype:  out[b,h,v] = sum_c w_uv[h,v,c] * o_lat[b,h,c].
+ * bf16 weights: the product runs on bf16 inputs (an f32 o_lat is rounded to
+ * bf16 first) with fp32 accumulation. f32 weights need f32 o_lat.
+ */
+mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const void* o_lat,
+                        int32_t o_dtype, const void* w_uv, int32_t w_dtype,
+                        void* out, int32_t out_dtype, mla_stream stream);
+
+/* Tokens per split chunk that mla_decode uses for (max_seq_len, num_splits):
+ * ceil(max_seq_len / num_splits) rounded up to a multiple of 32. */
+int32_t mla_split_chunk(int32_t max_seq_len, int32_t num_splits);
+
+/* A split count for mla_decode: chunks of about total_tokens / num_cus tokens
+ * (at least 256), so that the non-empty (sequence, split) items spread evenly
+ * over `num_cus` compute units. total_tokens <= 0 means batch * max_seq_len.
+ * Returns at least 1 and at most the largest count mla_combine accepts. */
+int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tokens,
+                           int32_t num_cus);
+
+/* Static, never-NULL description of a status code. */
+const char* mla_status_string(mla_status status);
+
+/* hipError_t of the last call on this thread that returned MLA_ERR_HIP. */
+int32_t mla_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,191 @@
+"""Python binding of libmla, the MI355X MLA latent-cache decode library.
+
+Argument marshalling only: every function hands device pointers, sizes and
+the current HIP stream to the C ABI declared in include/mla.h; all the
+arithmetic runs in the library's HIP kernels. PyTorch supplies device memory
+and streams. If libmla.so has not been built, or the tensors are not on a
+GPU, the calls raise instead of computing anything elsewhere.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+_STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
+           -4: "MLA_ERR_UNSUPPORTED", -5: "MLA_ERR_ALIGN", -6: "MLA_ERR_HIP"}
+
+# Every symbol include/mla.h declares.
+EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_split_chunk",
+           "mla_suggest_splits", "mla_status_string", "mla_last_hip_error")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = "%s failed: %s (%s)" % (where, _STATUS.get(status, status), status_string(status))
+        if status == -6:
+            msg += ", hipError_t %d" % last_hip_error()
+        super().__init__(msg)
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("latent", ctypes.c_void_p), ("rope", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("row_stride", ctypes.c_int64),
+                ("rope_stride", ctypes.c_int64), ("page_size", ctypes.c_int32),
+                ("seq_stride", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+                ("max_pages_per_seq", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmla.so is not built; run `python -m mla_latent_kv_28_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        pd = ctypes.POINTER(Dims)
+        L.mla_absorb_q.argtypes = [pd, i32, vp, vp, vp, vp, i32, vp]
+        L.mla_decode.argtypes = [pd, i32, vp, ctypes.POINTER(KVCache), vp, i32, f32, i32, vp, vp, i32, vp]
+        L.mla_combine.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, vp]
+        L.mla_out_proj.argtypes = [pd, i32, vp, i32, vp, i32, vp, i32, vp]
+        L.mla_split_chunk.argtypes = [i32, i32]
+        L.mla_suggest_splits.argtypes = [i32, i32, i64, i32]
+        L.mla_status_string.argtypes = [i32]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_last_hip_error.argtypes = []
+        for name in ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_split_chunk",
+                     "mla_suggest_splits", "mla_last_hip_error"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def dims_of(d):
+    """ctypes Dims from any object with num_heads, d_latent, d_rope, d_nope, d_v."""
+    return Dims(d.num_heads, d.d_latent, d.d_rope, d.d_nope, d.d_v)
+
+
+_TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+def _dev(t, name, dtype=None, numel=None):
+    """Device pointer of a GPU tensor (None -> NULL) after layout checks."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a torch tensor on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s holds %d elements, needs %d" % (name, t.numel(), numel))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status, where):
+    if status != 0:
+        raise MLAError(status, where)
+
+
+def mla_absorb_q(dims, batch, q_nope, q_rope, w_uk, q_lat, dtype, stream=None):
+    d = dims_of(dims)
+    td = _TORCH_DTYPE[dtype]
+    H = d.num_heads
+    st = lib().mla_absorb_q(
+        ctypes.byref(d), batch,
+        _dev(q_nope, "q_nope", td, batch * H * d.d_nope),
+        _dev(q_rope, "q_rope", td, batch * H * d.d_rope),
+        _dev(w_uk, "w_uk", td, H * d.d_nope * d.d_latent),
+        _dev(q_lat, "q_lat", td, batch * H * (d.d_latent + d.d_rope)),
+        dtype, _stream(stream))
+    _check(st, "mla_absorb_q")
+
+
+def kv_cache(dtype, latent, rope=None, scale=None, row_stride=None, rope_stride=0, page_size=0,
+             seq_stride=0, block_table=None, max_pages_per_seq=0):
+    """An mla_kv_cache describing GPU tensors (kept alive by the caller)."""
+    if row_stride is None:
+        row_stride = latent.shape[-1]
+    return KVCache(dtype, _dev(latent, "latent"), _dev(rope, "rope", torch.bfloat16),
+                   _dev(scale, "scale", torch.float32), row_stride, rope_stride, page_size,
+                   seq_stride, _dev(block_table, "block_table", torch.int32), max_pages_per_seq)
+
+
+def mla_decode(dims, batch, q_lat, cache, seq_lens, max_seq_len, sm_scale, num_splits, out, lse,
+               out_dtype, stream=None):
+    d = dims_of(dims)
+    H = d.num_heads
+    q_dtype = torch.float32 if cache.dtype == F32 else torch.bfloat16
+    parts = num_splits if num_splits > 1 else 1
+    st = lib().mla_decode(
+        ctypes.byref(d), batch,
+        _dev(q_lat, "q_lat", q_dtype, batch * H * (d.d_latent + d.d_rope)),
+        ctypes.byref(cache),
+        _dev(seq_lens, "seq_lens", torch.int32, batch),
+        max_seq_len, float(sm_scale), num_splits,
+        _dev(out, "out", _TORCH_DTYPE.get(out_dtype), batch * parts * H * d.d_latent),
+        _dev(lse, "lse", torch.float32, batch * parts * H),
+        out_dtype, _stream(stream))
+    _check(st, "mla_decode")
+
+
+def mla_combine(dims, batch, num_splits, o_part, lse_part, out, lse, out_dtype, stream=None):
+    d = dims_of(dims)
+    H = d.num_heads
+    st = lib().mla_combine(
+        ctypes.byref(d), batch, num_splits,
+        _dev(o_part, "o_part", torch.float32, batch * num_splits * H * d.d_latent),
+        _dev(lse_part, "lse_part", torch.float32, batch * num_splits * H),
+        _dev(out, "out", _TORCH_DTYPE.get(out_dtype), batch * H * d.d_latent),
+        _dev(lse, "lse", torch.float32, batch * H),
+        out_dtype, _stream(stream))
+    _check(st, "mla_combine")
+
+
+def mla_out_proj(dims, batch, o_lat, o_dtype, w_uv, w_dtype, out, out_dtype, stream=None):
+    d = dims_of(dims)
+    H = d.num_heads
+    st = lib().mla_out_proj(
+        ctypes.byref(d), batch,
+        _dev(o_lat, "o_lat", _TORCH_DTYPE.get(o_dtype), batch * H * d.d_latent), o_dtype,
+        _dev(w_uv, "w_uv", _TORCH_DTYPE.get(w_dtype), H * d.d_v * d.d_latent), w_dtype,
+        _dev(out, "out", _TORCH_DTYPE.get(out_dtype), batch * H * d.d_v), out_dtype,
+        _stream(stream))
+    _check(st, "mla_out_proj")
+
+
+def mla_split_chunk(max_seq_len, num_splits):
+    return lib().mla_split_chunk(max_seq_len, num_splits)
+
+
+def mla_suggest_splits(batch, max_seq_len, total_tokens, num_cus):
+    return lib().mla_suggest_splits(batch, max_seq_len, total_tokens, num_cus)
+
+
+def status_string(status):
+    return lib().mla_status_string(status).decode()
+
+
+def last_hip_error():
+    return lib().mla_last_hip_error()

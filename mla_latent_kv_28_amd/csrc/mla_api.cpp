@@ -1,0 +1,231 @@
+// libmla C ABI: argument validation, dispatch to the compiled head shapes,
+// status reporting. Nothing here allocates or synchronises.
+#include "../../include/mla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "mla_internal.h"
+
+namespace mla {
+int combine_max_splits();
+}
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+enum class Shape { kNone, kDsv2, kTiny };
+
+Shape shape_of(const mla_dims* d) {
+  if (d->num_heads == 128 && d->d_latent == 512 && d->d_rope == 64 && d->d_nope == 128 && d->d_v == 128)
+    return Shape::kDsv2;
+  if (d->num_heads == 4 && d->d_latent == 32 && d->d_rope == 16 && d->d_nope == 32 && d->d_v == 32)
+    return Shape::kTiny;
+  return Shape::kNone;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int64_t x) { int k = 0; while ((int64_t(1) << k) < x) ++k; return k; }
+
+mla_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  g_last_hip_error = static_cast<int32_t>(e);
+  return MLA_ERR_HIP;
+}
+
+bool valid_dtype(int32_t t) { return t == MLA_F32 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_split_chunk(int32_t max_seq_len, int32_t num_splits) {
+  if (num_splits < 1 || max_seq_len <= 0) return 0;
+  const int64_t c = (static_cast<int64_t>(max_seq_len) + num_splits - 1) / num_splits;
+  return static_cast<int32_t>((c + 31) / 32 * 32);
+}
+
+int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tokens, int32_t num_cus) {
+  if (batch <= 0 || max_seq_len <= 0 || num_cus <= 0) return 1;
+  if (total_tokens <= 0) total_tokens = static_cast<int64_t>(batch) * max_seq_len;
+  // Aim for about one (sequence, split) item of equal length per compute unit,
+  // with chunks of at least 256 tokens.
+  int64_t chunk = (total_tokens + num_cus - 1) / num_cus;
+  if (chunk < 256) chunk = 256;
+  int64_t s = (max_seq_len + chunk - 1) / chunk;
+  if (s < 1) s = 1;
+  if (s > mla::combine_max_splits()) s = mla::combine_max_splits();
+  return static_cast<int32_t>(s);
+}
+
+const char* mla_status_string(mla_status status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "a size is negative, zero where it must not be, or inconsistent";
+    case MLA_ERR_DTYPE: return "unknown dtype or unsupported dtype combination";
+    case MLA_ERR_UNSUPPORTED: return "head shape outside the compiled set";
+    case MLA_ERR_ALIGN: return "a pointer or stride is not 16-byte aligned";
+    case MLA_ERR_HIP: return "a HIP call failed (see mla_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int32_t mla_last_hip_error(void) { return g_last_hip_error; }
+
+mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_nope, const void* q_rope,
+                        const void* w_uk, void* q_lat, int32_t dtype, mla_stream stream) {
+  if (dims == nullptr) return MLA_ERR_NULL;
+  if (batch < 0) return MLA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  const Shape sh = shape_of(dims);
+  if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
+  if ((sh == Shape::kDsv2 && dtype != MLA_BF16) || (sh == Shape::kTiny && dtype != MLA_F32))
+    return MLA_ERR_DTYPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !w_uk || !q_lat) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(q_lat))
+    return MLA_ERR_ALIGN;
+  mla::GemmParams p{};
+  p.a = q_nope;
+  p.w = w_uk;
+  p.c = q_lat;
+  p.lda = dims->d_nope;
+  p.ldc = dims->d_latent + dims->d_rope;
+  p.batch = batch;
+  p.heads = dims->num_heads;
+  p.a_f32 = dtype == MLA_F32;
+  p.c_f32 = dtype == MLA_F32;
+  p.tail = q_rope;
+  p.n_tail = dims->d_rope;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(sh == Shape::kDsv2 ? mla::launch_absorb_dsv2_bf16(p, s)
+                                       : mla::launch_absorb_tiny_f32(p, s));
+}
+
+mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_kv_cache* cache,
+                      const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, int32_t num_splits,
+                      void* out, float* lse, int32_t out_dtype, mla_stream stream) {
+  if (dims == nullptr || cache == nullptr) return MLA_ERR_NULL;
+  if (batch < 0 || max_seq_len < 0 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (!valid_dtype(cache->dtype) || (out_dtype != MLA_F32 && out_dtype != MLA_BF16)) return MLA_ERR_DTYPE;
+  const Shape sh = shape_of(dims);
+  if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
+  if (sh == Shape::kDsv2 && cache->dtype == MLA_F32) return MLA_ERR_DTYPE;
+  if (sh == Shape::kTiny && cache->dtype != MLA_F32) return MLA_ERR_DTYPE;
+  if (num_splits > 1 && out_dtype != MLA_F32) return MLA_ERR_DTYPE;   // partials are f32
+  if (!std::isfinite(sm_scale)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!q_lat || !seq_lens || !out || !lse || !cache->latent) return MLA_ERR_NULL;
+  const bool fp8 = cache->dtype == MLA_FP8_E4M3;
+  if (fp8 && (!cache->rope || !cache->scale)) return MLA_ERR_NULL;
+  const bool paged = cache->page_size > 0;
+  if (cache->page_size < 0) return MLA_ERR_SHAPE;
+  if (paged) {
+    if (!cache->block_table) return MLA_ERR_NULL;
+    if (!is_pow2(cache->page_size)) return MLA_ERR_SHAPE;
+    const int64_t need = (static_cast<int64_t>(max_seq_len) + cache->page_size - 1) / cache->page_size;
+    if (cache->max_pages_per_seq < need) return MLA_ERR_SHAPE;
+  } else if (cache->seq_stride < max_seq_len) {
+    return MLA_ERR_SHAPE;
+  }
+  const int64_t width = fp8 ? dims->d_latent : dims->d_latent + dims->d_rope;
+  if (cache->row_stride < width) return MLA_ERR_SHAPE;
+  const int64_t elem = cache->dtype == MLA_F32 ? 4 : (fp8 ? 1 : 2);
+  if ((cache->row_stride * elem) % 16 != 0) return MLA_ERR_ALIGN;
+  if (fp8) {
+    if (cache->rope_stride < dims->d_rope) return MLA_ERR_SHAPE;
+    if ((cache->rope_stride * 2) % 16 != 0) return MLA_ERR_ALIGN;
+    if (!aligned16(cache->rope)) return MLA_ERR_ALIGN;
+  }
+  if (!aligned16(q_lat) || !aligned16(cache->latent) || !aligned16(out) || !aligned16(lse))
+    return MLA_ERR_ALIGN;
+  if (static_cast<int64_t>(batch) * num_splits > 0x7fffffff) return MLA_ERR_SHAPE;
+
+  mla::DecodeParams p{};
+  p.q_lat = q_lat;
+  p.latent = cache->latent;
+  p.rope = cache->rope;
+  p.scale = cache->scale;
+  p.row_stride = cache->row_stride;
+  p.rope_stride = cache->rope_stride;
+  p.seq_stride = cache->seq_stride;
+  p.block_table = cache->block_table;
+  p.max_pages = cache->max_pages_per_seq;
+  p.page_shift = paged ? log2i(cache->page_size) : -1;
+  p.seq_lens = seq_lens;
+  p.batch = batch;
+  p.max_seq_len = max_seq_len;
+  p.num_splits = num_splits;
+  p.chunk = mla_split_chunk(max_seq_len, num_splits);
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.out = out;
+  p.lse = lse;
+  p.out_bf16 = out_dtype == MLA_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (sh == Shape::kTiny) e = mla::launch_decode_tiny_f32(p, s);
+  else if (fp8) e = mla::launch_decode_dsv2_fp8(p, s);
+  else e = mla::launch_decode_dsv2_bf16(p, s);
+  return hip_status(e);
+}
+
+mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const float* o_part,
+                       const float* lse_part, void* out, float* lse, int32_t out_dtype, mla_stream stream) {
+  if (dims == nullptr) return MLA_ERR_NULL;
+  if (batch < 0 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (shape_of(dims) == Shape::kNone) return MLA_ERR_UNSUPPORTED;
+  if (num_splits > mla::combine_max_splits()) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!o_part || !lse_part || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(out)) return MLA_ERR_ALIGN;
+  mla::CombineParams p{};
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.out = out;
+  p.lse = lse;
+  p.batch = batch;
+  p.splits = num_splits;
+  p.heads = dims->num_heads;
+  p.d_latent = dims->d_latent;
+  p.out_bf16 = out_dtype == MLA_BF16;
+  return hip_status(mla::launch_combine(p, static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const void* o_lat, int32_t o_dtype,
+                        const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype, mla_stream stream) {
+  if (dims == nullptr) return MLA_ERR_NULL;
+  if (batch < 0) return MLA_ERR_SHAPE;
+  if (!valid_dtype(o_dtype) || !valid_dtype(w_dtype) || !valid_dtype(out_dtype)) return MLA_ERR_DTYPE;
+  const Shape sh = shape_of(dims);
+  if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
+  if (o_dtype == MLA_FP8_E4M3 || out_dtype == MLA_FP8_E4M3) return MLA_ERR_DTYPE;
+  if (sh == Shape::kDsv2 && w_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (sh == Shape::kTiny && (w_dtype != MLA_F32 || o_dtype != MLA_F32 || out_dtype != MLA_F32))
+    return MLA_ERR_DTYPE;
+  if (batch == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  mla::GemmParams p{};
+  p.a = o_lat;
+  p.w = w_uv;
+  p.c = out;
+  p.lda = dims->d_latent;
+  p.ldc = dims->d_v;
+  p.batch = batch;
+  p.heads = dims->num_heads;
+  p.a_f32 = o_dtype == MLA_F32;
+  p.c_f32 = out_dtype == MLA_F32;
+  p.tail = nullptr;
+  p.n_tail = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(sh == Shape::kDsv2 ? mla::launch_outproj_dsv2_bf16(p, s)
+                                       : mla::launch_outproj_tiny_f32(p, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Host-side launch interface between the C ABI (mla_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum CacheKind : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+struct DecodeParams {
+  const void* q_lat;            // [B, H, DC + DR]
+  const void* latent;           // cache rows (see mla_kv_cache)
+  const void* rope;             // fp8 only
+  const float* scale;           // fp8 only
+  int64_t row_stride;           // elements (bytes for fp8 codes)
+  int64_t rope_stride;          // fp8 only, elements
+  int64_t seq_stride;           // contiguous only
+  const int32_t* block_table;   // paged only
+  int32_t max_pages;
+  int32_t page_shift;           // log2(page_size); -1 = contiguous
+  const int32_t* seq_lens;      // [B]
+  int32_t batch;
+  int32_t max_seq_len;          // lengths are clamped to [0, max_seq_len]
+  int32_t num_splits;
+  int32_t chunk;                // tokens per split, multiple of the tile
+  float scale_log2;             // sm_scale * log2(e)
+  void* out;                    // S == 1: [B, H, DC] (bf16 | f32); S > 1: [B, S, H, DC] f32
+  float* lse;                   // S == 1: [B, H]; S > 1: [B, S, H]
+  int32_t out_bf16;             // S == 1 only
+  int32_t xcd_remap;            // 1: keep a sequence's splits on one XCD
+};
+
+// Decode launchers: return the hipError_t of the launch.
+hipError_t launch_decode_dsv2_bf16(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_dsv2_fp8(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_tiny_f32(const DecodeParams& p, hipStream_t s);
+
+struct CombineParams {
+  const float* o_part;   // [B, S, H, DC]
+  const float* lse_part; // [B, S, H]
+  void* out;             // [B, H, DC]
+  float* lse;            // [B, H] or null
+  int32_t batch, splits, heads, d_latent;
+  int32_t out_bf16;
+};
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+
+// Per-head batched GEMM: C[b, h, n] = sum_k A[b, h, k] * Bm_h(k, n).
+struct GemmParams {
+  const void* a;         // [B, H, lda] (bf16 or f32)
+  const void* w;         // absorb: [H, K, N]; out-proj: [H, N, K]
+  void* c;               // [B, H, ldc]
+  int64_t lda, ldc;      // elements per (b, h) row
+  int32_t batch, heads;
+  int32_t a_f32;         // A is f32 (bf16 weights: rounded to bf16 on load)
+  int32_t c_f32;         // C is written as f32 (else bf16)
+  // absorb only: copy this [B, H, n_tail] tensor into C[:, :, N:N + n_tail]
+  const void* tail;
+  int32_t n_tail;
+};
+hipError_t launch_absorb_dsv2_bf16(const GemmParams& p, hipStream_t s);
+hipError_t launch_absorb_tiny_f32(const GemmParams& p, hipStream_t s);
+hipError_t launch_outproj_dsv2_bf16(const GemmParams& p, hipStream_t s);
+hipError_t launch_outproj_tiny_f32(const GemmParams& p, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments with the documented status before any GPU
+work is enqueued. No kernel is launched here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import mla_latent_kv_28_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+# The argument-error cases below pass fake (never dereferenced) pointers. On a
+# machine with a GPU a validation bug could turn one into a launch, so they run
+# on GPU-less hosts only.
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer cases run without a GPU")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mla.LIB_PATH):
+        from mla_latent_kv_28_amd import build
+        build.build()
+    return mla.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj"):
+        assert n in names
+    assert set(names) == set(mla.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = mla.status_string(code)
+        assert s and s != "unknown status"
+    assert mla.status_string(-99) == "unknown status"
+    assert mla.last_hip_error() == 0
+
+
+def test_split_chunk(L):
+    assert mla.mla_split_chunk(4096, 8) == 512
+    assert mla.mla_split_chunk(131072, 64) == 2048
+    assert mla.mla_split_chunk(100, 3) == 64          # ceil(100/3) = 34 -> 64
+    assert mla.mla_split_chunk(1, 1) == 32
+    assert mla.mla_split_chunk(0, 4) == 0
+    assert mla.mla_split_chunk(100, 0) == 0
+
+
+def test_suggest_splits(L):
+    assert mla.mla_suggest_splits(32, 4096, 0, 256) == 8       # 256 items of 512 tokens
+    assert mla.mla_suggest_splits(4, 131072, 0, 256) == 64     # 2048-token chunks
+    assert mla.mla_suggest_splits(512, 4096, 0, 256) == 1
+    assert mla.mla_suggest_splits(1, 100, 0, 256) == 1         # chunks of at least 256
+    assert mla.mla_suggest_splits(0, 100, 0, 256) == 1
+    s = mla.mla_suggest_splits(64, 32768, 64 * 16640, 256)
+    assert 1 <= s <= 1024 and mla.mla_split_chunk(32768, s) >= 256
+
+
+DSV2 = mla.Dims(128, 512, 64, 128, 128)
+TINY = mla.Dims(4, 32, 16, 32, 32)
+P = 1 << 20          # a fake, aligned, non-null address: never dereferenced
+
+
+def _cache(**kw):
+    c = dict(dtype=mla.BF16, latent=P, rope=None, scale=None, row_stride=576, rope_stride=0,
+             page_size=0, seq_stride=4096, block_table=None, max_pages_per_seq=0)
+    c.update(kw)
+    return mla.KVCache(*[c[f] for f, _ in mla.KVCache._fields_])
+
+
+def _decode(L, dims=DSV2, batch=1, q=P, cache=None, lens=P, max_len=4096, scale=0.07, splits=1,
+            out=P, lse=P, out_dtype=mla.BF16):
+    cache = _cache() if cache is None else cache
+    d = ctypes.byref(dims) if dims is not None else None
+    return L.mla_decode(d, batch, q, ctypes.byref(cache), lens, max_len, scale, splits, out, lse,
+                        out_dtype, None)
+
+
+@no_gpu
+def test_decode_argument_errors(L):
+    assert L.mla_decode(None, 1, P, None, P, 1, 1.0, 1, P, P, 1, None) == -1
+    assert _decode(L, batch=-1) == -2
+    assert _decode(L, max_len=-1) == -2
+    assert _decode(L, splits=0) == -2
+    assert _decode(L, scale=float("nan")) == -2
+    assert _decode(L, dims=mla.Dims(64, 512, 64, 128, 128)) == -4
+    assert _decode(L, cache=_cache(dtype=7)) == -3
+    assert _decode(L, cache=_cache(dtype=mla.F32)) == -3          # f32 cache needs the tiny shape
+    assert _decode(L, dims=TINY, cache=_cache(dtype=mla.BF16, row_stride=48, seq_stride=64),
+                   max_len=64) == -3
+    assert _decode(L, splits=4, out_dtype=mla.BF16) == -3          # partials are f32
+    assert _decode(L, out_dtype=mla.FP8_E4M3) == -3
+    assert _decode(L, q=None) == -1
+    assert _decode(L, lens=None) == -1
+    assert _decode(L, out=None) == -1
+    assert _decode(L, lse=None) == -1
+    assert _decode(L, cache=_cache(latent=None)) == -1
+    assert _decode(L, cache=_cache(dtype=mla.FP8_E4M3, row_stride=512, rope=P, scale=None,
+                                   rope_stride=64)) == -1
+    assert _decode(L, cache=_cache(page_size=64, block_table=None, max_pages_per_seq=64)) == -1
+    assert _decode(L, cache=_cache(page_size=48, block_table=P, max_pages_per_seq=100)) == -2
+    assert _decode(L, cache=_cache(page_size=64, block_table=P, max_pages_per_seq=63)) == -2
+    assert _decode(L, cache=_cache(seq_stride=4095)) == -2
+    assert _decode(L, cache=_cache(row_stride=575)) == -2
+    assert _decode(L, cache=_cache(row_stride=580)) == -5          # rows must stay 16-byte aligned
+    assert _decode(L, q=P + 2) == -5
+    assert _decode(L, out=P + 8) == -5
+    assert _decode(L, cache=_cache(latent=P + 4)) == -5
+    assert _decode(L, batch=0) == 0                                 # empty batch: nothing to do
+
+
+@no_gpu
+def test_absorb_combine_outproj_argument_errors(L):
+    d = ctypes.byref(DSV2)
+    assert L.mla_absorb_q(None, 1, P, P, P, P, mla.BF16, None) == -1
+    assert L.mla_absorb_q(d, -1, P, P, P, P, mla.BF16, None) == -2
+    assert L.mla_absorb_q(d, 1, P, P, P, P, mla.F32, None) == -3
+    assert L.mla_absorb_q(d, 1, P, None, P, P, mla.BF16, None) == -1
+    assert L.mla_absorb_q(d, 1, P, P, P + 2, P, mla.BF16, None) == -5
+    assert L.mla_absorb_q(ctypes.byref(mla.Dims(128, 512, 64, 64, 128)), 1, P, P, P, P,
+                          mla.BF16, None) == -4
+    assert L.mla_absorb_q(d, 0, None, None, None, None, mla.BF16, None) == 0
+
+    assert L.mla_combine(None, 1, 2, P, P, P, P, mla.F32, None) == -1
+    assert L.mla_combine(d, 1, 0, P, P, P, P, mla.F32, None) == -2
+    assert L.mla_combine(d, 1, 2000, P, P, P, P, mla.F32, None) == -4
+    assert L.mla_combine(d, 1, 2, P, P, P, P, mla.FP8_E4M3, None) == -3
+    assert L.mla_combine(d, 1, 2, None, P, P, P, mla.F32, None) == -1
+    assert L.mla_combine(d, 1, 2, P + 4, P, P, P, mla.F32, None) == -5
+
+    assert L.mla_out_proj(None, 1, P, mla.BF16, P, mla.BF16, P, mla.BF16, None) == -1
+    assert L.mla_out_proj(d, 1, P, mla.BF16, P, mla.F32, P, mla.BF16, None) == -3
+    assert L.mla_out_proj(d, 1, P, mla.FP8_E4M3, P, mla.BF16, P, mla.BF16, None) == -3
+    assert L.mla_out_proj(ctypes.byref(TINY), 1, P, mla.BF16, P, mla.F32, P, mla.F32, None) == -3
+    assert L.mla_out_proj(d, 1, None, mla.BF16, P, mla.BF16, P, mla.BF16, None) == -1
+    assert L.mla_out_proj(d, 1, P, mla.BF16, P, mla.BF16, P + 2, mla.BF16, None) == -5
+    assert L.mla_out_proj(d, 0, None, mla.BF16, None, mla.BF16, None, mla.BF16, None) == 0
+
+
+def test_binding_refuses_host_tensors(L):
+    # the binding never hands a host pointer to the library
+    x = torch.zeros(4)
+    with pytest.raises(TypeError):
+        mla.mla_absorb_q(TINY, 1, x, x, x, x, mla.F32)

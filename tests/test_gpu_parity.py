@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case draws one seeded input, runs libmla's absorb -> decode -> combine
+-> out-proj on the GPU and the float64 non-absorbed oracle on the host, and
+compares element by element. Bounds: relative L2 <= 1e-2 and max abs <= 3e-2
+for bf16 with fp32 accumulation; relative L2 <= 4e-2 for the fp8 cache
+against the bf16 oracle; the fp32 tiny workload is held to 1e-4 (its only
+rounding is fp32 arithmetic over 64 tokens).
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_synth import make_inputs, oracle_args
+
+pytestmark = pytest.mark.gpu
+
+BF16_REL, BF16_ABS, FP8_REL, F32_REL = 1e-2, 3e-2, 4e-2, 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_latent_kv_28_amd as mla
+    mla.lib()     # fails loudly when the library is missing
+
+
+def _run(inp, **kw):
+    from mla_latent_kv_28_amd.pipeline import DecodePipeline
+    print("case: %s B=%d lens=%s splits=%s" % (inp.name, inp.batch, inp.seq_lens[:8].tolist(),
+                                                kw.get("num_splits")), flush=True)
+    pipe = DecodePipeline(inp, **kw)
+    out, lse = pipe.run()
+    torch.cuda.synchronize()
+    return pipe, out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def _rel(x, y):
+    den = np.linalg.norm(y.ravel())
+    return float(np.linalg.norm((x - y).ravel()) / (den if den > 0 else 1.0))
+
+
+def _check(out, ref, rel, absb=None):
+    assert np.all(np.isfinite(out))
+    r = _rel(out, ref)
+    m = float(np.abs(out - ref).max()) if out.size else 0.0
+    print("rel_l2 %.3e max_abs %.3e (max|ref| %.3e)" % (r, m, float(np.abs(ref).max())), flush=True)
+    assert r <= rel
+    if absb is not None:
+        assert m <= absb
+
+
+def _lse_check(lse, ref_lse, tol):
+    """|lse - ref| <= tol + 4e-3 |ref|: the absorbed query is rounded to bf16
+    (relative error 2^-9 per element), so large scores carry a proportional
+    absolute error."""
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.all(lse[~fin] == -np.inf)
+    if fin.any():
+        d = np.abs(lse[fin] - ref_lse[fin])
+        print("lse max abs err %.3e" % d.max(), flush=True)
+        assert np.all(d <= tol + 4e-3 * np.abs(ref_lse[fin]))
+
+
+# --- the tiny fp32 workload (batch 1, 64 tokens, 4 heads) ------------------------
+
+def test_tiny_fp32_full_pipeline():
+    inp = make_inputs("tiny")
+    _, out, lse = _run(inp)
+    ref, ref_lse = oracle.decode(**oracle_args(inp))
+    _check(out, ref, F32_REL)
+    _lse_check(lse, ref_lse, 1e-4)
+    # absorbed and non-absorbed agreement, the workload's own check
+    _check(out, ref, BF16_REL, BF16_ABS)
+
+
+@pytest.mark.parametrize("lens,splits", [([1], 1), ([33], 1), ([64], 4), ([0], 1), ([50], 2)])
+def test_tiny_fp32_lengths_and_splits(lens, splits):
+    inp = make_inputs("tiny", seq_lens=lens, seq_stride=64, pad_fill=float("nan"))
+    _, out, lse = _run(inp, num_splits=splits)
+    ref, ref_lse = oracle.decode(**oracle_args(inp))
+    if lens[0] == 0:
+        assert np.all(out == 0) and np.all(lse == -np.inf)
+        return
+    _check(out, ref, F32_REL)
+    _lse_check(lse, ref_lse, 1e-4)
+
+
+# --- DeepSeek-V2 shapes, small batches that span several tiles and a ragged tail ----
+
+RAGGED = [1, 77, 1000, 32, 513]
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8])
+def test_dsv2_bf16_contiguous_ragged(splits):
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=RAGGED, pad_fill=float("nan"))
+    _, out, lse = _run(inp, num_splits=splits)
+    ref, ref_lse = oracle.decode(**oracle_args(inp))
+    _check(out, ref, BF16_REL, BF16_ABS)
+    _lse_check(lse, ref_lse, 2e-2)
+
+
+def test_dsv2_bf16_latent_output_matches_oracle_latent_sum():
+    # the decode output before W_UV, against the oracle's softmax-weighted latent sum
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=[300, 45])
+    pipe, _, _ = _run(inp, num_splits=1, o_lat_dtype=0, out_dtype=0)
+    o_lat = pipe.o_lat.double().cpu().numpy()
+    a = oracle_args(inp)
+    for b in range(2):
+        c_kv, k_rope = oracle.gather_rows(a["cache"], b, int(inp.seq_lens[b]))
+        _, _, ref_lat = oracle.attend_absorbed(c_kv, k_rope, a["q_nope"][b], a["q_rope"][b],
+                                               a["w_uk"], a["w_uv"], a["sm_scale"])
+        _check(o_lat[b], ref_lat, BF16_REL, BF16_ABS)
+
+
+def test_dsv2_paged_equals_contiguous_and_oracle():
+    lens = [130, 64, 1, 700, 0, 191]
+    common = dict(seq_lens=lens, pad_fill=float("nan"))
+    cont = make_inputs("dsv2_b32_l4096", **common)
+    paged = make_inputs("dsv2_b32_l4096", layout="paged", page_size=64, **common)
+    _, out_c, lse_c = _run(cont, num_splits=2)
+    _, out_p, lse_p = _run(paged, num_splits=2)
+    assert np.array_equal(out_c, out_p) and np.array_equal(lse_c, lse_p)
+    ref, ref_lse = oracle.decode(**oracle_args(paged))
+    _check(out_p, ref, BF16_REL, BF16_ABS)
+    _lse_check(lse_p, ref_lse, 2e-2)
+    assert np.all(out_p[4] == 0)
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 128])
+def test_dsv2_paged_other_page_sizes(page_size):
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=[200, 33], layout="paged", page_size=page_size,
+                      pad_fill=float("nan"))
+    _, out, _ = _run(inp, num_splits=1)
+    ref, _ = oracle.decode(**oracle_args(inp))
+    _check(out, ref, BF16_REL, BF16_ABS)
+
+
+def test_dsv2_peaked_attention():
+    # q x 30: logits spread over tens of units, so the reference maximum of the
+    # first tile is overtaken and the recompute path runs
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=[900, 257], q_scale=30.0)
+    _, out, lse = _run(inp, num_splits=1)
+    ref, ref_lse = oracle.decode(**oracle_args(inp))
+    _check(out, ref, BF16_REL)
+    _lse_check(lse, ref_lse, 5e-2)
+
+
+def test_dsv2_rising_scores_force_recompute():
+    # later tokens score far above the first tile: each new maximum exceeds the
+    # first tile's by more than the exponent headroom
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=[200])
+    rows = inp.rows.float()
+    ramp = torch.linspace(0.0, 12.0, 200)[:, None]
+    rows[:200, :512] = rows[:200, :512] * (1.0 + ramp)
+    inp.rows = rows.to(torch.bfloat16)
+    inp.q_nope = (inp.q_nope.float() * 40).to(torch.bfloat16)
+    _, out, lse = _run(inp, num_splits=1)
+    ref, ref_lse = oracle.decode(**oracle_args(inp))
+    _check(out, ref, BF16_REL)
+    _lse_check(lse, ref_lse, 5e-2)
+
+
+def test_dsv2_long_split_small():
+    inp = make_inputs("long_b4_l131072", batch=1, seq_lens=[5000])
+    _, out, lse = _run(inp, num_splits=64)
+    ref, ref_lse = oracle.decode(**oracle_args(inp))
+    _check(out, ref, BF16_REL, BF16_ABS)
+    _lse_check(lse, ref_lse, 2e-2)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_dsv2_fp8_against_both_oracles(splits):
+    inp = make_inputs("fp8_b128_l8192", seq_lens=[600, 97, 1])
+    _, out, lse = _run(inp, num_splits=splits)
+    ref_q, ref_q_lse = oracle.decode(**oracle_args(inp, "dequantised"))
+    ref_b, _ = oracle.decode(**oracle_args(inp, "bf16"))
+    _check(out, ref_q, BF16_REL, BF16_ABS)
+    _lse_check(lse, ref_q_lse, 2e-2)
+    _check(out, ref_b, FP8_REL)
+
+
+def test_bf16_final_output_dtype():
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=[100, 40])
+    _, out, _ = _run(inp, num_splits=2, o_lat_dtype=1, out_dtype=1)
+    ref, _ = oracle.decode(**oracle_args(inp))
+    _check(out, ref, BF16_REL, BF16_ABS)
+
+
+def test_determinism():
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=[700, 333, 64])
+    _, o1, l1 = _run(inp, num_splits=4)
+    _, o2, l2 = _run(inp, num_splits=4)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# --- full workload sizes, in the launch configuration the benchmark times ---------
+
+def _sampled(inp, out, lse, pairs, rel, absb=None, fp8_reference="dequantised"):
+    a = oracle_args(inp, fp8_reference)
+    for b, h in pairs:
+        ro, rl = oracle.decode_one(b=b, h=h, **a)
+        _check(out[b, h], ro, rel, absb)
+        assert abs(lse[b, h] - rl) <= 2e-2 + 4e-3 * abs(rl)
+
+
+def _pairs(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(n)] + [(B - 1, H - 1), (0, 0)]
+
+
+def test_full_dsv2_b32_l4096():
+    inp = make_inputs("dsv2_b32_l4096")
+    _, out, lse = _run(inp)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    _sampled(inp, out, lse, _pairs(32, 128, 12, 1), BF16_REL, BF16_ABS)
+
+
+def test_full_paged_varlen_b64():
+    inp = make_inputs("paged_varlen_b64")
+    _, out, lse = _run(inp)
+    assert np.all(np.isfinite(out))
+    _sampled(inp, out, lse, _pairs(64, 128, 10, 2), BF16_REL, BF16_ABS)
+
+
+def test_full_long_b4_l131072():
+    inp = make_inputs("long_b4_l131072")
+    _, out, lse = _run(inp)
+    assert np.all(np.isfinite(out))
+    _sampled(inp, out, lse, _pairs(4, 128, 4, 3), BF16_REL, BF16_ABS)
+
+
+def test_full_fp8_b128_l8192():
+    inp = make_inputs("fp8_b128_l8192")
+    _, out, lse = _run(inp)
+    assert np.all(np.isfinite(out))
+    _sampled(inp, out, lse, _pairs(128, 128, 10, 4), BF16_REL, BF16_ABS)
+    # against the bf16 cache before quantisation, relative L2 per sampled head
+    a = oracle_args(inp, "bf16")
+    for b, h in _pairs(128, 128, 6, 5):
+        ro, _ = oracle.decode_one(b=b, h=h, **a)
+        assert _rel(out[b, h], ro) <= FP8_REL
