@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""MLA latent-cache decode benchmark on one MI355X.
+
+One step = the whole decode hot path for one batch: mla_absorb_q ->
+mla_decode (split-KV) -> mla_combine -> mla_out_proj, on the DeepSeek-V2
+shaped workload (128 heads, d_c 512, rotary 64, batch 32, every sequence 4096
+tokens, bf16 cache). Inputs are seeded synthetic tensors already resident in
+HBM. The timed region replays HIP graphs of whole steps; the latent cache is
+rotated over several copies (>= 600 MB in all) so the 256 MB Infinity Cache
+cannot hold it between steps.
+
+Prints one JSON line: queries/s of the step (value), the decode kernel's
+latent-cache bandwidth against the 8 TB/s HBM peak (roofline), and the CPU
+oracle timed on a bounded sample on this host (cpu_baseline).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode queries/sec + latent-cache HBM GB/s (% peak) at B=32, L=4096 bf16"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv2_b32_l4096")
+    ap.add_argument("--splits", type=int, default=0, help="0 = library suggestion")
+    ap.add_argument("--eager", action="store_true", help="launch from Python instead of graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, budget_s):
+    """The float64 oracle, as it stands, on whole sequences of the same
+    workload until about `budget_s` seconds of CPU work have run."""
+    import numpy as np
+    import oracle
+    from mla_synth import oracle_args
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    a = oracle_args(inp)
+    done, t0 = 0, time.perf_counter()
+    while done < inp.batch:
+        L = int(inp.seq_lens[done])
+        c_kv, k_rope = oracle.gather_rows(a["cache"], done, L)
+        oracle.attend_nonabsorbed(c_kv, k_rope, a["q_nope"][done], a["q_rope"][done],
+                                  a["w_uk"], a["w_uv"], a["sm_scale"])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d sequences (all %d heads, %d tokens each), %.1f s, float64 "
+                      "non-absorbed oracle" % (done, inp.batch, inp.dims.num_heads,
+                                               int(inp.seq_lens[0]), dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the decode path has no multi-GPU mode "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mla_latent_kv_28_amd as mla
+    from mla_latent_kv_28_amd.pipeline import DecodePipeline
+    from mla_synth import make_inputs
+
+    mla.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    inp = make_inputs(args.workload)
+    B, L = inp.batch, inp.max_seq_len
+    cache_bytes = inp.cache_bytes()
+    pipe = DecodePipeline(inp, num_splits=args.splits or None, device="cuda:0")
+    S = pipe.num_splits
+
+    # rotate copies of the cache so that the working set exceeds the MALL
+    nbuf = max(4, math.ceil(2.3 * MALL_BYTES / max(cache_bytes, 1)))
+    if inp.dtype == "fp8":
+        copies = [(pipe.codes, pipe.rope, pipe.scale)] + [
+            (pipe.codes.clone(), pipe.rope.clone(), pipe.scale.clone()) for _ in range(nbuf - 1)]
+        caches = [mla.kv_cache(mla.FP8_E4M3, c, rope=r, scale=s, row_stride=inp.dims.d_latent,
+                               rope_stride=inp.dims.d_rope, page_size=pipe.cache.page_size,
+                               seq_stride=pipe.cache.seq_stride, block_table=pipe.block_table,
+                               max_pages_per_seq=pipe.cache.max_pages_per_seq) for c, r, s in copies]
+    else:
+        copies = [pipe.rows] + [pipe.rows.clone() for _ in range(nbuf - 1)]
+        caches = [mla.kv_cache(pipe.compute, r, row_stride=inp.dims.width,
+                               page_size=pipe.cache.page_size, seq_stride=pipe.cache.seq_stride,
+                               block_table=pipe.block_table,
+                               max_pages_per_seq=pipe.cache.max_pages_per_seq) for r in copies]
+
+    stream = torch.cuda.Stream()
+
+    def step(i):
+        pipe.cache = caches[i % nbuf]
+        pipe.run()
+
+    def decode_only(i):
+        pipe.cache = caches[i % nbuf]
+        pipe.decode()
+        pipe.combine()
+
+    def decode_kernel(i):
+        pipe.cache = caches[i % nbuf]
+        pipe.decode()
+
+    # graphs: one whole step per cache copy, and the decode kernel alone
+    graphs = {}
+    if not args.eager:
+        with torch.cuda.stream(stream):
+            for i in range(nbuf):       # warm the launch path before capture
+                step(i)
+        torch.cuda.synchronize()
+        for name, fn in (("step", step), ("decode_combine", decode_only), ("decode", decode_kernel)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(nbuf):
+                    fn(i)
+            graphs[name] = g
+
+    def run(name, fn, n):
+        """n replays of `name` (each = nbuf launches of fn) or eager calls."""
+        if not args.eager:
+            for _ in range(n):
+                graphs[name].replay()
+        else:
+            with torch.cuda.stream(stream):
+                for i in range(n * nbuf):
+                    fn(i)
+
+    def timed(name, fn, steps, warmup):
+        reps = max(1, math.ceil(steps / nbuf))
+        wreps = max(1, math.ceil(warmup / nbuf))
+        run(name, fn, wreps)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            run(name, fn, reps)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        n = reps * nbuf
+        return e0.elapsed_time(e1) / n, n       # ms per launch set, count
+
+    torch.cuda.synchronize()
+    ms_step, nsteps = timed("step", step, args.steps, args.warmup)
+    ms_dc, _ = timed("decode_combine", decode_only, args.steps, args.warmup)
+    ms_dec, ndec = timed("decode", decode_kernel, args.steps, args.warmup)
+
+    q_step = B / (ms_step * 1e-3)
+    gbps_step = cache_bytes / (ms_step * 1e-3) / 1e9
+    gbps_dec = cache_bytes / (ms_dec * 1e-3) / 1e9
+    flops_dec = B * L * 2 * inp.dims.num_heads * (inp.dims.width + inp.dims.d_latent)
+
+    result = {
+        "metric": METRIC,
+        "value": round(q_step, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": nsteps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 cache, bf16" if inp.dtype == "fp8" else inp.compute_dtype,
+        "data": "synthetic (seeded; DeepSeek-V2 shapes, random-init weights)",
+        "config": {
+            "workload": inp.name, "batch": B, "seq_len": L, "heads": inp.dims.num_heads,
+            "d_latent": inp.dims.d_latent, "d_rope": inp.dims.d_rope, "layout": inp.layout,
+            "splits": S, "cache_copies_rotated": nbuf, "launch": "eager" if args.eager else "hip-graph",
+            "parallelism": "single GPU",
+        },
+        "cache_GBps": round(gbps_step, 1),
+        "cache_GBps_frac_of_8TBps": round(gbps_step / HBM_PEAK_GBPS, 4),
+        "decode_plus_combine_queries_per_s": round(B / (ms_dc * 1e-3), 1),
+        "roofline": {
+            "kernel": "mla_decode",
+            "bound": "hbm",
+            "achieved": round(gbps_dec, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps_dec / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "us_per_launch": round(ms_dec * 1e3, 3),
+            "algorithmic_bytes_per_launch": cache_bytes,
+            "mfma_tflops": round(flops_dec / (ms_dec * 1e-3) / 1e12, 1),
+            "mfma_frac_of_bf16_dense_peak": round(flops_dec / (ms_dec * 1e-3) / 2.5e15, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
