@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mb", type=int, default=512,
+                    help="size of the plain copy run once for byte-counter calibration")
     return ap.parse_args()
 
 
@@ -164,6 +166,16 @@ def main():
         torch.cuda.synchronize()
         n = reps * nbuf
         return e0.elapsed_time(e1) / n, n       # ms per launch set, count
+
+    # A plain device-to-device copy of known size: hardware byte counters
+    # (FETCH_SIZE / WRITE_SIZE) read on it calibrate those read on the decode.
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb << 18
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     torch.cuda.synchronize()
     ms_step, nsteps = timed("step", step, args.steps, args.warmup)

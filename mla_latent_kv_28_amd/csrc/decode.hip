@@ -11,12 +11,21 @@
 //   S^T[tokens x heads] = Rows[tokens x 576] . Q^T[576 x heads]      (MFMA)
 //   O^T[512 x heads]   += C_KV^T[512 x tokens] . P^T[tokens x heads]  (MFMA)
 //
-// One workgroup handles one (sequence, split) for all heads: wave w owns heads
-// 32w .. 32w+31 (its query fragments stay in VGPRs, its 32 x 512 output in
-// AGPRs). Tiles of 32 tokens are streamed HBM -> LDS with direct 16-byte
-// loads, double buffered, and every tile is read from HBM exactly once for
-// all heads. The softmax is the streaming form in fp32 and base 2 against a
-// fixed per-head reference maximum (see kHeadroom).
+// One workgroup handles one (sequence, split) for all heads, and every cache
+// tile is read from HBM once for all heads. Tiles of 32 tokens stream
+// HBM -> LDS with direct 16-byte loads into a ring of LDS buffers (two tiles
+// in flight while a third is computed). Wave w:
+//   - scores its 32 heads 32w..32w+31 (their query fragments stay in VGPRs),
+//     runs the softmax for them and writes P^T of those heads to LDS;
+//   - after one workgroup barrier, accumulates latent features
+//     w*d_c/waves .. (w+1)*d_c/waves - 1 for ALL heads (its O^T slice lives in
+//     AGPRs), reading P^T of every head from LDS and its own C_KV^T slice with
+//     transposing reads.
+// Splitting the latent sum by features (not by heads) means each wave reads
+// only its slice of the tile through the slower transposing LDS path.
+// The softmax is the streaming form in fp32 and base 2 against a fixed
+// per-head reference maximum (see kHeadroom), so the accumulators are never
+// rescaled inside the loop.
 #include <type_traits>
 
 #include "mla_device.h"
@@ -32,8 +41,11 @@ struct Cfg {
   static constexpr bool F32 = KIND_ == kF32;
   static constexpr bool FP8 = KIND_ == kFP8;
   static constexpr int T = 32;                          // tokens per tile
-  static constexpr int WAVES = (H + 31) / 32;
+  static constexpr int WAVES = (H + 31) / 32;           // = head blocks of 32
+  static constexpr int HB = WAVES;
   static constexpr int THREADS = WAVES * 64;
+  static constexpr int FPW = DC / WAVES;                // latent features per wave (latent sum)
+  static constexpr int NFJ = FPW / 32;                  // 32-feature fragments per wave
   static constexpr int ESZ = F32 ? 4 : 2;               // LDS element bytes
   static constexpr int LAT_CH = DC * ESZ / 16;          // 16-byte chunks per LDS latent row
   static constexpr int ROPE_CH = DR * ESZ / 16;
@@ -41,18 +53,30 @@ struct Cfg {
   static constexpr int ROPE_BYTES = T * DR * ESZ;
   static constexpr int SCALE_BYTES = FP8 ? T * 4 : 0;
   static constexpr int BUF_BYTES = LAT_BYTES + ROPE_BYTES + SCALE_BYTES;
+  static constexpr int NBUF = FP8 ? 3 : 4;              // tile ring
+  static constexpr int AHEAD = NBUF - 2;                // tiles in flight beyond the next one
+  static constexpr int PROW = T * ESZ;                  // bytes of one head's P^T row
+  static constexpr int P_BYTES = HB * 32 * PROW;
   static constexpr int NKC_LAT = DC / 16, NKC_ROPE = DR / 16, NKC = NKC_LAT + NKC_ROPE;
-  static constexpr int NFRAG = DC / 32;                 // 32-feature output fragments
-  static_assert(DC % 32 == 0 && DR % 16 == 0, "head shape");
+  static constexpr int LDS_BYTES = NBUF * BUF_BYTES + 2 * P_BYTES;
+  static_assert(DC % (32 * WAVES) == 0 && DR % 16 == 0, "head shape");
+  static_assert(FPW % 128 == 0 || F32, "a wave's feature slice starts on a swizzle period");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// XOR swizzle of 16-byte chunks within an LDS row. The key moves chunk pairs
-// (t & 3 -> 0, 2, 4, 6) so that the transposing reads of 4 consecutive tokens
-// hit distinct banks, and the low bit (t >> 2 & 1) separates rows 4 apart for
-// the row-wise reads of 8 consecutive tokens.
+// XOR swizzle of 16-byte chunks within an LDS row (the LDS serves 256 bytes,
+// i.e. 16 chunks, per cycle).
+//  - 1 KiB latent rows (64 chunks): key = (t & 3) << 2 | (t >> 2) & 3, a
+//    bijection on t mod 16. Sixteen consecutive rows read at the same chunk
+//    (the row-wise score reads) land on 16 distinct chunk slots, and the
+//    transposing reads of 4 consecutive tokens x 4 consecutive chunks also
+//    cover all 16 slots (the token's low bits select the slot's high bits).
+//  - 128-byte rotary rows (8 chunks): key = (t >> 1) & 7; two rows share a
+//    256-byte window, so sixteen rows again cover 16 distinct slots.
 template <int CH>
 __device__ __forceinline__ int swz(int t) {
-  if constexpr (CH >= 8) return ((t & 3) << 1) | ((t >> 2) & 1);
+  if constexpr (CH >= 16) return ((t & 3) << 2) | ((t >> 2) & 3);
+  else if constexpr (CH == 8) return (t >> 1) & 7;
   else return 0;
 }
 
@@ -64,16 +88,59 @@ template <class C>
 __device__ __forceinline__ int rope_off(int t, int byte) {
   return C::LAT_BYTES + t * (C::DR * C::ESZ) + ((((byte >> 4) ^ swz<C::ROPE_CH>(t))) << 4) + (byte & 15);
 }
-
-template <bool PAGED>
-__device__ __forceinline__ int64_t row_of(const DecodeParams& p, int b, int tok) {
-  if constexpr (!PAGED) {
-    return (int64_t)b * p.seq_stride + tok;
-  } else {
-    const int page = p.block_table[(int64_t)b * p.max_pages + (tok >> p.page_shift)];
-    return ((int64_t)page << p.page_shift) + (tok & ((1 << p.page_shift) - 1));
-  }
+// P^T row of head h, chunk k (16 bytes): bf16 rows hold four chunks (four
+// rows per 256-byte window), swizzled by (h >> 2) & 3 so that sixteen
+// consecutive heads at one chunk cover 16 distinct slots; f32 rows are plain.
+template <class C>
+__device__ __forceinline__ int p_off(int h, int k) {
+  if constexpr (C::F32) return h * C::PROW + 16 * k;
+  else return h * C::PROW + 16 * (k ^ ((h >> 2) & 3));
 }
+
+// Physical cache rows of the tokens of one tile. Tiles start on multiples of
+// 32 tokens; a token past the split's end is replaced by the tile's first
+// token (always valid), whose score is masked later. With pages of at least
+// 16 tokens a tile touches at most two pages, looked up once per tile with
+// scalar loads; smaller pages are looked up per token.
+template <bool PAGED>
+struct TileRows {
+  int b, tile_base, end;
+  int64_t seq_row;         // contiguous: first row of the sequence
+  int shift, lp0;          // paged: log2(page size), first logical page of the tile
+  int64_t pg0, pg1;        // paged, big pages: physical pages of the tile
+  bool small_pages;
+  const int32_t* bt_row;
+
+  __device__ __forceinline__ TileRows(const DecodeParams& p, int b_, int tile_base_, int end_)
+      : b(b_), tile_base(tile_base_), end(end_) {
+    if constexpr (!PAGED) {
+      seq_row = (int64_t)b * p.seq_stride;
+    } else {
+      shift = p.page_shift;
+      bt_row = p.block_table + (int64_t)b * p.max_pages;
+      lp0 = tile_base >> shift;
+      small_pages = shift < 4;
+      if (!small_pages) {
+        pg0 = bt_row[lp0];
+        pg1 = (shift == 4 && tile_base + 16 < end) ? (int64_t)bt_row[lp0 + 1] : pg0;
+      }
+    }
+  }
+  __device__ __forceinline__ int64_t row(int t) const {   // t: token index within the tile
+    int tok = tile_base + t;
+    tok = tok < end ? tok : tile_base;
+    if constexpr (!PAGED) {
+      return seq_row + tok;
+    } else {
+      const int mask = (1 << shift) - 1;
+      if (!small_pages) {
+        const int64_t pg = ((tok >> shift) == lp0) ? pg0 : pg1;
+        return (pg << shift) + (tok & mask);
+      }
+      return ((int64_t)bt_row[tok >> shift] << shift) + (tok & mask);
+    }
+  }
+};
 
 // Staging registers of the fp8 loader (codes and scales pass through VGPRs).
 template <class C>
@@ -87,10 +154,9 @@ struct Fp8Stage {
 
 // Per-lane direct loads of a region whose rows hold CH 16-byte chunks
 // (CH < 64: several rows per wave instruction).
-template <class C, bool PAGED, int CH>
-__device__ __forceinline__ void issue_rows_lanewise(const DecodeParams& p, const char* src,
-                                                    int64_t src_row_bytes, MLA_LDS char* dst, int b,
-                                                    int tile_base, int start, int end) {
+template <class C, int CH, class Rows>
+__device__ __forceinline__ void issue_rows_lanewise(const Rows& tr, const char* src, int64_t src_row_bytes,
+                                                    MLA_LDS char* dst) {
   const int tid = threadIdx.x, wave = tid >> 6;
   constexpr int TOT = C::T * CH;
 #pragma unroll
@@ -99,21 +165,49 @@ __device__ __forceinline__ void issue_rows_lanewise(const DecodeParams& p, const
     if (TOT % C::THREADS == 0 || pc < TOT) {
       const int t = pc / CH;
       const int c = (pc % CH) ^ swz<CH>(t);
-      int tok = tile_base + t;
-      tok = tok < end ? tok : start;
-      load16_to_lds(src + row_of<PAGED>(p, b, tok) * src_row_bytes + c * 16,
-                    dst + (k * C::THREADS + wave * 64) * 16);
+      load16_to_lds(src + tr.row(t) * src_row_bytes + c * 16, dst + (k * C::THREADS + wave * 64) * 16);
     }
   }
 }
 
+// Vector-memory instructions one tile costs each thread (for vmcnt waits).
+template <class C>
+constexpr int loads_per_tile() {
+  constexpr int lat = C::FP8 ? Fp8Stage<C>::ROUNDS
+                             : (C::LAT_CH == 64 ? C::T / C::WAVES
+                                                : (C::T * C::LAT_CH + C::THREADS - 1) / C::THREADS);
+  constexpr int rope = (C::T * C::ROPE_CH + C::THREADS - 1) / C::THREADS;
+  return lat + rope;
+}
+
 // Start the HBM -> LDS transfer of tile rows [tile_base, tile_base + T).
-// Rows past `end` are replaced by row `start` (always valid); their scores are
-// masked, so they only need to be finite.
 template <class C, bool PAGED>
 __device__ __forceinline__ void issue_tile(const DecodeParams& p, MLA_LDS char* buf, int b,
-                                           int tile_base, int start, int end, Fp8Stage<C>& st) {
+                                           int tile_base, int end, Fp8Stage<C>& st) {
   const int tid = threadIdx.x, lane = tid & 63;
+  const TileRows<PAGED> tr(p, b, tile_base, end);
+  if constexpr (!C::FP8 && C::LAT_CH == 64) {
+    // Fast path: a full tile whose 32 rows are consecutive in memory (a
+    // contiguous cache, or pages of at least 32 tokens). Row addresses are
+    // wave-uniform scalar values; lanes add their swizzled chunk offsets.
+    const bool consecutive = !PAGED || p.page_shift >= 5;
+    if (consecutive && tile_base + C::T <= end) {
+      const int64_t rs = p.row_stride * C::ESZ;
+      const char* tile = (const char*)p.latent + tr.row(0) * rs;
+      const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+      static_assert(C::WAVES == 4, "row 4k + wave has swizzle key (wave << 2) | (k & 3)");
+#pragma unroll
+      for (int k = 0; k < C::T / C::WAVES; ++k) {
+        const int t = k * C::WAVES + wave;
+        load16_to_lds(tile + t * rs + ((lane ^ swz<64>(t)) << 4), buf + t * (C::DC * C::ESZ));
+      }
+      // rotary keys: 8 lanes per row, one instruction for the whole tile
+      static_assert(C::T * C::ROPE_CH == C::THREADS, "one rotary chunk per thread");
+      const int t = tid / C::ROPE_CH, c = (tid % C::ROPE_CH) ^ swz<C::ROPE_CH>(t);
+      load16_to_lds(tile + t * rs + C::DC * C::ESZ + c * 16, buf + C::LAT_BYTES + wave * 64 * 16);
+      return;
+    }
+  }
   if constexpr (!C::FP8) {
     const char* base = (const char*)p.latent;
     const int64_t rs = p.row_stride * C::ESZ;
@@ -124,16 +218,13 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, MLA_LDS char* 
 #pragma unroll
       for (int k = 0; k < C::T / C::WAVES; ++k) {
         const int t = k * C::WAVES + wave;
-        int tok = tile_base + t;
-        tok = tok < end ? tok : start;
-        const char* g = base + row_of<PAGED>(p, b, tok) * rs + ((lane ^ swz<64>(t)) << 4);
+        const char* g = base + tr.row(t) * rs + ((lane ^ swz<64>(t)) << 4);
         load16_to_lds(g, buf + t * (C::DC * C::ESZ));
       }
     } else {
-      issue_rows_lanewise<C, PAGED, C::LAT_CH>(p, base, rs, buf, b, tile_base, start, end);
+      issue_rows_lanewise<C, C::LAT_CH>(tr, base, rs, buf);
     }
-    issue_rows_lanewise<C, PAGED, C::ROPE_CH>(p, base + C::DC * C::ESZ, rs, buf + C::LAT_BYTES, b,
-                                              tile_base, start, end);
+    issue_rows_lanewise<C, C::ROPE_CH>(tr, base + C::DC * C::ESZ, rs, buf + C::LAT_BYTES);
   } else {
     // e4m3 codes: 16 per chunk, staged in VGPRs and widened to bf16 later.
     const char* codes = (const char*)p.latent;
@@ -142,17 +233,10 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, MLA_LDS char* 
     for (int k = 0; k < Fp8Stage<C>::ROUNDS; ++k) {
       const int pc = k * C::THREADS + tid;
       const int t = pc / CPR, c = pc % CPR;
-      int tok = tile_base + t;
-      tok = tok < end ? tok : start;
-      st.codes[k] = load16(codes + row_of<PAGED>(p, b, tok) * p.row_stride + c * 16);
+      st.codes[k] = load16(codes + tr.row(t) * p.row_stride + c * 16);
     }
-    issue_rows_lanewise<C, PAGED, C::ROPE_CH>(p, (const char*)p.rope, p.rope_stride * 2,
-                                              buf + C::LAT_BYTES, b, tile_base, start, end);
-    if (tid < C::T) {
-      int tok = tile_base + tid;
-      tok = tok < end ? tok : start;
-      st.scale = p.scale[row_of<PAGED>(p, b, tok)];
-    }
+    issue_rows_lanewise<C, C::ROPE_CH>(tr, (const char*)p.rope, p.rope_stride * 2, buf + C::LAT_BYTES);
+    if (tid < C::T) st.scale = p.scale[tr.row(tid)];
   }
 }
 
@@ -179,34 +263,39 @@ __device__ __forceinline__ void commit_tile(MLA_LDS char* buf, const Fp8Stage<C>
   }
 }
 
-// Per-lane LDS byte offsets, computed once. Every LDS read of the tile loop is
-// one of these plus a compile-time constant, so the reads use the DS
-// instruction's immediate offset instead of one address register per read.
-// (The XOR key only touches the low 3 bits of a chunk index.)
+// Per-lane LDS byte offsets, computed once. Every tile-buffer read of the loop
+// is one of these plus a compile-time constant (the DS instruction's
+// immediate offset). The XOR key only touches the low 4 bits of a chunk index.
 template <class C>
 struct LaneOffs {
-  int qk_lat[4];    // latent k block kc:  qk_lat[kc & 3] + 128 * (kc >> 2)
-  int qk_rope[4];   // rotary k block kk:  qk_rope[kk]
-  int pv[2];        // C_KV^T fragment f, k step u, half q:
-                    //   pv[f & 1] + ROWB * (16u + 8q) + 128 * (f >> 1)
+  int qk_lat[8];     // latent k block kc:  qk_lat[kc & 7] + 256 * (kc >> 3)
+  int qk_rope[4];    // rotary k block kk:  qk_rope[kk]
+  int pv[2][4];      // C_KV^T fragment j of this wave's slice, k step u, half q:
+                     //   pv[q][j & 3] + ROWB * 16u + 256 * (j >> 2)
 };
 
 template <class C>
-__device__ __forceinline__ LaneOffs<C> lane_offsets() {
+__device__ __forceinline__ LaneOffs<C> lane_offsets(int wave) {
   LaneOffs<C> o;
   const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
   constexpr int ROWB = C::DC * C::ESZ;
   const int kr = swz<C::LAT_CH>(r);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) o.qk_lat[j] = r * ROWB + 16 * ((2 * j + hh) ^ kr);
+  for (int j = 0; j < 8; ++j) o.qk_lat[j] = r * ROWB + 16 * ((2 * j + hh) ^ kr);
   const int kq = swz<C::ROPE_CH>(r);
 #pragma unroll
   for (int j = 0; j < 4; ++j) o.qk_rope[j] = C::LAT_BYTES + r * (C::DR * C::ESZ) + 16 * ((2 * j + hh) ^ kq);
+  // transposing reads: source lane (a, e) of 16-lane group `sub` points at
+  // token 16u + 8q + 4hh + e, features wave*FPW + 32j + 16*sub + 4a .. +3
   const int s16 = lane & 15, a4 = s16 & 3, e4 = s16 >> 2, sub = (lane >> 4) & 1;
-  const int kt = swz<C::LAT_CH>(4 * hh + e4);     // equals the key of 16u + 8q + 4hh + e4
 #pragma unroll
-  for (int fp = 0; fp < 2; ++fp)
-    o.pv[fp] = (4 * hh + e4) * ROWB + 16 * ((4 * fp + 2 * sub + (a4 >> 1)) ^ kt) + 8 * (a4 & 1);
+  for (int q = 0; q < 2; ++q) {
+    const int kt = swz<C::LAT_CH>(8 * q + 4 * hh + e4);   // = key of 16u + 8q + 4hh + e4
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o.pv[q][j] = (8 * q + 4 * hh + e4) * ROWB + 16 * ((4 * j + 2 * sub + (a4 >> 1)) ^ kt) +
+                   8 * (a4 & 1) + 2 * wave * C::FPW;
+  }
   return o;
 }
 
@@ -218,8 +307,8 @@ struct QFrag {
 
 template <class C>
 struct State {
-  f32x16 o[C::NFRAG];
-  float m_ref;     // reference maximum the exponentials are taken against
+  f32x16 o[C::NFJ][C::HB];   // O^T: this wave's feature fragments x all head blocks
+  float m_ref;     // reference maximum the exponentials are taken against (own heads)
   float m_max;     // largest base-2 scaled score seen so far
   float l;         // this lane's share of the softmax denominator
   bool overflow;   // a score exceeded m_ref by more than kHeadroom
@@ -233,12 +322,12 @@ struct State {
 // split is recomputed with the true maximum as reference.
 constexpr float kHeadroom = 64.0f;
 
-// One tile: scores, online softmax, weighted latent sum.
+// Scores of this wave's heads for one tile, online softmax, P^T to LDS.
 template <class C>
-__device__ __forceinline__ void compute_tile(const MLA_LDS char* buf, const QFrag<C>& q, State<C>& s,
-                                             const LaneOffs<C>& lo, int tile_base, int end,
-                                             float scale_log2) {
-  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+__device__ __forceinline__ void scores_tile(const MLA_LDS char* buf, MLA_LDS char* pbuf, const QFrag<C>& q,
+                                            State<C>& s, const LaneOffs<C>& lo, int nvalid,
+                                            float scale_log2) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
 
   // ---- S^T = Rows . Q^T : lane (hh, c) gets tokens 8j + 4hh + i of head c ----
   f32x16 sl = {}, sr = {};
@@ -257,10 +346,23 @@ __device__ __forceinline__ void compute_tile(const MLA_LDS char* buf, const QFra
       for (int e = 0; e < 4; ++e) { a[e] = x0[e]; a[4 + e] = x1[e]; }
       sl = mfma32x32x16_f32(a, q.v[kc], sl);
     } else {
-      const int off = rope_part ? lo.qk_rope[kk] : lo.qk_lat[kk & 3] + 128 * (kk >> 2);
-      const bf16x8 a = *(const MLA_LDS bf16x8*)(buf + off);
-      if (C::FP8 && rope_part) sr = mfma32x32x16(a, q.v[kc], sr);
-      else sl = mfma32x32x16(a, q.v[kc], sl);
+      (void)kk;
+    }
+  }
+  if constexpr (!C::F32) {
+    // K fragments are read three blocks ahead of the MFMA that consumes them
+    auto ld = [&](int kc) -> bf16x8 {
+      const int off = kc >= C::NKC_LAT ? lo.qk_rope[kc - C::NKC_LAT]
+                                       : lo.qk_lat[kc & 7] + 256 * (kc >> 3);
+      return *(const MLA_LDS bf16x8*)(buf + off);
+    };
+    bf16x8 a0 = ld(0), a1 = ld(1), a2 = ld(2);
+#pragma unroll
+    for (int kc = 0; kc < C::NKC; ++kc) {
+      const bf16x8 a3 = kc + 3 < C::NKC ? ld(kc + 3) : bf16x8{};
+      if (C::FP8 && kc >= C::NKC_LAT) sr = mfma32x32x16(a0, q.v[kc], sr);
+      else sl = mfma32x32x16(a0, q.v[kc], sl);
+      a0 = a1; a1 = a2; a2 = a3;
     }
   }
 
@@ -279,10 +381,10 @@ __device__ __forceinline__ void compute_tile(const MLA_LDS char* buf, const QFra
   float mt = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int tok = tile_base + 8 * (i >> 2) + 4 * hh + (i & 3);
+    const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
     float v = C::FP8 ? (tok_scale[i] * sl[i] + sr[i]) : sl[i];
     v *= scale_log2;
-    x[i] = tok < end ? v : -INFINITY;
+    x[i] = tok < nvalid ? v : -INFINITY;
     mt = fmaxf(mt, x[i]);
   }
   mt = wave_max32(mt);
@@ -297,86 +399,126 @@ __device__ __forceinline__ void compute_tile(const MLA_LDS char* buf, const QFra
     if constexpr (C::FP8) pr[i] *= tok_scale[i];
   }
 
-  // ---- O^T += C_KV^T . P^T over two 16-token k steps ----
+  // ---- P^T rows of this wave's heads: element e of k step u is token
+  //      16u + 8(e/4) + 4hh + e%4, i.e. pr[8u + e] ----
+  const int head = 32 * wave + r;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if constexpr (C::F32) {
-      float pb[8];
+      f32x4 v0, v1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = pr[8 * u + e];
+      for (int e = 0; e < 4; ++e) { v0[e] = pr[8 * u + e]; v1[e] = pr[8 * u + 4 + e]; }
+      *(MLA_LDS f32x4*)(pbuf + p_off<C>(head, 4 * u + 2 * hh)) = v0;
+      *(MLA_LDS f32x4*)(pbuf + p_off<C>(head, 4 * u + 2 * hh + 1)) = v1;
+    } else {
+      u32x4 v;
 #pragma unroll
-      for (int f = 0; f < C::NFRAG; ++f) {
+      for (int d = 0; d < 4; ++d) v[d] = pack_bf16x2(pr[8 * u + 2 * d], pr[8 * u + 2 * d + 1]);
+      *(MLA_LDS u32x4*)(pbuf + p_off<C>(head, 2 * u + hh)) = v;
+    }
+  }
+}
+
+// O^T[this wave's features, all heads] += C_KV^T . P^T for one tile.
+template <class C>
+__device__ __forceinline__ void latent_sum_tile(const MLA_LDS char* buf, const MLA_LDS char* pbuf,
+                                                State<C>& s, const LaneOffs<C>& lo) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if constexpr (C::F32) {
+#pragma unroll
+      for (int j = 0; j < C::NFJ; ++j) {
         float a[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int t = 16 * u + 8 * (e >> 2) + 4 * hh + (e & 3);
-          a[e] = *(const MLA_LDS float*)(buf + lat_off<C>(t, (32 * f + r) * 4));
+          a[e] = *(const MLA_LDS float*)(buf + lat_off<C>(t, (wave * C::FPW + 32 * j + r) * 4));
         }
-        s.o[f] = mfma32x32x16_f32(a, pb, s.o[f]);
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) {
+          float pb[8];
+          const f32x4 x0 = *(const MLA_LDS f32x4*)(pbuf + p_off<C>(32 * hb + r, 4 * u + 2 * hh));
+          const f32x4 x1 = *(const MLA_LDS f32x4*)(pbuf + p_off<C>(32 * hb + r, 4 * u + 2 * hh + 1));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { pb[e] = x0[e]; pb[4 + e] = x1[e]; }
+          s.o[j][hb] = mfma32x32x16_f32(a, pb, s.o[j][hb]);
+        }
       }
     } else {
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)pr[8 * u + e];
-      // transposing reads: source lane s = a + 4e of each 16-lane group points
-      // at token 16u + 8q + 4hh + e, features 32f + 16*sub + 4a .. +3
       constexpr int ROWB = C::DC * C::ESZ;
+      bf16x8 a[C::NFJ];
 #pragma unroll
-      for (int f = 0; f < C::NFRAG; ++f) {
-        const int off = lo.pv[f & 1] + ROWB * 16 * u + 128 * (f >> 1);
-        const bf16x4 v0 = lds_read_tr16(buf + off);
-        const bf16x4 v1 = lds_read_tr16(buf + off + ROWB * 8);
-        const bf16x8 a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        s.o[f] = mfma32x32x16(a, pb, s.o[f]);
+      for (int j = 0; j < C::NFJ; ++j) {
+        const int off = ROWB * 16 * u + 256 * (j >> 2);
+        const bf16x4 v0 = lds_read_tr16(buf + lo.pv[0][j & 3] + off);
+        const bf16x4 v1 = lds_read_tr16(buf + lo.pv[1][j & 3] + off);
+        a[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int hb = 0; hb < C::HB; ++hb) {
+        const bf16x8 pb = *(const MLA_LDS bf16x8*)(pbuf + p_off<C>(32 * hb + r, 2 * u + hh));
+#pragma unroll
+        for (int j = 0; j < C::NFJ; ++j) s.o[j][hb] = mfma32x32x16(a[j], pb, s.o[j][hb]);
       }
     }
   }
 }
 
-template <class C>
-__device__ __forceinline__ void write_result(const DecodeParams& p, int b, int split, const State<C>& s,
-                                             bool empty) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
-  const int head = wave * 32 + r;
-  const float l_tot = s.l + __shfl_xor(s.l, 32);   // lanes r and r + 32 hold one head
-  if (head >= C::H) return;
-  float inv = empty ? 0.0f : 1.0f / l_tot;
-  float lse = empty ? -INFINITY : (s.m_ref + fast_log2(l_tot)) * kLn2;
-  const bool split_out = p.num_splits > 1;
-  const int64_t row = split_out ? (((int64_t)b * p.num_splits + split) * C::H + head)
-                                : ((int64_t)b * C::H + head);
-  if (hh == 0) p.lse[row] = lse;
-  if (split_out || !p.out_bf16) {
-    float* o = (float*)p.out + row * C::DC;
-#pragma unroll
-    for (int f = 0; f < C::NFRAG; ++f)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = empty ? 0.0f : s.o[f][4 * j + i] * inv;
-        *(f32x4*)(o + 32 * f + 8 * j + 4 * hh) = v;
-      }
-  } else {
-    uint16_t* o = (uint16_t*)p.out + row * C::DC;
-#pragma unroll
-    for (int f = 0; f < C::NFRAG; ++f)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 v;
-        float w0 = empty ? 0.0f : s.o[f][4 * j + 0] * inv, w1 = empty ? 0.0f : s.o[f][4 * j + 1] * inv;
-        float w2 = empty ? 0.0f : s.o[f][4 * j + 2] * inv, w3 = empty ? 0.0f : s.o[f][4 * j + 3] * inv;
-        v[0] = pack_bf16x2(w0, w1);
-        v[1] = pack_bf16x2(w2, w3);
-        *(u32x2*)(o + 32 * f + 8 * j + 4 * hh) = v;
-      }
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else static_assert(N == 0, "add the vmcnt value here");
+}
+
+// Workgroup barrier for the tile loop. LDS stores of this wave are drained
+// first; the direct HBM->LDS loads are waited for explicitly by the caller
+// (s_waitcnt vmcnt), so no fence has to drain every load still in flight.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One tile of the loop. The buffers are distinct ring slots: `cur` is read,
+// `next` (the following tile) may still be receiving its data, `ahead` is
+// refilled. __restrict__ tells the compiler that reading `cur` does not have
+// to wait for the loads into the other slots; the explicit vmcnt wait before
+// the barrier is what makes the following tile resident.
+template <class C, bool PAGED>
+__device__ __forceinline__ void tile_step(const DecodeParams& p, const MLA_LDS char* __restrict__ cur,
+                                          MLA_LDS char* __restrict__ pbuf, MLA_LDS char* __restrict__ next,
+                                          MLA_LDS char* __restrict__ ahead, const QFrag<C>& q, State<C>& s,
+                                          const LaneOffs<C>& lo, Fp8Stage<C>& st, int b, int it, int ntiles,
+                                          int start, int end) {
+  constexpr int LPT = loads_per_tile<C>();
+  scores_tile<C>(cur, pbuf, q, s, lo, end - (start + it * C::T), p.scale_log2);
+  // make tile it + 1 resident; later tiles may stay in flight
+  if (it + 1 < ntiles) {
+    if constexpr (C::FP8) {
+      wait_vmem_le<0>();
+      commit_tile<C>(next, st);
+    } else {
+      if (C::AHEAD >= 2 && it + 2 < ntiles) wait_vmem_le<LPT>();
+      else wait_vmem_le<0>();
+    }
   }
+  // P^T of every head written; tile it + 1 resident; nobody reads tile it - 1
+  tile_barrier();
+  const int nxt = it + 1 + C::AHEAD;
+  if (nxt < ntiles) issue_tile<C, PAGED>(p, ahead, b, start + nxt * C::T, end, st);
+  latent_sum_tile<C>(cur, pbuf, s, lo);
+}
+
+template <class C>
+__device__ __forceinline__ int64_t out_row(const DecodeParams& p, int b, int split, int head) {
+  return p.num_splits > 1 ? (((int64_t)b * p.num_splits + split) * C::H + head)
+                          : ((int64_t)b * C::H + head);
 }
 
 template <class C, bool PAGED>
 __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) char buf0[C::BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) char buf1[C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
   int w = blockIdx.x;
   if (p.xcd_remap) w = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
@@ -385,21 +527,35 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   const int start = split * p.chunk;
   const int end = min(start + p.chunk, L);
 
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
+  const int head = wave * 32 + r;
+  MLA_LDS char* lds = (MLA_LDS char*)smem;
+  MLA_LDS char* pbase = lds + C::NBUF * C::BUF_BYTES;
+  const bool f32_out = p.num_splits > 1 || !p.out_bf16;
+
+  if (start >= end) {             // uniform over the workgroup: no tokens
+    if (head < C::H) {
+      const int64_t row = out_row<C>(p, b, split, head);
+      if (hh == 0) p.lse[row] = -INFINITY;
+      for (int f = hh; f < C::DC / 4; f += 2) {
+        if (f32_out) *(f32x4*)((float*)p.out + row * C::DC + 4 * f) = f32x4{};
+        else *(u32x2*)((uint16_t*)p.out + row * C::DC + 4 * f) = u32x2{};
+      }
+    }
+    return;
+  }
+
   State<C> s;
 #pragma unroll
-  for (int f = 0; f < C::NFRAG; ++f) s.o[f] = f32x16{};
+  for (int j = 0; j < C::NFJ; ++j)
+#pragma unroll
+    for (int hb = 0; hb < C::HB; ++hb) s.o[j][hb] = f32x16{};
   s.m_ref = -INFINITY;
   s.m_max = -INFINITY;
   s.l = 0.0f;
   s.overflow = false;
-  if (start >= end) {             // uniform over the workgroup
-    write_result<C>(p, b, split, s, true);
-    return;
-  }
 
   // Absorbed query fragments of this wave's 32 heads (B operand of S^T).
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
-  const int head = wave * 32 + r;
   QFrag<C> q;
   {
     const bool ok = head < C::H;
@@ -423,42 +579,76 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   }
 
   Fp8Stage<C> st;
-  const LaneOffs<C> lo = lane_offsets<C>();
+  const LaneOffs<C> lo = lane_offsets<C>(wave);
   const int ntiles = (end - start + C::T - 1) / C::T;
-  MLA_LDS char* B0 = (MLA_LDS char*)buf0;
-  MLA_LDS char* B1 = (MLA_LDS char*)buf1;
-  __shared__ int redo_flag[C::WAVES];
 
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {   // recompute with the true maximum as reference
 #pragma unroll
-      for (int f = 0; f < C::NFRAG; ++f) s.o[f] = f32x16{};
+      for (int j = 0; j < C::NFJ; ++j)
+#pragma unroll
+        for (int hb = 0; hb < C::HB; ++hb) s.o[j][hb] = f32x16{};
       s.l = 0.0f;
       s.m_ref = s.m_max;
     }
-    issue_tile<C, PAGED>(p, B0, b, start, start, end, st);
-    wait_vmem();
-    commit_tile<C>(B0, st);
+    // prologue: tile 0 resident, tiles 1 .. AHEAD in flight
+    issue_tile<C, PAGED>(p, lds, b, start, end, st);
+    wait_vmem_le<0>();
+    commit_tile<C>(lds, st);
+#pragma unroll
+    for (int k = 1; k <= C::AHEAD; ++k)
+      if (k < ntiles) issue_tile<C, PAGED>(p, lds + k * C::BUF_BYTES, b, start + k * C::T, end, st);
     __syncthreads();
+
     for (int it = 0; it < ntiles; ++it) {
-      MLA_LDS char* cur = (it & 1) ? B1 : B0;
-      MLA_LDS char* nxt = (it & 1) ? B0 : B1;
-      const bool more = it + 1 < ntiles;
-      if (more) issue_tile<C, PAGED>(p, nxt, b, start + (it + 1) * C::T, start, end, st);
-      compute_tile<C>(cur, q, s, lo, start + it * C::T, end, p.scale_log2);
-      if (more) { wait_vmem(); commit_tile<C>(nxt, st); }
-      __syncthreads();
+      tile_step<C, PAGED>(p, lds + (it % C::NBUF) * C::BUF_BYTES, pbase + (it & 1) * C::P_BYTES,
+                          lds + ((it + 1) % C::NBUF) * C::BUF_BYTES,
+                          lds + ((it + 1 + C::AHEAD) % C::NBUF) * C::BUF_BYTES, q, s, lo, st, b, it,
+                          ntiles, start, end);
     }
+    __syncthreads();
     if (pass == 1) break;
+    // did any wave's scores outrun the headroom? (uniform decision)
+    MLA_LDS int* redo = (MLA_LDS int*)pbase;
     const bool wave_overflow = __ballot(s.overflow) != 0;
-    if ((threadIdx.x & 63) == 0) redo_flag[threadIdx.x >> 6] = wave_overflow ? 1 : 0;
+    if (lane == 0) redo[wave] = wave_overflow ? 1 : 0;
     __syncthreads();
     int any = 0;
 #pragma unroll
-    for (int w = 0; w < C::WAVES; ++w) any |= redo_flag[w];
-    if (!any) break;    // uniform over the workgroup
+    for (int v = 0; v < C::WAVES; ++v) any |= redo[v];
+    __syncthreads();
+    if (!any) break;
   }
-  write_result<C>(p, b, split, s, false);
+
+  // ---- normalise and store; every head's denominator goes through LDS ----
+  MLA_LDS float* lden = (MLA_LDS float*)pbase;
+  const float l_tot = s.l + __shfl_xor(s.l, 32);   // lanes r and r + 32 hold one head
+  if (hh == 0) lden[head] = l_tot;
+  if (hh == 0 && head < C::H) p.lse[out_row<C>(p, b, split, head)] = (s.m_ref + fast_log2(l_tot)) * kLn2;
+  __syncthreads();
+#pragma unroll
+  for (int hb = 0; hb < C::HB; ++hb) {
+    const int h = 32 * hb + r;
+    if (h >= C::H) continue;
+    const float inv = 1.0f / lden[h];
+    const int64_t row = out_row<C>(p, b, split, h);
+#pragma unroll
+    for (int j = 0; j < C::NFJ; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int feat = wave * C::FPW + 32 * j + 8 * jj + 4 * hh;
+        const float v0 = s.o[j][hb][4 * jj + 0] * inv, v1 = s.o[j][hb][4 * jj + 1] * inv;
+        const float v2 = s.o[j][hb][4 * jj + 2] * inv, v3 = s.o[j][hb][4 * jj + 3] * inv;
+        if (f32_out) {
+          *(f32x4*)((float*)p.out + row * C::DC + feat) = f32x4{v0, v1, v2, v3};
+        } else {
+          u32x2 v;
+          v[0] = pack_bf16x2(v0, v1);
+          v[1] = pack_bf16x2(v2, v3);
+          *(u32x2*)((uint16_t*)p.out + row * C::DC + feat) = v;
+        }
+      }
+  }
 }
 
 template <class C>
