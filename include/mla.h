@@ -126,9 +126,11 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch,
  *            computed independently.
  *   S == 1: out [B, H, d_latent] in out_dtype (MLA_BF16 or MLA_F32),
  *           lse [B, H] f32 (natural log).
- *   S  > 1: out [B, S, H, d_latent] f32 partials, each normalised over its
- *           own chunk; lse [B, S, H] f32. Merge them with mla_combine.
+ *   S  > 1: out [B, S, H, d_latent] partials in out_dtype (MLA_BF16 or
+ *           MLA_F32), each normalised over its own chunk; lse [B, S, H] f32.
+ *           Merge them with mla_combine (same dtype as its part_dtype).
  * A sequence (or chunk) with no tokens yields out = 0 and lse = -inf.
+ * Limits: row_stride (and rope_stride) at most 2^24 bytes.
  */
 mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat,
                       const mla_kv_cache* cache, const int32_t* seq_lens,
@@ -140,13 +142,14 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat,
  *   lse[b,h] = log sum_s exp(lse_part[b,s,h]),
  *   out[b,h] = sum_s exp(lse_part[b,s,h] - lse[b,h]) * o_part[b,s,h,:].
  * Parts with lse = -inf contribute nothing; if all do, out = 0, lse = -inf.
- *   o_part [B, S, H, d_latent] f32, lse_part [B, S, H] f32,
- *   out [B, H, d_latent] in out_dtype (MLA_BF16 or MLA_F32), lse [B, H] f32
- *   (lse may be NULL when not wanted).
+ *   o_part [B, S, H, d_latent] in part_dtype (MLA_BF16 or MLA_F32),
+ *   lse_part [B, S, H] f32, out [B, H, d_latent] in out_dtype (MLA_BF16 or
+ *   MLA_F32), lse [B, H] f32 (lse may be NULL when not wanted).
+ * The weighted sum runs in fp32.
  */
 mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t num_splits,
-                       const float* o_part, const float* lse_part, void* out,
-                       float* lse, int32_t out_dtype, mla_stream stream);
+                       const void* o_part, int32_t part_dtype, const float* lse_part,
+                       void* out, float* lse, int32_t out_dtype, mla_stream stream);
 
 /*
  * Apply W_UV on the output side (DeepSeek-V2 paper, section 2.1.2: W_UV

@@ -60,7 +60,7 @@ def lib():
         pd = ctypes.POINTER(Dims)
         L.mla_absorb_q.argtypes = [pd, i32, vp, vp, vp, vp, i32, vp]
         L.mla_decode.argtypes = [pd, i32, vp, ctypes.POINTER(KVCache), vp, i32, f32, i32, vp, vp, i32, vp]
-        L.mla_combine.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, vp]
+        L.mla_combine.argtypes = [pd, i32, i32, vp, i32, vp, vp, vp, i32, vp]
         L.mla_out_proj.argtypes = [pd, i32, vp, i32, vp, i32, vp, i32, vp]
         L.mla_split_chunk.argtypes = [i32, i32]
         L.mla_suggest_splits.argtypes = [i32, i32, i64, i32]
@@ -150,12 +150,14 @@ def mla_decode(dims, batch, q_lat, cache, seq_lens, max_seq_len, sm_scale, num_s
     _check(st, "mla_decode")
 
 
-def mla_combine(dims, batch, num_splits, o_part, lse_part, out, lse, out_dtype, stream=None):
+def mla_combine(dims, batch, num_splits, o_part, part_dtype, lse_part, out, lse, out_dtype,
+                stream=None):
     d = dims_of(dims)
     H = d.num_heads
     st = lib().mla_combine(
         ctypes.byref(d), batch, num_splits,
-        _dev(o_part, "o_part", torch.float32, batch * num_splits * H * d.d_latent),
+        _dev(o_part, "o_part", _TORCH_DTYPE.get(part_dtype), batch * num_splits * H * d.d_latent),
+        part_dtype,
         _dev(lse_part, "lse_part", torch.float32, batch * num_splits * H),
         _dev(out, "out", _TORCH_DTYPE.get(out_dtype), batch * H * d.d_latent),
         _dev(lse, "lse", torch.float32, batch * H),

@@ -5,8 +5,10 @@
 // the union is   lse = log sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) o_s.
 // Splits with no tokens carry lse_s = -inf and contribute nothing.
 //
-// One workgroup per (sequence, head); each thread owns four latent features.
-// The merge weights are computed once per workgroup into LDS.
+// One workgroup per (sequence, head). The merge weights are computed once per
+// workgroup into LDS; each thread then owns one 16-byte vector of latent
+// features (4 fp32 or 8 bf16 partial values) and sums it over the splits with
+// four loads in flight.
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -15,7 +17,30 @@ namespace {
 
 constexpr int kMaxSplitsLds = 1024;
 
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+template <bool PART_BF16>
+struct PartVec {
+  static constexpr int N = PART_BF16 ? 8 : 4;   // features per 16-byte vector
+  __device__ static void unpack(const u32x4& x, float (&v)[N]) {
+    if constexpr (PART_BF16) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        v[2 * d] = bf16_bits_to_f32(x[d] & 0xffffu);
+        v[2 * d + 1] = bf16_bits_to_f32(x[d] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = x[d];   // __builtin_bit_cast of a vector element itself reads element 0
+        v[d] = __builtin_bit_cast(float, w);
+      }
+    }
+  }
+};
+
+template <bool PART_BF16>
+__global__ __launch_bounds__(128) void combine_kernel(CombineParams p) {
+  using V = PartVec<PART_BF16>;
+  constexpr int ESZ = PART_BF16 ? 2 : 4;
   __shared__ float wts[kMaxSplitsLds];
   __shared__ float red[2];
   const int bh = blockIdx.x;
@@ -45,24 +70,44 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   if (threadIdx.x == 0 && p.lse != nullptr)
     p.lse[(int64_t)b * p.heads + h] = empty ? -INFINITY : m + fast_log2(z) * kLn2;
 
-  const int nvec = p.d_latent / 4;
+  const int nvec = p.d_latent / V::N;
+  const int64_t split_stride = (int64_t)p.heads * p.d_latent * ESZ;
+  const char* part = (const char*)p.o_part + ((int64_t)b * S * p.heads + h) * p.d_latent * ESZ;
   for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) {
-      const float w = wts[s];
-      if (w == 0.0f) continue;
-      const f32x4 x = *(const f32x4*)(p.o_part + (((int64_t)b * S + s) * p.heads + h) * p.d_latent + 4 * v);
-      acc += w * x;
+    const char* src = part + v * 16;
+    float acc[V::N];
+#pragma unroll
+    for (int e = 0; e < V::N; ++e) acc[e] = 0.0f;
+    // a split with weight 0 is skipped element-wise, so whatever it holds
+    // (an empty split's zeros or anything else) cannot reach the sum
+    auto add = [&](const u32x4& x, float w) {
+      float xv[V::N];
+      V::unpack(x, xv);
+#pragma unroll
+      for (int e = 0; e < V::N; ++e) acc[e] += w == 0.0f ? 0.0f : w * xv[e];
+    };
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+      u32x4 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = load16(src + (s + i) * split_stride);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) add(x[i], wts[s + i]);
     }
-    acc *= inv;
-    const int64_t o = ((int64_t)b * p.heads + h) * p.d_latent + 4 * v;
-    if (p.out_bf16) {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(acc[0], acc[1]);
-      pk[1] = pack_bf16x2(acc[2], acc[3]);
-      *(u32x2*)((__bf16*)p.out + o) = pk;
-    } else {
-      *(f32x4*)((float*)p.out + o) = acc;
+    for (; s < S; ++s) add(load16(src + s * split_stride), wts[s]);
+
+    const int64_t o = ((int64_t)b * p.heads + h) * p.d_latent + V::N * v;
+#pragma unroll
+    for (int q = 0; q < V::N / 4; ++q) {
+      const f32x4 r = {acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv, acc[4 * q + 3] * inv};
+      if (p.out_bf16) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(r[0], r[1]);
+        pk[1] = pack_bf16x2(r[2], r[3]);
+        *(u32x2*)((__bf16*)p.out + o + 4 * q) = pk;
+      } else {
+        *(f32x4*)((float*)p.out + o + 4 * q) = r;
+      }
     }
   }
 }
@@ -73,8 +118,12 @@ int combine_max_splits() { return kMaxSplitsLds; }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
-  const int threads = p.d_latent / 4 >= 128 ? 128 : 64;
-  hipLaunchKernelGGL(combine_kernel, dim3(p.batch * p.heads), dim3(threads), 0, s, p);
+  const int vec = p.part_bf16 ? 8 : 4;
+  const int threads = p.d_latent / vec >= 128 ? 128 : 64;   // >= 64: one full wave computes the weights
+  if (p.part_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(p.batch * p.heads), dim3(threads), 0, s, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(p.batch * p.heads), dim3(threads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -102,22 +102,36 @@ __device__ __forceinline__ int p_off(int h, int k) {
 // token (always valid), whose score is masked later. With pages of at least
 // 16 tokens a tile touches at most two pages, looked up once per tile with
 // scalar loads; smaller pages are looked up per token.
+// Where one sequence's rows live, computed once per workgroup.
+struct SeqView {
+  int64_t seq_row;          // contiguous: first row of the sequence
+  const int32_t* bt_row;    // paged: the sequence's block-table row
+};
+
+template <bool PAGED>
+__device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int b) {
+  SeqView v;
+  v.seq_row = PAGED ? 0 : (int64_t)b * p.seq_stride;
+  v.bt_row = PAGED ? p.block_table + (int64_t)b * p.max_pages : nullptr;
+  return v;
+}
+
 template <bool PAGED>
 struct TileRows {
-  int b, tile_base, end;
+  int tile_base, end;
   int64_t seq_row;         // contiguous: first row of the sequence
   int shift, lp0;          // paged: log2(page size), first logical page of the tile
   int64_t pg0, pg1;        // paged, big pages: physical pages of the tile
   bool small_pages;
   const int32_t* bt_row;
 
-  __device__ __forceinline__ TileRows(const DecodeParams& p, int b_, int tile_base_, int end_)
-      : b(b_), tile_base(tile_base_), end(end_) {
+  __device__ __forceinline__ TileRows(const DecodeParams& p, const SeqView& sv, int tile_base_, int end_)
+      : tile_base(tile_base_), end(end_) {
     if constexpr (!PAGED) {
-      seq_row = (int64_t)b * p.seq_stride;
+      seq_row = sv.seq_row;
     } else {
       shift = p.page_shift;
-      bt_row = p.block_table + (int64_t)b * p.max_pages;
+      bt_row = sv.bt_row;
       lp0 = tile_base >> shift;
       small_pages = shift < 4;
       if (!small_pages) {
@@ -140,6 +154,12 @@ struct TileRows {
       return ((int64_t)bt_row[tok >> shift] << shift) + (tok & mask);
     }
   }
+};
+
+// Per-lane global byte offsets of the fast tile loader (see issue_tile).
+struct DmaOffs {
+  int lat;    // latent chunk of row 4k + wave: lat ^ 16 (k & 3)
+  int rope;   // this thread's rotary chunk, bytes from the tile's first row
 };
 
 // Staging registers of the fp8 loader (codes and scales pass through VGPRs).
@@ -182,10 +202,10 @@ constexpr int loads_per_tile() {
 
 // Start the HBM -> LDS transfer of tile rows [tile_base, tile_base + T).
 template <class C, bool PAGED>
-__device__ __forceinline__ void issue_tile(const DecodeParams& p, MLA_LDS char* buf, int b,
-                                           int tile_base, int end, Fp8Stage<C>& st) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const TileRows<PAGED> tr(p, b, tile_base, end);
+__device__ __forceinline__ void issue_tile(const DecodeParams& p, const SeqView& sv, const DmaOffs& dma,
+                                           MLA_LDS char* buf, int tile_base, int end, Fp8Stage<C>& st) {
+  const int tid = threadIdx.x;
+  const TileRows<PAGED> tr(p, sv, tile_base, end);
   if constexpr (!C::FP8 && C::LAT_CH == 64) {
     // Fast path: a full tile whose 32 rows are consecutive in memory (a
     // contiguous cache, or pages of at least 32 tokens). Row addresses are
@@ -196,15 +216,18 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, MLA_LDS char* 
       const char* tile = (const char*)p.latent + tr.row(0) * rs;
       const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
       static_assert(C::WAVES == 4, "row 4k + wave has swizzle key (wave << 2) | (k & 3)");
-#pragma unroll
-      for (int k = 0; k < C::T / C::WAVES; ++k) {
-        const int t = k * C::WAVES + wave;
-        load16_to_lds(tile + t * rs + ((lane ^ swz<64>(t)) << 4), buf + t * (C::DC * C::ESZ));
-      }
       // rotary keys: 8 lanes per row, one instruction for the whole tile
       static_assert(C::T * C::ROPE_CH == C::THREADS, "one rotary chunk per thread");
-      const int t = tid / C::ROPE_CH, c = (tid % C::ROPE_CH) ^ swz<C::ROPE_CH>(t);
-      load16_to_lds(tile + t * rs + C::DC * C::ESZ + c * 16, buf + C::LAT_BYTES + wave * 64 * 16);
+      load16_to_lds(tile + (uint32_t)dma.rope, buf + C::LAT_BYTES + wave * 64 * 16);
+      // latent rows wave, wave + 4, ...: one scalar row pointer stepped by 4 rows
+      const char* row = tile + wave * rs;
+      MLA_LDS char* dst = buf + wave * (C::DC * C::ESZ);
+#pragma unroll
+      for (int k = 0; k < C::T / C::WAVES; ++k) {
+        load16_to_lds(row + (uint32_t)(dma.lat ^ (16 * (k & 3))), dst);
+        row += C::WAVES * rs;
+        dst += C::WAVES * (C::DC * C::ESZ);
+      }
       return;
     }
   }
@@ -218,7 +241,7 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, MLA_LDS char* 
 #pragma unroll
       for (int k = 0; k < C::T / C::WAVES; ++k) {
         const int t = k * C::WAVES + wave;
-        const char* g = base + tr.row(t) * rs + ((lane ^ swz<64>(t)) << 4);
+        const char* g = base + tr.row(t) * rs + (uint32_t)(dma.lat ^ (16 * (k & 3)));
         load16_to_lds(g, buf + t * (C::DC * C::ESZ));
       }
     } else {
@@ -263,40 +286,59 @@ __device__ __forceinline__ void commit_tile(MLA_LDS char* buf, const Fp8Stage<C>
   }
 }
 
-// Per-lane LDS byte offsets, computed once. Every tile-buffer read of the loop
-// is one of these plus a compile-time constant (the DS instruction's
-// immediate offset). The XOR key only touches the low 4 bits of a chunk index.
+// Per-lane LDS byte offsets of the tile-buffer reads (16-bit cache layouts).
+// The swizzle keys only flip address bits below the bits that select the
+// fragment, so every read of the loop is one of these bases XOR a constant
+// (the fragment's position inside a 256-byte window) plus a constant (the
+// DS instruction's immediate offset). Five registers instead of one per read.
 template <class C>
 struct LaneOffs {
-  int qk_lat[8];     // latent k block kc:  qk_lat[kc & 7] + 256 * (kc >> 3)
-  int qk_rope[4];    // rotary k block kk:  qk_rope[kk]
-  int pv[2][4];      // C_KV^T fragment j of this wave's slice, k step u, half q:
-                     //   pv[q][j & 3] + ROWB * 16u + 256 * (j >> 2)
+  int lat;     // latent score operand of k block kc:  (lat ^ 32 (kc & 7)) + 256 (kc >> 3)
+  int rope;    // rotary score operand of k block kk:  rope ^ 32 kk
+  int pv[2];   // C_KV^T fragment j, k step u, half q: (pv[q] ^ 64 (j & 3)) + ROWB 16u + 256 (j >> 2)
+  int p;       // P^T of head 32 hb + r, k step u:     (p ^ 32 u) + 32 hb PROW
 };
 
 template <class C>
 __device__ __forceinline__ LaneOffs<C> lane_offsets(int wave) {
-  LaneOffs<C> o;
-  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
-  constexpr int ROWB = C::DC * C::ESZ;
-  const int kr = swz<C::LAT_CH>(r);
+  LaneOffs<C> o{};
+  if constexpr (!C::F32) {
+    static_assert(C::LAT_CH == 64 && C::ROPE_CH == 8 && C::DR * C::ESZ == 128 && C::PROW == 64,
+                  "the XOR forms below assume 1 KiB latent rows, 128-byte rotary rows, 64-byte P rows");
+    const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+    constexpr int ROWB = C::DC * C::ESZ;
+    // chunk (2 kb + hh) ^ key = 2 kb ^ (hh ^ key): the k block flips bits 5.. of the byte offset
+    o.lat = r * ROWB + 16 * (hh ^ swz<C::LAT_CH>(r));
+    o.rope = C::LAT_BYTES + r * (C::DR * C::ESZ) + 16 * (hh ^ swz<C::ROPE_CH>(r));
+    // transposing reads: source lane (a, e) of 16-lane group `sub` points at
+    // token 16u + 8q + 4hh + e, features wave*FPW + 32j + 16*sub + 4a .. +3,
+    // i.e. chunk (4j + 2 sub + a/2) ^ key: j flips bits 6..7 of the byte offset
+    const int s16 = lane & 15, a4 = s16 & 3, e4 = s16 >> 2, sub = (lane >> 4) & 1;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o.qk_lat[j] = r * ROWB + 16 * ((2 * j + hh) ^ kr);
-  const int kq = swz<C::ROPE_CH>(r);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) o.qk_rope[j] = C::LAT_BYTES + r * (C::DR * C::ESZ) + 16 * ((2 * j + hh) ^ kq);
-  // transposing reads: source lane (a, e) of 16-lane group `sub` points at
-  // token 16u + 8q + 4hh + e, features wave*FPW + 32j + 16*sub + 4a .. +3
-  const int s16 = lane & 15, a4 = s16 & 3, e4 = s16 >> 2, sub = (lane >> 4) & 1;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int kt = swz<C::LAT_CH>(8 * q + 4 * hh + e4);   // = key of 16u + 8q + 4hh + e4
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o.pv[q][j] = (8 * q + 4 * hh + e4) * ROWB + 16 * ((4 * j + 2 * sub + (a4 >> 1)) ^ kt) +
-                   8 * (a4 & 1) + 2 * wave * C::FPW;
+    for (int q = 0; q < 2; ++q) {
+      const int tok = 8 * q + 4 * hh + e4;
+      o.pv[q] = tok * ROWB + 16 * ((2 * sub + (a4 >> 1)) ^ swz<C::LAT_CH>(tok)) + 8 * (a4 & 1) +
+                2 * wave * C::FPW;
+    }
+    o.p = r * C::PROW + 16 * (hh ^ ((r >> 2) & 3));
   }
   return o;
+}
+
+// The bases are made opaque once per tile so that the compiler recomputes the
+// XORs next to their reads instead of keeping every offset live in a register.
+template <class C>
+__device__ __forceinline__ void refresh(LaneOffs<C>& lo) {
+  asm volatile("" : "+v"(lo.lat), "+v"(lo.rope), "+v"(lo.pv[0]), "+v"(lo.pv[1]), "+v"(lo.p));
+}
+
+template <class C>
+__device__ __forceinline__ int pv_off(const LaneOffs<C>& lo, int q, int j, int u) {
+  return (lo.pv[q] ^ (64 * (j & 3))) + C::DC * C::ESZ * 16 * u + 256 * (j >> 2);
+}
+template <class C>
+__device__ __forceinline__ int p_rd_off(const LaneOffs<C>& lo, int hb, int u) {
+  return (lo.p ^ (32 * u)) + 32 * hb * C::PROW;
 }
 
 template <class C>
@@ -309,9 +351,9 @@ template <class C>
 struct State {
   f32x16 o[C::NFJ][C::HB];   // O^T: this wave's feature fragments x all head blocks
   float m_ref;     // reference maximum the exponentials are taken against (own heads)
-  float m_max;     // largest base-2 scaled score seen so far
+  float m_max;     // this lane's largest base-2 scaled score
   float l;         // this lane's share of the softmax denominator
-  bool overflow;   // a score exceeded m_ref by more than kHeadroom
+  bool overflow;   // one of this lane's scores exceeded m_ref by more than kHeadroom
 };
 
 // Scores may exceed the reference maximum by up to 2^kHeadroom before the
@@ -322,20 +364,63 @@ struct State {
 // split is recomputed with the true maximum as reference.
 constexpr float kHeadroom = 64.0f;
 
-// Scores of this wave's heads for one tile, online softmax, P^T to LDS.
+// Raw scores of one tile for this wave's 32 heads: lane (hh, c) holds tokens
+// 8j + 4hh + i (accumulator 4j + i) of head 32*wave + c. The e4m3 cache keeps
+// the latent part apart: it still has to be multiplied by the token's scale.
 template <class C>
-__device__ __forceinline__ void scores_tile(const MLA_LDS char* buf, MLA_LDS char* pbuf, const QFrag<C>& q,
-                                            State<C>& s, const LaneOffs<C>& lo, int nvalid,
-                                            float scale_log2) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
+struct Scores {
+  f32x16 lat, rope;
+};
 
-  // ---- S^T = Rows . Q^T : lane (hh, c) gets tokens 8j + 4hh + i of head c ----
-  f32x16 sl = {}, sr = {};
+template <class C>
+__device__ __forceinline__ bf16x8 qk_operand(const MLA_LDS char* buf, const LaneOffs<C>& lo, int kc) {
+  const int off = kc >= C::NKC_LAT ? (lo.rope ^ (32 * (kc - C::NKC_LAT)))
+                                   : (lo.lat ^ (32 * (kc & 7))) + 256 * (kc >> 3);
+  return *(const MLA_LDS bf16x8*)(buf + off);
+}
+
+// One latent-sum accumulator lives in VGPRs. A wave's latent-sum accumulators
+// would fill all 256 AGPRs, and the MFMA builtins keep every accumulator in
+// AGPRs, so the score accumulator would not fit and the register allocator
+// would shuttle accumulators between the register files every tile. The
+// product for the last fragment is therefore issued with VGPR operands.
+// Dependent products that accumulate into exactly the same registers need no
+// wait states; VALU reads of the result wait for vgpr_acc_drain().
+__device__ __forceinline__ void mfma_vgpr_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// More wait states than the longest MFMA needs before VALU reads its result.
+__device__ __forceinline__ void vgpr_acc_drain(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+
+template <class C>
+__device__ __forceinline__ void pv_mfma(State<C>& s, int j, int hb, const bf16x8& a, const bf16x8& b) {
+  if (j == C::NFJ - 1 && hb == C::HB - 1) mfma_vgpr_acc(s.o[j][hb], a, b);
+  else s.o[j][hb] = mfma32x32x16(a, b, s.o[j][hb]);
+}
+
+template <class C>
+__device__ __forceinline__ void qk_mfma(Scores<C>& sc, const bf16x8& a, const QFrag<C>& q, int kc) {
+  if (C::FP8 && kc >= C::NKC_LAT) sc.rope = mfma32x32x16(a, q.v[kc], sc.rope);
+  else sc.lat = mfma32x32x16(a, q.v[kc], sc.lat);
+}
+
+
+
+// S^T = Rows . Q^T for one tile (k = all d_c + d_rope columns).
+template <class C>
+__device__ __forceinline__ Scores<C> qk_tile(const MLA_LDS char* __restrict__ buf, const QFrag<C>& q,
+                                             const LaneOffs<C>& lo) {
+  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+  Scores<C> sc;
+  sc.lat = f32x16{};
+  sc.rope = f32x16{};
+  if constexpr (C::F32) {
 #pragma unroll
-  for (int kc = 0; kc < C::NKC; ++kc) {
-    const bool rope_part = kc >= C::NKC_LAT;
-    const int kk = rope_part ? kc - C::NKC_LAT : kc;
-    if constexpr (C::F32) {
+    for (int kc = 0; kc < C::NKC; ++kc) {
+      const bool rope_part = kc >= C::NKC_LAT;
+      const int kk = rope_part ? kc - C::NKC_LAT : kc;
       float a[8];
       const int byte = (16 * kk + 8 * hh) * 4;
       const int o0 = rope_part ? rope_off<C>(r, byte) : lat_off<C>(r, byte);
@@ -344,85 +429,26 @@ __device__ __forceinline__ void scores_tile(const MLA_LDS char* buf, MLA_LDS cha
       const f32x4 x1 = *(const MLA_LDS f32x4*)(buf + o1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) { a[e] = x0[e]; a[4 + e] = x1[e]; }
-      sl = mfma32x32x16_f32(a, q.v[kc], sl);
-    } else {
-      (void)kk;
+      sc.lat = mfma32x32x16_f32(a, q.v[kc], sc.lat);
     }
-  }
-  if constexpr (!C::F32) {
-    // K fragments are read three blocks ahead of the MFMA that consumes them
-    auto ld = [&](int kc) -> bf16x8 {
-      const int off = kc >= C::NKC_LAT ? lo.qk_rope[kc - C::NKC_LAT]
-                                       : lo.qk_lat[kc & 7] + 256 * (kc >> 3);
-      return *(const MLA_LDS bf16x8*)(buf + off);
-    };
-    bf16x8 a0 = ld(0), a1 = ld(1), a2 = ld(2);
+  } else {
+    // operands are read three k blocks ahead of the MFMA that consumes them
+    bf16x8 a0 = qk_operand<C>(buf, lo, 0), a1 = qk_operand<C>(buf, lo, 1), a2 = qk_operand<C>(buf, lo, 2);
 #pragma unroll
     for (int kc = 0; kc < C::NKC; ++kc) {
-      const bf16x8 a3 = kc + 3 < C::NKC ? ld(kc + 3) : bf16x8{};
-      if (C::FP8 && kc >= C::NKC_LAT) sr = mfma32x32x16(a0, q.v[kc], sr);
-      else sl = mfma32x32x16(a0, q.v[kc], sl);
+      const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(buf, lo, kc + 3) : bf16x8{};
+      qk_mfma<C>(sc, a0, q, kc);
       a0 = a1; a1 = a2; a2 = a3;
     }
   }
-
-  // ---- online softmax (base 2) ----
-  float x[16];
-  float tok_scale[16];
-  if constexpr (C::FP8) {
-    const MLA_LDS float* sc = (const MLA_LDS float*)(buf + C::LAT_BYTES + C::ROPE_BYTES);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 v = *(const MLA_LDS f32x4*)(sc + 8 * j + 4 * hh);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tok_scale[4 * j + i] = v[i];
-    }
-  }
-  float mt = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
-    float v = C::FP8 ? (tok_scale[i] * sl[i] + sr[i]) : sl[i];
-    v *= scale_log2;
-    x[i] = tok < nvalid ? v : -INFINITY;
-    mt = fmaxf(mt, x[i]);
-  }
-  mt = wave_max32(mt);
-  if (s.m_ref == -INFINITY) s.m_ref = mt;     // first tile of the first pass
-  s.m_max = fmaxf(s.m_max, mt);
-  s.overflow = s.overflow || (mt > s.m_ref + kHeadroom);
-  float pr[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    pr[i] = x[i] == -INFINITY ? 0.0f : fast_exp2(x[i] - s.m_ref);
-    s.l += pr[i];
-    if constexpr (C::FP8) pr[i] *= tok_scale[i];
-  }
-
-  // ---- P^T rows of this wave's heads: element e of k step u is token
-  //      16u + 8(e/4) + 4hh + e%4, i.e. pr[8u + e] ----
-  const int head = 32 * wave + r;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    if constexpr (C::F32) {
-      f32x4 v0, v1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { v0[e] = pr[8 * u + e]; v1[e] = pr[8 * u + 4 + e]; }
-      *(MLA_LDS f32x4*)(pbuf + p_off<C>(head, 4 * u + 2 * hh)) = v0;
-      *(MLA_LDS f32x4*)(pbuf + p_off<C>(head, 4 * u + 2 * hh + 1)) = v1;
-    } else {
-      u32x4 v;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) v[d] = pack_bf16x2(pr[8 * u + 2 * d], pr[8 * u + 2 * d + 1]);
-      *(MLA_LDS u32x4*)(pbuf + p_off<C>(head, 2 * u + hh)) = v;
-    }
-  }
+  return sc;
 }
 
 // O^T[this wave's features, all heads] += C_KV^T . P^T for one tile.
 template <class C>
-__device__ __forceinline__ void latent_sum_tile(const MLA_LDS char* buf, const MLA_LDS char* pbuf,
-                                                State<C>& s, const LaneOffs<C>& lo) {
+__device__ __forceinline__ void latent_sum_tile(const MLA_LDS char* __restrict__ buf,
+                                                const MLA_LDS char* __restrict__ pbuf, State<C>& s,
+                                                const LaneOffs<C>& lo) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -450,17 +476,133 @@ __device__ __forceinline__ void latent_sum_tile(const MLA_LDS char* buf, const M
       bf16x8 a[C::NFJ];
 #pragma unroll
       for (int j = 0; j < C::NFJ; ++j) {
-        const int off = ROWB * 16 * u + 256 * (j >> 2);
-        const bf16x4 v0 = lds_read_tr16(buf + lo.pv[0][j & 3] + off);
-        const bf16x4 v1 = lds_read_tr16(buf + lo.pv[1][j & 3] + off);
+        const bf16x4 v0 = lds_read_tr16(buf + pv_off<C>(lo, 0, j, u));
+        const bf16x4 v1 = lds_read_tr16(buf + pv_off<C>(lo, 1, j, u));
         a[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
       for (int hb = 0; hb < C::HB; ++hb) {
-        const bf16x8 pb = *(const MLA_LDS bf16x8*)(pbuf + p_off<C>(32 * hb + r, 2 * u + hh));
+        const bf16x8 pb = *(const MLA_LDS bf16x8*)(pbuf + p_rd_off<C>(lo, hb, u));
 #pragma unroll
-        for (int j = 0; j < C::NFJ; ++j) s.o[j][hb] = mfma32x32x16(a[j], pb, s.o[j][hb]);
+        for (int j = 0; j < C::NFJ; ++j) pv_mfma<C>(s, j, hb, a[j], pb);
       }
+    }
+  }
+}
+
+// The two contractions of the steady state in one instruction stream: the
+// scores of tile t (operands from `cur`) and the latent sum of tile t - 1
+// (`prev`, with its probabilities in `pr`) are independent, so their MFMAs
+// alternate and the LDS reads of one hide behind the products of the other.
+template <class C>
+__device__ __forceinline__ Scores<C> qk_and_latent_sum(const MLA_LDS char* __restrict__ cur,
+                                                       const MLA_LDS char* __restrict__ prev,
+                                                       const MLA_LDS char* __restrict__ pr,
+                                                       const QFrag<C>& q, State<C>& s,
+                                                       const LaneOffs<C>& lo) {
+  if constexpr (C::F32) {
+    Scores<C> sc = qk_tile<C>(cur, q, lo);
+    latent_sum_tile<C>(prev, pr, s, lo);
+    return sc;
+  } else {
+    const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+    constexpr int ROWB = C::DC * C::ESZ;
+    constexpr int PV_STEPS = 2 * C::HB * C::NFJ;
+    static_assert(PV_STEPS <= C::NKC, "every latent-sum MFMA pairs with a score MFMA");
+    Scores<C> sc;
+    sc.lat = f32x16{};
+    sc.rope = f32x16{};
+    bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16x8 va[C::NFJ];
+#pragma unroll
+      for (int j = 0; j < C::NFJ; ++j) {
+        const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
+        const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
+        va[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+#pragma unroll
+      for (int hb = 0; hb < C::HB; ++hb) {
+        const bf16x8 pb = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, hb, u));
+#pragma unroll
+        for (int j = 0; j < C::NFJ; ++j) {
+          const int kc = (u * C::HB + hb) * C::NFJ + j;
+          const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
+          qk_mfma<C>(sc, a0, q, kc);
+          a0 = a1; a1 = a2; a2 = a3;
+          pv_mfma<C>(s, j, hb, va[j], pb);
+        }
+      }
+    }
+#pragma unroll
+    for (int kc = PV_STEPS; kc < C::NKC; ++kc) {
+      const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
+      qk_mfma<C>(sc, a0, q, kc);
+      a0 = a1; a1 = a2; a2 = a3;
+    }
+    return sc;
+  }
+}
+
+// Streaming softmax of one tile (base 2, fixed reference) and P^T to LDS.
+// `first` (uniform): the first tile of the first pass sets the reference.
+template <class C>
+__device__ __forceinline__ void softmax_tile(const MLA_LDS char* __restrict__ buf, MLA_LDS char* __restrict__ pbuf,
+                                             const Scores<C>& sc, State<C>& s, int nvalid, float scale_log2,
+                                             bool first) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
+  float tok_scale[16];
+  if constexpr (C::FP8) {
+    const MLA_LDS float* scl = (const MLA_LDS float*)(buf + C::LAT_BYTES + C::ROPE_BYTES);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v = *(const MLA_LDS f32x4*)(scl + 8 * j + 4 * hh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tok_scale[4 * j + i] = v[i];
+    }
+  }
+  float x[16];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
+    float v = C::FP8 ? (tok_scale[i] * sc.lat[i] + sc.rope[i]) : sc.lat[i];
+    v *= scale_log2;
+    x[i] = tok < nvalid ? v : -INFINITY;
+    mt = fmaxf(mt, x[i]);
+  }
+  if (first) s.m_ref = wave_max32(mt);    // lanes r and r + 32 hold one head
+  s.m_max = fmaxf(s.m_max, mt);
+  s.overflow = s.overflow || (mt > s.m_ref + kHeadroom);
+  float pr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pr[i] = fast_exp2(x[i] - s.m_ref);   // masked: exp2(-inf) = 0
+  float q4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q4[j] = (pr[4 * j] + pr[4 * j + 1]) + (pr[4 * j + 2] + pr[4 * j + 3]);
+  s.l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
+  if constexpr (C::FP8) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pr[i] *= tok_scale[i];
+  }
+
+  // P^T rows of this wave's heads: element e of k step u is token
+  // 16u + 8(e/4) + 4hh + e%4, i.e. pr[8u + e].
+  const int head = 32 * wave + r;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if constexpr (C::F32) {
+      f32x4 v0, v1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v0[e] = pr[8 * u + e]; v1[e] = pr[8 * u + 4 + e]; }
+      *(MLA_LDS f32x4*)(pbuf + p_off<C>(head, 4 * u + 2 * hh)) = v0;
+      *(MLA_LDS f32x4*)(pbuf + p_off<C>(head, 4 * u + 2 * hh + 1)) = v1;
+    } else {
+      u32x4 v;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) v[d] = pack_bf16x2(pr[8 * u + 2 * d], pr[8 * u + 2 * d + 1]);
+      *(MLA_LDS u32x4*)(pbuf + p_off<C>(head, 2 * u + hh)) = v;
     }
   }
 }
@@ -468,6 +610,7 @@ __device__ __forceinline__ void latent_sum_tile(const MLA_LDS char* buf, const M
 template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
   else static_assert(N == 0, "add the vmcnt value here");
@@ -480,34 +623,44 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// One tile of the loop. The buffers are distinct ring slots: `cur` is read,
-// `next` (the following tile) may still be receiving its data, `ahead` is
-// refilled. __restrict__ tells the compiler that reading `cur` does not have
-// to wait for the loads into the other slots; the explicit vmcnt wait before
-// the barrier is what makes the following tile resident.
-template <class C, bool PAGED>
+// One step of the software-pipelined tile loop, t = 0 .. ntiles - 1:
+//   (bf16) start loading tile t + 2 into the slot freed by tile t - 2;
+//   scores of tile t, interleaved with the latent sum of tile t - 1 (t > 0);
+//   softmax of tile t, P^T(t) to LDS;
+//   make tile t + 1 resident (e4m3: widen it into its slot and start tile t + 2);
+//   barrier.
+// The ring slots are distinct buffers (for the three-slot e4m3 ring, `fill`
+// and `prev` share a slot, but only the rotary/scale part of `fill` and only
+// the latent part of `prev` are touched). __restrict__ tells the compiler
+// that LDS reads of one slot need not wait for the loads into another; the
+// explicit vmcnt wait before the barrier is what makes tile t + 1 resident.
+template <class C, bool PAGED, bool FIRST>
 __device__ __forceinline__ void tile_step(const DecodeParams& p, const MLA_LDS char* __restrict__ cur,
-                                          MLA_LDS char* __restrict__ pbuf, MLA_LDS char* __restrict__ next,
-                                          MLA_LDS char* __restrict__ ahead, const QFrag<C>& q, State<C>& s,
-                                          const LaneOffs<C>& lo, Fp8Stage<C>& st, int b, int it, int ntiles,
-                                          int start, int end) {
+                                          const MLA_LDS char* __restrict__ prev, MLA_LDS char* __restrict__ next,
+                                          MLA_LDS char* __restrict__ fill, MLA_LDS char* __restrict__ pw,
+                                          const MLA_LDS char* __restrict__ pr, const QFrag<C>& q, State<C>& s,
+                                          LaneOffs<C>& lo, const SeqView& sv, DmaOffs& dma, Fp8Stage<C>& st,
+                                          int t, int ntiles, int start, int end, bool first) {
   constexpr int LPT = loads_per_tile<C>();
-  scores_tile<C>(cur, pbuf, q, s, lo, end - (start + it * C::T), p.scale_log2);
-  // make tile it + 1 resident; later tiles may stay in flight
-  if (it + 1 < ntiles) {
+  refresh<C>(lo);
+  asm volatile("" : "+v"(dma.lat));
+  if constexpr (!C::FP8)
+    if (t + 2 < ntiles) issue_tile<C, PAGED>(p, sv, dma, fill, start + (t + 2) * C::T, end, st);
+  Scores<C> sc;
+  if constexpr (FIRST) sc = qk_tile<C>(cur, q, lo);
+  else sc = qk_and_latent_sum<C>(cur, prev, pr, q, s, lo);
+  softmax_tile<C>(cur, pw, sc, s, end - (start + t * C::T), p.scale_log2, first);
+  if (t + 1 < ntiles) {
     if constexpr (C::FP8) {
       wait_vmem_le<0>();
       commit_tile<C>(next, st);
+      if (t + 2 < ntiles) issue_tile<C, PAGED>(p, sv, dma, fill, start + (t + 2) * C::T, end, st);
     } else {
-      if (C::AHEAD >= 2 && it + 2 < ntiles) wait_vmem_le<LPT>();
+      if (t + 2 < ntiles) wait_vmem_le<LPT>();
       else wait_vmem_le<0>();
     }
   }
-  // P^T of every head written; tile it + 1 resident; nobody reads tile it - 1
   tile_barrier();
-  const int nxt = it + 1 + C::AHEAD;
-  if (nxt < ntiles) issue_tile<C, PAGED>(p, ahead, b, start + nxt * C::T, end, st);
-  latent_sum_tile<C>(cur, pbuf, s, lo);
 }
 
 template <class C>
@@ -531,7 +684,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   const int head = wave * 32 + r;
   MLA_LDS char* lds = (MLA_LDS char*)smem;
   MLA_LDS char* pbase = lds + C::NBUF * C::BUF_BYTES;
-  const bool f32_out = p.num_splits > 1 || !p.out_bf16;
+  const bool f32_out = !p.out_bf16;
 
   if (start >= end) {             // uniform over the workgroup: no tokens
     if (head < C::H) {
@@ -579,8 +732,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   }
 
   Fp8Stage<C> st;
-  const LaneOffs<C> lo = lane_offsets<C>(wave);
+  LaneOffs<C> lo = lane_offsets<C>(wave);
+  const SeqView sv = seq_view<PAGED>(p, b);
+  DmaOffs dma;
+  {
+    const int tr_ = threadIdx.x / C::ROPE_CH, cr = (threadIdx.x % C::ROPE_CH) ^ swz<C::ROPE_CH>(tr_);
+    dma.lat = (lane ^ (wave << 2)) << 4;
+    dma.rope = (int)(tr_ * (p.row_stride * C::ESZ)) + C::DC * C::ESZ + cr * 16;
+  }
   const int ntiles = (end - start + C::T - 1) / C::T;
+  constexpr int LPT = loads_per_tile<C>();
+  auto slot = [&](int x) -> MLA_LDS char* { return lds + (x % C::NBUF) * C::BUF_BYTES; };   // x >= 0
+  auto pslot = [&](int x) -> MLA_LDS char* { return pbase + (x & 1) * C::P_BYTES; };
 
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {   // recompute with the true maximum as reference
@@ -589,26 +752,35 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int hb = 0; hb < C::HB; ++hb) s.o[j][hb] = f32x16{};
       s.l = 0.0f;
-      s.m_ref = s.m_max;
+      s.m_ref = fmaxf(s.m_max, __shfl_xor(s.m_max, 32));
+      s.overflow = false;
     }
-    // prologue: tile 0 resident, tiles 1 .. AHEAD in flight
-    issue_tile<C, PAGED>(p, lds, b, start, end, st);
-    wait_vmem_le<0>();
-    commit_tile<C>(lds, st);
-#pragma unroll
-    for (int k = 1; k <= C::AHEAD; ++k)
-      if (k < ntiles) issue_tile<C, PAGED>(p, lds + k * C::BUF_BYTES, b, start + k * C::T, end, st);
-    __syncthreads();
+    // prologue: tile 0 resident, tile 1 in flight
+    issue_tile<C, PAGED>(p, sv, dma, slot(0), start, end, st);
+    if constexpr (C::FP8) {
+      wait_vmem_le<0>();
+      commit_tile<C>(slot(0), st);
+      if (ntiles > 1) issue_tile<C, PAGED>(p, sv, dma, slot(1), start + C::T, end, st);
+    } else {
+      if (ntiles > 1) {
+        issue_tile<C, PAGED>(p, sv, dma, slot(1), start + C::T, end, st);
+        wait_vmem_le<LPT>();
+      } else {
+        wait_vmem_le<0>();
+      }
+    }
+    tile_barrier();
 
-    for (int it = 0; it < ntiles; ++it) {
-      tile_step<C, PAGED>(p, lds + (it % C::NBUF) * C::BUF_BYTES, pbase + (it & 1) * C::P_BYTES,
-                          lds + ((it + 1) % C::NBUF) * C::BUF_BYTES,
-                          lds + ((it + 1 + C::AHEAD) % C::NBUF) * C::BUF_BYTES, q, s, lo, st, b, it,
-                          ntiles, start, end);
-    }
+    tile_step<C, PAGED, true>(p, slot(0), slot(C::NBUF - 1), slot(1), slot(2), pslot(0), pslot(1), q, s, lo,
+                              sv, dma, st, 0, ntiles, start, end, pass == 0);
+    for (int t = 1; t < ntiles; ++t)
+      tile_step<C, PAGED, false>(p, slot(t), slot(t - 1), slot(t + 1), slot(t + 2), pslot(t), pslot(t - 1), q,
+                                 s, lo, sv, dma, st, t, ntiles, start, end, false);
+    latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
+    if constexpr (!C::F32) vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
     __syncthreads();
     if (pass == 1) break;
-    // did any wave's scores outrun the headroom? (uniform decision)
+    // did any lane's scores outrun the headroom? (uniform decision)
     MLA_LDS int* redo = (MLA_LDS int*)pbase;
     const bool wave_overflow = __ballot(s.overflow) != 0;
     if (lane == 0) redo[wave] = wave_overflow ? 1 : 0;

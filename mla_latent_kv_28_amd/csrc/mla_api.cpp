@@ -117,7 +117,6 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, co
   if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
   if (sh == Shape::kDsv2 && cache->dtype == MLA_F32) return MLA_ERR_DTYPE;
   if (sh == Shape::kTiny && cache->dtype != MLA_F32) return MLA_ERR_DTYPE;
-  if (num_splits > 1 && out_dtype != MLA_F32) return MLA_ERR_DTYPE;   // partials are f32
   if (!std::isfinite(sm_scale)) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!q_lat || !seq_lens || !out || !lse || !cache->latent) return MLA_ERR_NULL;
@@ -137,9 +136,11 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, co
   if (cache->row_stride < width) return MLA_ERR_SHAPE;
   const int64_t elem = cache->dtype == MLA_F32 ? 4 : (fp8 ? 1 : 2);
   if ((cache->row_stride * elem) % 16 != 0) return MLA_ERR_ALIGN;
+  if (cache->row_stride * elem > (int64_t{1} << 24)) return MLA_ERR_UNSUPPORTED;
   if (fp8) {
     if (cache->rope_stride < dims->d_rope) return MLA_ERR_SHAPE;
     if ((cache->rope_stride * 2) % 16 != 0) return MLA_ERR_ALIGN;
+    if (cache->rope_stride * 2 > (int64_t{1} << 24)) return MLA_ERR_UNSUPPORTED;
     if (!aligned16(cache->rope)) return MLA_ERR_ALIGN;
   }
   if (!aligned16(q_lat) || !aligned16(cache->latent) || !aligned16(out) || !aligned16(lse))
@@ -174,11 +175,13 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, co
   return hip_status(e);
 }
 
-mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const float* o_part,
-                       const float* lse_part, void* out, float* lse, int32_t out_dtype, mla_stream stream) {
+mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const void* o_part,
+                       int32_t part_dtype, const float* lse_part, void* out, float* lse, int32_t out_dtype,
+                       mla_stream stream) {
   if (dims == nullptr) return MLA_ERR_NULL;
   if (batch < 0 || num_splits < 1) return MLA_ERR_SHAPE;
   if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (part_dtype != MLA_F32 && part_dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (shape_of(dims) == Shape::kNone) return MLA_ERR_UNSUPPORTED;
   if (num_splits > mla::combine_max_splits()) return MLA_ERR_UNSUPPORTED;
   if (batch == 0) return MLA_OK;
@@ -194,6 +197,7 @@ mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, 
   p.heads = dims->num_heads;
   p.d_latent = dims->d_latent;
   p.out_bf16 = out_dtype == MLA_BF16;
+  p.part_bf16 = part_dtype == MLA_BF16;
   return hip_status(mla::launch_combine(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -25,9 +25,9 @@ struct DecodeParams {
   int32_t num_splits;
   int32_t chunk;                // tokens per split, multiple of the tile
   float scale_log2;             // sm_scale * log2(e)
-  void* out;                    // S == 1: [B, H, DC] (bf16 | f32); S > 1: [B, S, H, DC] f32
+  void* out;                    // S == 1: [B, H, DC]; S > 1: [B, S, H, DC] (bf16 | f32)
   float* lse;                   // S == 1: [B, H]; S > 1: [B, S, H]
-  int32_t out_bf16;             // S == 1 only
+  int32_t out_bf16;             // out is bf16 (else f32)
   int32_t xcd_remap;            // 1: keep a sequence's splits on one XCD
 };
 
@@ -37,12 +37,13 @@ hipError_t launch_decode_dsv2_fp8(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_tiny_f32(const DecodeParams& p, hipStream_t s);
 
 struct CombineParams {
-  const float* o_part;   // [B, S, H, DC]
+  const void* o_part;    // [B, S, H, DC] (bf16 | f32)
   const float* lse_part; // [B, S, H]
   void* out;             // [B, H, DC]
   float* lse;            // [B, H] or null
   int32_t batch, splits, heads, d_latent;
   int32_t out_bf16;
+  int32_t part_bf16;
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 

@@ -18,7 +18,8 @@ class DecodePipeline:
     `inp` is any object with the fields of mla_synth.Inputs (dims, dtype,
     seq_lens, sm_scale, q_nope, q_rope, w_uk, w_uv, rows or codes/scale/rope,
     layout, seq_stride, page_size, block_table).
-    o_lat_dtype: precision of the merged latent output handed to out-proj.
+    o_lat_dtype: precision of the merged latent output handed to out-proj, and
+                 of the split partials when there is more than one split.
     out_dtype:   precision of the final per-head output.
     """
 
@@ -64,7 +65,7 @@ class DecodePipeline:
         fdt = torch.float32 if self.out_dtype == F32 else torch.bfloat16
         self.q_lat = torch.empty((B, H, d.width), dtype=cdt, device=dev)
         if S > 1:
-            self.o_part = torch.empty((B, S, H, d.d_latent), dtype=torch.float32, device=dev)
+            self.o_part = torch.empty((B, S, H, d.d_latent), dtype=odt, device=dev)
             self.lse_part = torch.empty((B, S, H), dtype=torch.float32, device=dev)
         else:
             self.o_part = self.lse_part = None
@@ -80,7 +81,7 @@ class DecodePipeline:
         if self.num_splits > 1:
             mla_decode(self.dims, self.batch, self.q_lat, self.cache, self.seq_lens,
                        self.max_seq_len, self.sm_scale, self.num_splits, self.o_part,
-                       self.lse_part, F32, stream)
+                       self.lse_part, self.o_lat_dtype, stream)
         else:
             mla_decode(self.dims, self.batch, self.q_lat, self.cache, self.seq_lens,
                        self.max_seq_len, self.sm_scale, 1, self.o_lat, self.lse,
@@ -88,8 +89,8 @@ class DecodePipeline:
 
     def combine(self, stream=None):
         if self.num_splits > 1:
-            mla_combine(self.dims, self.batch, self.num_splits, self.o_part, self.lse_part,
-                        self.o_lat, self.lse, self.o_lat_dtype, stream)
+            mla_combine(self.dims, self.batch, self.num_splits, self.o_part, self.o_lat_dtype,
+                        self.lse_part, self.o_lat, self.lse, self.o_lat_dtype, stream)
 
     def out_proj(self, stream=None):
         mla_out_proj(self.dims, self.batch, self.o_lat, self.o_lat_dtype, self.w_uv,

@@ -105,7 +105,7 @@ def test_decode_argument_errors(L):
     assert _decode(L, cache=_cache(dtype=mla.F32)) == -3          # f32 cache needs the tiny shape
     assert _decode(L, dims=TINY, cache=_cache(dtype=mla.BF16, row_stride=48, seq_stride=64),
                    max_len=64) == -3
-    assert _decode(L, splits=4, out_dtype=mla.BF16) == -3          # partials are f32
+    assert _decode(L, cache=_cache(row_stride=1 << 24)) == -4      # rows beyond 2^24 bytes
     assert _decode(L, out_dtype=mla.FP8_E4M3) == -3
     assert _decode(L, q=None) == -1
     assert _decode(L, lens=None) == -1
@@ -138,12 +138,13 @@ def test_absorb_combine_outproj_argument_errors(L):
                           mla.BF16, None) == -4
     assert L.mla_absorb_q(d, 0, None, None, None, None, mla.BF16, None) == 0
 
-    assert L.mla_combine(None, 1, 2, P, P, P, P, mla.F32, None) == -1
-    assert L.mla_combine(d, 1, 0, P, P, P, P, mla.F32, None) == -2
-    assert L.mla_combine(d, 1, 2000, P, P, P, P, mla.F32, None) == -4
-    assert L.mla_combine(d, 1, 2, P, P, P, P, mla.FP8_E4M3, None) == -3
-    assert L.mla_combine(d, 1, 2, None, P, P, P, mla.F32, None) == -1
-    assert L.mla_combine(d, 1, 2, P + 4, P, P, P, mla.F32, None) == -5
+    assert L.mla_combine(None, 1, 2, P, mla.F32, P, P, P, mla.F32, None) == -1
+    assert L.mla_combine(d, 1, 0, P, mla.F32, P, P, P, mla.F32, None) == -2
+    assert L.mla_combine(d, 1, 2000, P, mla.F32, P, P, P, mla.F32, None) == -4
+    assert L.mla_combine(d, 1, 2, P, mla.F32, P, P, P, mla.FP8_E4M3, None) == -3
+    assert L.mla_combine(d, 1, 2, P, mla.FP8_E4M3, P, P, P, mla.F32, None) == -3
+    assert L.mla_combine(d, 1, 2, None, mla.BF16, P, P, P, mla.F32, None) == -1
+    assert L.mla_combine(d, 1, 2, P + 4, mla.F32, P, P, P, mla.F32, None) == -5
 
     assert L.mla_out_proj(None, 1, P, mla.BF16, P, mla.BF16, P, mla.BF16, None) == -1
     assert L.mla_out_proj(d, 1, P, mla.BF16, P, mla.F32, P, mla.BF16, None) == -3

@@ -247,3 +247,37 @@ def test_full_fp8_b128_l8192():
     for b, h in _pairs(128, 128, 6, 5):
         ro, _ = oracle.decode_one(b=b, h=h, **a)
         assert _rel(out[b, h], ro) <= FP8_REL
+
+
+# --- the split merge on its own, against the oracle's LSE merge ---------------------
+
+@pytest.mark.parametrize("part_dtype", [0, 1])
+@pytest.mark.parametrize("splits", [1, 3, 8, 70])
+def test_combine_against_oracle_merge(splits, part_dtype):
+    import mla_latent_kv_28_amd as mla
+    from mla_synth import DSV2
+    B, H, D = 3, DSV2.num_heads, DSV2.d_latent
+    rng = np.random.default_rng(11 + splits)
+    o = rng.standard_normal((B, splits, H, D))
+    lse = rng.standard_normal((B, splits, H)) * 3.0
+    lse[0, :, :5] = -np.inf                          # heads with no tokens at all
+    if splits > 1:
+        lse[1, 1, :] = -np.inf                       # an empty split holding garbage
+        o[1, 1] = np.nan
+    tdt = torch.float32 if part_dtype == 0 else torch.bfloat16
+    o_dev = torch.from_numpy(o).to(tdt).cuda()
+    o_in = o_dev.double().cpu().numpy()              # the values the kernel reads
+    lse_dev = torch.from_numpy(lse).float().cuda()
+    out = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+    lse_out = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    print("case: combine S=%d part_dtype=%d" % (splits, part_dtype), flush=True)
+    mla.mla_combine(DSV2, B, splits, o_dev, part_dtype, lse_dev, out, lse_out, mla.F32)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.lse_merge(np.moveaxis(np.nan_to_num(o_in, nan=0.0), 1, 0),
+                                    np.moveaxis(lse_dev.double().cpu().numpy(), 1, 0))
+    got = out.double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.all(got[0, :5] == 0) and np.all(lse_out[0, :5].cpu().numpy() == -np.inf)
+    np.testing.assert_allclose(got, ref_o, rtol=0, atol=2e-5 * max(1.0, np.abs(ref_o).max()))
+    fin = np.isfinite(ref_l)
+    np.testing.assert_allclose(lse_out.double().cpu().numpy()[fin], ref_l[fin], rtol=0, atol=2e-5 * 8)
