@@ -490,68 +490,42 @@ __device__ __forceinline__ void latent_sum_tile(const MLA_LDS char* __restrict__
   }
 }
 
-// The two contractions of the steady state in one instruction stream: the
-// scores of tile t (operands from `cur`) and the latent sum of tile t - 1
-// (`prev`, with its probabilities in `pr`) are independent, so their MFMAs
-// alternate and the LDS reads of one hide behind the products of the other.
-template <class C>
-__device__ __forceinline__ Scores<C> qk_and_latent_sum(const MLA_LDS char* __restrict__ cur,
-                                                       const MLA_LDS char* __restrict__ prev,
-                                                       const MLA_LDS char* __restrict__ pr,
-                                                       const QFrag<C>& q, State<C>& s,
-                                                       const LaneOffs<C>& lo) {
-  if constexpr (C::F32) {
-    Scores<C> sc = qk_tile<C>(cur, q, lo);
-    latent_sum_tile<C>(prev, pr, s, lo);
-    return sc;
-  } else {
-    const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
-    constexpr int ROWB = C::DC * C::ESZ;
-    constexpr int PV_STEPS = 2 * C::HB * C::NFJ;
-    static_assert(PV_STEPS <= C::NKC, "every latent-sum MFMA pairs with a score MFMA");
-    Scores<C> sc;
-    sc.lat = f32x16{};
-    sc.rope = f32x16{};
-    bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16x8 va[C::NFJ];
-#pragma unroll
-      for (int j = 0; j < C::NFJ; ++j) {
-        const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
-        const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
-        va[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-#pragma unroll
-      for (int hb = 0; hb < C::HB; ++hb) {
-        const bf16x8 pb = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, hb, u));
-#pragma unroll
-        for (int j = 0; j < C::NFJ; ++j) {
-          const int kc = (u * C::HB + hb) * C::NFJ + j;
-          const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
-          qk_mfma<C>(sc, a0, q, kc);
-          a0 = a1; a1 = a2; a2 = a3;
-          pv_mfma<C>(s, j, hb, va[j], pb);
-        }
-      }
-    }
-#pragma unroll
-    for (int kc = PV_STEPS; kc < C::NKC; ++kc) {
-      const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
-      qk_mfma<C>(sc, a0, q, kc);
-      a0 = a1; a1 = a2; a2 = a3;
-    }
-    return sc;
-  }
-}
-
 // Streaming softmax of one tile (base 2, fixed reference) and P^T to LDS.
-// `first` (uniform): the first tile of the first pass sets the reference.
-template <class C>
+//
+// Rows past the end of a partial tile hold the tile's first token (a real
+// score of this split), so they may take part in the maxima; only their
+// probabilities are zeroed. `first` (uniform): the first tile of the first
+// pass sets the reference. With LATENT_SUM, the latent-sum products of the
+// previous tile (`prev`, probabilities in `pr`) are issued between the
+// softmax's vector instructions: they are independent, and the matrix cores
+// work through them while the vector unit runs the softmax.
+template <class C, bool LATENT_SUM>
 __device__ __forceinline__ void softmax_tile(const MLA_LDS char* __restrict__ buf, MLA_LDS char* __restrict__ pbuf,
-                                             const Scores<C>& sc, State<C>& s, int nvalid, float scale_log2,
+                                             const MLA_LDS char* __restrict__ prev,
+                                             const MLA_LDS char* __restrict__ pr, const Scores<C>& sc,
+                                             State<C>& s, const LaneOffs<C>& lo, int nvalid, float scale_log2,
                                              bool first) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
+  constexpr bool INTERLEAVE = LATENT_SUM && !C::F32;
+  if constexpr (LATENT_SUM && C::F32) latent_sum_tile<C>(prev, pr, s, lo);
+
+  // latent-sum operands and products of k step u (16 tokens of the previous tile)
+  bf16x8 va[C::NFJ];
+  auto pv_load = [&](int u) {
+#pragma unroll
+    for (int j = 0; j < C::NFJ; ++j) {
+      const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
+      const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
+      va[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto pv_block = [&](int u, int hb) {
+    const bf16x8 pb = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, hb, u));
+#pragma unroll
+    for (int j = 0; j < C::NFJ; ++j) pv_mfma<C>(s, j, hb, va[j], pb);
+  };
+  if constexpr (INTERLEAVE) { pv_load(0); pv_block(0, 0); }
+
   float tok_scale[16];
   if constexpr (C::FP8) {
     const MLA_LDS float* scl = (const MLA_LDS float*)(buf + C::LAT_BYTES + C::ROPE_BYTES);
@@ -563,48 +537,62 @@ __device__ __forceinline__ void softmax_tile(const MLA_LDS char* __restrict__ bu
     }
   }
   float x[16];
-  float mt = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
-    float v = C::FP8 ? (tok_scale[i] * sc.lat[i] + sc.rope[i]) : sc.lat[i];
-    v *= scale_log2;
-    x[i] = tok < nvalid ? v : -INFINITY;
-    mt = fmaxf(mt, x[i]);
+    const float v = C::FP8 ? (tok_scale[i] * sc.lat[i] + sc.rope[i]) : sc.lat[i];
+    x[i] = v * scale_log2;
   }
+  if constexpr (INTERLEAVE) pv_block(0, 1);
+  float mt = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
   if (first) s.m_ref = wave_max32(mt);    // lanes r and r + 32 hold one head
   s.m_max = fmaxf(s.m_max, mt);
   s.overflow = s.overflow || (mt > s.m_ref + kHeadroom);
-  float pr[16];
+  if constexpr (INTERLEAVE) pv_block(0, 2);
+  float pr_[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) pr[i] = fast_exp2(x[i] - s.m_ref);   // masked: exp2(-inf) = 0
+  for (int i = 0; i < 8; ++i) pr_[i] = fast_exp2(x[i] - s.m_ref);
+  if constexpr (INTERLEAVE) { pv_block(0, 3); pv_load(1); pv_block(1, 0); }
+#pragma unroll
+  for (int i = 8; i < 16; ++i) pr_[i] = fast_exp2(x[i] - s.m_ref);
+  if constexpr (INTERLEAVE) pv_block(1, 1);
+  if (nvalid < C::T) {    // partial tile (uniform)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
+      pr_[i] = tok < nvalid ? pr_[i] : 0.0f;
+    }
+  }
   float q4[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) q4[j] = (pr[4 * j] + pr[4 * j + 1]) + (pr[4 * j + 2] + pr[4 * j + 3]);
+  for (int j = 0; j < 4; ++j) q4[j] = (pr_[4 * j] + pr_[4 * j + 1]) + (pr_[4 * j + 2] + pr_[4 * j + 3]);
   s.l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
   if constexpr (C::FP8) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) pr[i] *= tok_scale[i];
+    for (int i = 0; i < 16; ++i) pr_[i] *= tok_scale[i];
   }
+  if constexpr (INTERLEAVE) pv_block(1, 2);
 
   // P^T rows of this wave's heads: element e of k step u is token
-  // 16u + 8(e/4) + 4hh + e%4, i.e. pr[8u + e].
+  // 16u + 8(e/4) + 4hh + e%4, i.e. pr_[8u + e].
   const int head = 32 * wave + r;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if constexpr (C::F32) {
       f32x4 v0, v1;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { v0[e] = pr[8 * u + e]; v1[e] = pr[8 * u + 4 + e]; }
+      for (int e = 0; e < 4; ++e) { v0[e] = pr_[8 * u + e]; v1[e] = pr_[8 * u + 4 + e]; }
       *(MLA_LDS f32x4*)(pbuf + p_off<C>(head, 4 * u + 2 * hh)) = v0;
       *(MLA_LDS f32x4*)(pbuf + p_off<C>(head, 4 * u + 2 * hh + 1)) = v1;
     } else {
       u32x4 v;
 #pragma unroll
-      for (int d = 0; d < 4; ++d) v[d] = pack_bf16x2(pr[8 * u + 2 * d], pr[8 * u + 2 * d + 1]);
+      for (int d = 0; d < 4; ++d) v[d] = pack_bf16x2(pr_[8 * u + 2 * d], pr_[8 * u + 2 * d + 1]);
       *(MLA_LDS u32x4*)(pbuf + p_off<C>(head, 2 * u + hh)) = v;
     }
   }
+  if constexpr (INTERLEAVE) pv_block(1, 3);
 }
 
 template <int N>
@@ -625,8 +613,9 @@ __device__ __forceinline__ void tile_barrier() {
 
 // One step of the software-pipelined tile loop, t = 0 .. ntiles - 1:
 //   (bf16) start loading tile t + 2 into the slot freed by tile t - 2;
-//   scores of tile t, interleaved with the latent sum of tile t - 1 (t > 0);
-//   softmax of tile t, P^T(t) to LDS;
+//   scores of tile t;
+//   softmax of tile t, P^T(t) to LDS, interleaved with the latent sum of
+//   tile t - 1 (t > 0);
 //   make tile t + 1 resident (e4m3: widen it into its slot and start tile t + 2);
 //   barrier.
 // The ring slots are distinct buffers (for the three-slot e4m3 ring, `fill`
@@ -646,10 +635,8 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const MLA_LDS c
   asm volatile("" : "+v"(dma.lat));
   if constexpr (!C::FP8)
     if (t + 2 < ntiles) issue_tile<C, PAGED>(p, sv, dma, fill, start + (t + 2) * C::T, end, st);
-  Scores<C> sc;
-  if constexpr (FIRST) sc = qk_tile<C>(cur, q, lo);
-  else sc = qk_and_latent_sum<C>(cur, prev, pr, q, s, lo);
-  softmax_tile<C>(cur, pw, sc, s, end - (start + t * C::T), p.scale_log2, first);
+  const Scores<C> sc = qk_tile<C>(cur, q, lo);
+  softmax_tile<C, !FIRST>(cur, pw, prev, pr, sc, s, lo, end - (start + t * C::T), p.scale_log2, first);
   if (t + 1 < ntiles) {
     if constexpr (C::FP8) {
       wait_vmem_le<0>();

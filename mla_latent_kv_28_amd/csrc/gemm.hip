@@ -3,9 +3,12 @@
 // folded into the query side and W_UV into the output side).
 //   absorb:   q_lat[b,h,n] = sum_k q_nope[b,h,k] * W_UK[h,k,n]   (W stored [K][N])
 //   out-proj: o[b,h,n]     = sum_k o_lat[b,h,k]  * W_UV[h,n,k]   (W stored [N][K])
-// For every head this is a (batch x K) . (K x N) product. One wave computes a
-// 32-row x NT-column block with v_mfma_f32_32x32x16_bf16 (or eight fp32
-// 32x32x2 per 16-wide k block); the weights are streamed once per 32 rows.
+// For every head this is a (batch x K) . (K x N) product with a small batch:
+// the time goes into reading the weights (16.8 MB per call at the
+// DeepSeek-V2 shapes), so the bf16 kernels spread each head's weights over a
+// 256-thread workgroup whose four waves split K, issue all their weight loads
+// at once, keep the weight fragments in registers while they loop over
+// 32-row batch blocks, and add their K-partials through LDS.
 //
 // A weight stored [K][N] (absorb) has N contiguous, but an MFMA B operand
 // needs eight consecutive k of one column per lane. Each lane therefore reads
@@ -146,6 +149,155 @@ __global__ __launch_bounds__(64) void head_gemm(GemmParams p) {
   }
 }
 
+// ---- bf16 absorb: W [K=128][N=512] per head, one workgroup per (head, 256 columns)
+constexpr int kAbsK = 128, kAbsN = 512, kAbsNT = 256;
+
+__global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(GemmParams p) {
+  // K-partials of the four waves: [wave][i][lane][m] fp32, m = fragment
+  __shared__ __attribute__((aligned(16))) float part[4 * 16 * 64 * 8];
+  const int h = blockIdx.x, n0 = blockIdx.y * kAbsNT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, r = lane & 31;
+  constexpr int KCW = kAbsK / 16 / 4;                     // 16-wide k blocks per wave (2)
+
+  // weight fragments of this wave's k blocks: all loads issued before any use
+  u32x4 raw[KCW][8];
+  const __bf16* wh = (const __bf16*)p.w + (int64_t)h * kAbsK * kAbsN;
+#pragma unroll
+  for (int q = 0; q < KCW; ++q) {
+    const int k0 = 16 * (wave * KCW + q) + 8 * hh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) raw[q][e] = load16(wh + (int64_t)(k0 + e) * kAbsN + n0 + 8 * r);
+  }
+  bf16x8 wf[KCW][8];
+#pragma unroll
+  for (int q = 0; q < KCW; ++q)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      u32x4 f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        f[d] = (m & 1) ? pack_hi16(raw[q][2 * d][m >> 1], raw[q][2 * d + 1][m >> 1])
+                       : pack_lo16(raw[q][2 * d][m >> 1], raw[q][2 * d + 1][m >> 1]);
+      wf[q][m] = __builtin_bit_cast(bf16x8, f);
+    }
+
+  for (int b0 = 0; b0 < p.batch; b0 += 32) {
+    const int brow = b0 + r;
+    const bool ok = brow < p.batch;
+    const __bf16* arow = (const __bf16*)p.a + ((int64_t)(ok ? brow : 0) * p.heads + h) * p.lda;
+    f32x16 acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = f32x16{};
+#pragma unroll
+    for (int q = 0; q < KCW; ++q) {
+      bf16x8 a = *(const bf16x8*)(arow + 16 * (wave * KCW + q) + 8 * hh);
+      if (!ok) a = bf16x8{};
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] = mfma32x32x16(a, wf[q][m], acc[m]);
+    }
+    // accumulator i of lane (hh, c): row 8(i/4) + 4hh + i%4, columns n0 + 8c + m
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float* dst = part + ((wave * 16 + i) * 64 + lane) * 8;
+      *(f32x4*)dst = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+      *(f32x4*)(dst + 4) = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+    }
+    __syncthreads();
+    // each thread sums four (i, lane) pairs over the waves: eight consecutive
+    // columns of one row, one 16-byte store
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int pr = k * 256 + tid, i = pr >> 6, ln = pr & 63;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float* src = part + ((w * 16 + i) * 64 + ln) * 8;
+        const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] += x0[e]; v[4 + e] += x1[e]; }
+      }
+      const int row = b0 + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
+      if (row < p.batch) {
+        u32x4 o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(v[2 * d], v[2 * d + 1]);
+        *(u32x4*)((__bf16*)p.c + ((int64_t)row * p.heads + h) * p.ldc + n0 + 8 * (ln & 31)) = o;
+      }
+    }
+    // the rotary query goes after the latent part (one 16-byte chunk per thread)
+    if (blockIdx.y == 0 && p.tail != nullptr) {
+      const int cpr = p.n_tail / 8;                        // 16-byte chunks per row
+      for (int c = tid; c < 32 * cpr; c += 256) {
+        const int row = b0 + c / cpr, j = c % cpr;
+        if (row < p.batch) {
+          const u32x4 x = load16((const __bf16*)p.tail + ((int64_t)row * p.heads + h) * p.n_tail + 8 * j);
+          *(u32x4*)((__bf16*)p.c + ((int64_t)row * p.heads + h) * p.ldc + kAbsN + 8 * j) = x;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---- bf16 out-proj: W [N=128][K=512] per head, one workgroup per (head, 32 columns)
+constexpr int kOutK = 512, kOutN = 128, kOutNT = 32;
+
+__global__ __launch_bounds__(256, 2) void outproj_bf16_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) float part[4 * 64 * 16];   // [wave][lane][i]
+  const int h = blockIdx.x, n0 = blockIdx.y * kOutNT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, r = lane & 31;
+  constexpr int KCW = kOutK / 16 / 4;                     // 16-wide k blocks per wave (8)
+
+  // B fragments: W[n0 + r][k .. k + 7] is contiguous
+  bf16x8 wf[KCW];
+  const __bf16* wrow = (const __bf16*)p.w + ((int64_t)h * kOutN + n0 + r) * kOutK;
+#pragma unroll
+  for (int q = 0; q < KCW; ++q) wf[q] = *(const bf16x8*)(wrow + 16 * (wave * KCW + q) + 8 * hh);
+
+  for (int b0 = 0; b0 < p.batch; b0 += 32) {
+    const int brow = b0 + r;
+    const bool ok = brow < p.batch;
+    const int64_t aoff = ((int64_t)(ok ? brow : 0) * p.heads + h) * p.lda;
+    bf16x8 a[KCW];
+#pragma unroll
+    for (int q = 0; q < KCW; ++q) {
+      const int k0 = 16 * (wave * KCW + q) + 8 * hh;
+      a[q] = load_a_bf16((const char*)p.a + aoff * (p.a_f32 ? 4 : 2), k0, ok, p.a_f32);
+    }
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int q = 0; q < KCW; ++q) acc = mfma32x32x16(a[q], wf[q], acc);
+    float* dst = part + (wave * 64 + lane) * 16;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(f32x4*)(dst + 4 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    __syncthreads();
+    // thread t: row t / 8 of the block, columns n0 + 4 (t % 8) .. + 3
+    {
+      const int rr = tid >> 3, c0 = 4 * (tid & 7);
+      const int i = 4 * (rr >> 3) + (rr & 3), hh2 = (rr >> 2) & 1;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += part[(w * 64 + 32 * hh2 + c0 + e) * 16 + i];
+      const int row = b0 + rr;
+      if (row < p.batch) {
+        const int64_t o = ((int64_t)row * p.heads + h) * p.ldc + n0 + c0;
+        if (p.c_f32) {
+          *(f32x4*)((float*)p.c + o) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(v[0], v[1]);
+          pk[1] = pack_bf16x2(v[2], v[3]);
+          *(u32x2*)((__bf16*)p.c + o) = pk;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <bool F32, bool W_KN, int K, int N>
 hipError_t launch(const GemmParams& p, hipStream_t s) {
   using G = GemmCfg<F32, W_KN, K, N>;
@@ -158,13 +310,17 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_absorb_dsv2_bf16(const GemmParams& p, hipStream_t s) {
-  return launch<false, true, 128, 512>(p, s);
+  if (p.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(absorb_bf16_kernel, dim3(p.heads, kAbsN / kAbsNT), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 hipError_t launch_absorb_tiny_f32(const GemmParams& p, hipStream_t s) {
   return launch<true, true, 32, 32>(p, s);
 }
 hipError_t launch_outproj_dsv2_bf16(const GemmParams& p, hipStream_t s) {
-  return launch<false, false, 512, 128>(p, s);
+  if (p.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(outproj_bf16_kernel, dim3(p.heads, kOutN / kOutNT), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 hipError_t launch_outproj_tiny_f32(const GemmParams& p, hipStream_t s) {
   return launch<true, false, 32, 32>(p, s);
