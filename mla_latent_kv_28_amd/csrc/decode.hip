@@ -59,6 +59,9 @@ struct Cfg {
   static constexpr int P_BYTES = HB * 32 * PROW;
   static constexpr int NKC_LAT = DC / 16, NKC_ROPE = DR / 16, NKC = NKC_LAT + NKC_ROPE;
   static constexpr int LDS_BYTES = NBUF * BUF_BYTES + 2 * P_BYTES;
+  // bf16 output rows staged in the tile ring (row stride padded by 16 bytes)
+  static constexpr int OROW = DC * 2 + 16;
+  static constexpr bool OUT_STAGE = !F32 && DC * 2 == 64 * 16 && H * OROW <= NBUF * BUF_BYTES;
   static_assert(DC % (32 * WAVES) == 0 && DR % 16 == 0, "head shape");
   static_assert(FPW % 128 == 0 || F32, "a wave's feature slice starts on a swizzle period");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -785,6 +788,36 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   if (hh == 0) lden[head] = l_tot;
   if (hh == 0 && head < C::H) p.lse[out_row<C>(p, b, split, head)] = (s.m_ref + fast_log2(l_tot)) * kLn2;
   __syncthreads();
+  if constexpr (C::OUT_STAGE) {
+    if (!f32_out) {
+      // bf16 rows go through LDS (the idle tile ring) so that every store
+      // writes whole 1 KiB rows: row h at h * OROW, padded by 16 bytes so the
+      // 32 heads of one fragment write to different banks
+      MLA_LDS char* ob = lds;
+#pragma unroll
+      for (int hb = 0; hb < C::HB; ++hb) {
+        const int h = 32 * hb + r;
+        const float inv = 1.0f / lden[h];
+#pragma unroll
+        for (int j = 0; j < C::NFJ; ++j)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int feat = wave * C::FPW + 32 * j + 8 * jj + 4 * hh;
+            u32x2 v;
+            v[0] = pack_bf16x2(s.o[j][hb][4 * jj + 0] * inv, s.o[j][hb][4 * jj + 1] * inv);
+            v[1] = pack_bf16x2(s.o[j][hb][4 * jj + 2] * inv, s.o[j][hb][4 * jj + 3] * inv);
+            *(MLA_LDS u32x2*)(ob + h * C::OROW + feat * 2) = v;
+          }
+      }
+      __syncthreads();
+      // wave w stores rows w, w + WAVES, ...: 64 lanes x 16 bytes per row
+      for (int h = wave; h < C::H; h += C::WAVES) {
+        const u32x4 v = *(const MLA_LDS u32x4*)(ob + h * C::OROW + lane * 16);
+        *(u32x4*)((uint16_t*)p.out + out_row<C>(p, b, split, h) * C::DC + lane * 8) = v;
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int hb = 0; hb < C::HB; ++hb) {
     const int h = 32 * hb + r;
