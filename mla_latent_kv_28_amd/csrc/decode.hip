@@ -161,8 +161,9 @@ struct TileRows {
 
 // Per-lane global byte offsets of the fast tile loader (see issue_tile).
 struct DmaOffs {
-  int lat;    // latent chunk of row 4k + wave: lat ^ 16 (k & 3)
-  int rope;   // this thread's rotary chunk, bytes from the tile's first row
+  int lat;         // latent chunk of row 4k + wave: lat ^ 16 (k & 3)
+  int rope;        // this thread's rotary chunk, bytes from the tile's first row
+  int rope_chunk;  // the same chunk, bytes from the start of its own row
 };
 
 // Staging registers of the fp8 loader (codes and scales pass through VGPRs).
@@ -604,6 +605,8 @@ __device__ __forceinline__ void wait_vmem_le() {
   else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if constexpr (N == 27) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
   else static_assert(N == 0, "add the vmcnt value here");
 }
 
@@ -650,6 +653,86 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const MLA_LDS c
       else wait_vmem_le<0>();
     }
   }
+  tile_barrier();
+}
+
+// Steady state for a contiguous 16-bit cache: one basic block per tile.
+// The scores of tile t and the latent sum of tile t - 1 share one MFMA
+// stream, and the nine direct loads of tile t + 2 are spread through it, so
+// the LDS reads, the matrix cores and the load issue overlap. Past the end of
+// the split the loads fetch the last tile again (its rows are still in L2
+// and its slot is not read), which keeps the per-thread load count, and with
+// it the vmcnt wait, the same for every tile.
+template <class C>
+__device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const MLA_LDS char* __restrict__ cur,
+                                                 const MLA_LDS char* __restrict__ prev,
+                                                 MLA_LDS char* __restrict__ fill, MLA_LDS char* __restrict__ pw,
+                                                 const MLA_LDS char* __restrict__ pr, const QFrag<C>& q,
+                                                 State<C>& s, LaneOffs<C>& lo, DmaOffs& dma, const char* seq_base,
+                                                 int t, int ntiles, int start, int end) {
+  static_assert(!C::F32 && !C::FP8 && C::LAT_CH == 64 && C::WAVES == 4, "16-bit DeepSeek-V2 layout");
+  constexpr int LPT = loads_per_tile<C>();
+  constexpr int ROWB = C::DC * C::ESZ;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  refresh<C>(lo);
+  asm volatile("" : "+v"(dma.lat), "+v"(dma.rope_chunk));
+
+  // the tile to load: t + 2, clamped to the last one; rows past its end
+  // repeat its last valid row
+  const int ft = min(t + 2, ntiles - 1);
+  const int tb = start + ft * C::T;
+  const int last = min(end - tb, C::T) - 1;
+  const int rs = (int)(p.row_stride * C::ESZ);
+  const char* tile = seq_base + (int64_t)tb * rs;
+  auto dma_latent = [&](int k) {     // row 4k + wave
+    const int row = min(k * C::WAVES + wave, last);
+    load16_to_lds(tile + row * rs + (uint32_t)(dma.lat ^ (16 * (k & 3))),
+                  fill + (k * C::WAVES + wave) * ROWB);
+  };
+  auto dma_rope = [&]() {           // 8 lanes per row, rows tid / 8
+    const int row = min((int)(threadIdx.x >> 3), last);
+    load16_to_lds(tile + row * rs + (uint32_t)dma.rope_chunk, fill + C::LAT_BYTES + wave * 64 * 16);
+  };
+
+  Scores<C> sc;
+  sc.lat = f32x16{};
+  sc.rope = f32x16{};
+  bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
+  constexpr int PV_STEPS = 2 * C::HB * C::NFJ;
+  static_assert(PV_STEPS == 32 && C::NKC == 36, "step schedule");
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    bf16x8 va[C::NFJ];
+#pragma unroll
+    for (int j = 0; j < C::NFJ; ++j) {
+      const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
+      const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
+      va[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int hb = 0; hb < C::HB; ++hb) {
+      const bf16x8 pb = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, hb, u));
+#pragma unroll
+      for (int j = 0; j < C::NFJ; ++j) {
+        const int kc = (u * C::HB + hb) * C::NFJ + j;
+        if (kc % 4 == 0) dma_latent(kc / 4);
+        const bf16x8 a3 = qk_operand<C>(cur, lo, kc + 3);
+        qk_mfma<C>(sc, a0, q, kc);
+        a0 = a1; a1 = a2; a2 = a3;
+        pv_mfma<C>(s, j, hb, va[j], pb);
+      }
+    }
+  }
+  dma_rope();
+#pragma unroll
+  for (int kc = PV_STEPS; kc < C::NKC; ++kc) {
+    const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
+    qk_mfma<C>(sc, a0, q, kc);
+    a0 = a1; a1 = a2; a2 = a3;
+  }
+  softmax_tile<C, false>(cur, pw, prev, pr, sc, s, lo, end - (start + t * C::T), p.scale_log2, false);
+  wait_vmem_le<LPT>();
   tile_barrier();
 }
 
@@ -700,7 +783,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
 
   // Absorbed query fragments of this wave's 32 heads (B operand of S^T).
   QFrag<C> q;
-  {
+  auto load_q = [&]() {
     const bool ok = head < C::H;
     if constexpr (C::F32) {
       const float* qr = (const float*)p.q_lat + ((int64_t)b * C::H + (ok ? head : 0)) * C::W;
@@ -719,8 +802,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
         q.v[kc] = ok ? v : bf16x8{};
       }
     }
-  }
-
+  };
   Fp8Stage<C> st;
   LaneOffs<C> lo = lane_offsets<C>(wave);
   const SeqView sv = seq_view<PAGED>(p, b);
@@ -728,12 +810,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   {
     const int tr_ = threadIdx.x / C::ROPE_CH, cr = (threadIdx.x % C::ROPE_CH) ^ swz<C::ROPE_CH>(tr_);
     dma.lat = (lane ^ (wave << 2)) << 4;
-    dma.rope = (int)(tr_ * (p.row_stride * C::ESZ)) + C::DC * C::ESZ + cr * 16;
+    dma.rope_chunk = C::DC * C::ESZ + cr * 16;
+    dma.rope = (int)(tr_ * (p.row_stride * C::ESZ)) + dma.rope_chunk;
   }
   const int ntiles = (end - start + C::T - 1) / C::T;
   constexpr int LPT = loads_per_tile<C>();
+  constexpr bool STREAM = !PAGED && !C::F32 && !C::FP8;
+  const char* seq_base = (const char*)p.latent + sv.seq_row * (p.row_stride * C::ESZ);
   auto slot = [&](int x) -> MLA_LDS char* { return lds + (x % C::NBUF) * C::BUF_BYTES; };   // x >= 0
   auto pslot = [&](int x) -> MLA_LDS char* { return pbase + (x & 1) * C::P_BYTES; };
+
+  if constexpr (!STREAM) load_q();
 
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {   // recompute with the true maximum as reference
@@ -745,6 +832,36 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       s.m_ref = fmaxf(s.m_max, __shfl_xor(s.m_max, 32));
       s.overflow = false;
     }
+    if constexpr (STREAM) {
+      // prologue: every ring slot gets a tile (the last one again where the
+      // split is shorter), tile 0 first, then the query, then tiles 1..3
+      static_assert(C::NBUF == 4, "four-slot ring");
+      issue_tile<C, PAGED>(p, sv, dma, slot(0), start, end, st);
+      if (pass == 0) load_q();
+#pragma unroll
+      for (int k = 1; k < C::NBUF; ++k)
+        issue_tile<C, PAGED>(p, sv, dma, slot(k), start + min(k, ntiles - 1) * C::T, end, st);
+      wait_vmem_le<3 * LPT>();
+      tile_barrier();
+      // first step: scores and softmax of tile 0 (no latent sum yet); tile 1
+      // resident at its end, tiles 2 and 3 may still be arriving
+      {
+        refresh<C>(lo);
+        const Scores<C> sc = qk_tile<C>(slot(0), q, lo);
+        softmax_tile<C, false>(slot(0), pslot(0), slot(C::NBUF - 1), pslot(1), sc, s, lo,
+                               end - start, p.scale_log2, pass == 0);
+        wait_vmem_le<2 * LPT>();
+        tile_barrier();
+      }
+      // step 1 loads tile 3 a second time (its slot is not read before step 3
+      // and receives the same bytes); from step 2 on, each step loads t + 2
+      for (int t = 1; t < ntiles; ++t)
+        tile_step_stream<C>(p, slot(t), slot(t - 1), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma,
+                            seq_base, t, ntiles, start, end);
+      latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
+      if constexpr (!C::F32) vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
+      __syncthreads();
+    } else {
     // prologue: tile 0 resident, tile 1 in flight
     issue_tile<C, PAGED>(p, sv, dma, slot(0), start, end, st);
     if constexpr (C::FP8) {
@@ -769,6 +886,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
     latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
     if constexpr (!C::F32) vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
     __syncthreads();
+    }
     if (pass == 1) break;
     // did any lane's scores outrun the headroom? (uniform decision)
     MLA_LDS int* redo = (MLA_LDS int*)pbase;
