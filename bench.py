@@ -44,6 +44,24 @@ def parse():
     return ap.parse_args()
 
 
+def hbm_traffic(workload):
+    """HBM bytes per decode launch from the committed byte-counter profile of
+    this workload (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by what it
+    reads on a plain copy of known size), or None when there is none or the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "mla_decode_%s_hbm_bytes.json" % workload)
+    if not os.path.exists(path):
+        return None
+    prof = json.load(open(path))
+    h = hashlib.sha256()
+    for f in prof["source_files"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != prof["source_sha256"]:
+        return None
+    return int(round(prof["bytes_per_launch"]))
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle, as it stands, on whole sequences of the same
     workload until about `budget_s` seconds of CPU work have run."""
@@ -216,7 +234,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps_dec / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": hbm_traffic(inp.name) if S == 8 else None,
             "us_per_launch": round(ms_dec * 1e3, 3),
             "algorithmic_bytes_per_launch": cache_bytes,
             "mfma_tflops": round(flops_dec / (ms_dec * 1e-3) / 1e12, 1),
