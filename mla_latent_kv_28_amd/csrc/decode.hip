@@ -351,6 +351,48 @@ struct QFrag {
   typename std::conditional<C::F32, float[C::NKC][8], bf16x8[C::NKC]>::type v;
 };
 
+// Query fragments through LDS (16-bit layouts with 32 heads per wave). Lane
+// (hh, r) needs 16-byte chunks 2kc + hh of head r's row for every k block kc;
+// loading them directly touches 32 cache lines per instruction (one 32-byte
+// piece of each head's row). Staged, each wave copies its 32 head rows with
+// direct-to-LDS loads of consecutive bytes, in two halves of 36 chunks per
+// row, each row padded to 37 chunks so that the 16 rows read by a quarter
+// wave land on 16 distinct bank slots; then it reads its fragments.
+template <class C>
+struct QStage {
+  static constexpr int CH = C::W * 2 / 16;            // 16-byte chunks per row
+  static constexpr int HALF = CH / 2;
+  static constexpr int PITCH = HALF + 1;
+  static constexpr int CHUNKS = 32 * PITCH;           // per wave and half
+  static constexpr int LOADS = (CHUNKS + 63) / 64;    // load instructions per half
+  static constexpr int BYTES = CHUNKS * 16;
+  static_assert(C::F32 || (CH % 2 == 0 && HALF % 2 == 0 && C::NKC * 2 == CH), "two halves of whole k blocks");
+};
+
+template <class C>
+__device__ __forceinline__ void stage_q_issue(const DecodeParams& p, int b, int half, MLA_LDS char* region) {
+  using Q = QStage<C>;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* rows = (const char*)p.q_lat + ((int64_t)b * C::H + 32 * wave) * (C::W * 2) + half * Q::HALF * 16;
+#pragma unroll 1
+  for (int i = 0; i < Q::LOADS; ++i) {     // not unrolled: no address registers kept live
+    const int pos = 64 * i + lane;
+    const int r = pos / Q::PITCH, c = min(pos % Q::PITCH, Q::HALF - 1);   // the pad re-reads a real chunk
+    if (Q::CHUNKS % 64 == 0 || pos < Q::CHUNKS)
+      load16_to_lds(rows + r * (C::W * 2) + c * 16, region + 64 * 16 * i);
+  }
+}
+
+template <class C, class QF>
+__device__ __forceinline__ void stage_q_read(QF& q, int half, const MLA_LDS char* region) {
+  using Q = QStage<C>;
+  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int k = 0; k < Q::HALF / 2; ++k)
+    q.v[half * (Q::HALF / 2) + k] = *(const MLA_LDS bf16x8*)(region + (r * Q::PITCH + 2 * k + hh) * 16);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the region is refilled
+}
+
 template <class C>
 struct State {
   f32x16 o[C::NFJ][C::HB];   // O^T: this wave's feature fragments x all head blocks
@@ -509,6 +551,9 @@ __device__ __forceinline__ void softmax_tile(const MLA_LDS char* __restrict__ bu
                                              const MLA_LDS char* __restrict__ pr, const Scores<C>& sc,
                                              State<C>& s, const LaneOffs<C>& lo, int nvalid, float scale_log2,
                                              bool first) {
+  // every rounding step as written, whatever the surrounding code: the
+  // contiguous and paged kernels give bit-identical results
+#pragma clang fp contract(off)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
   constexpr bool INTERLEAVE = LATENT_SUM && !C::F32;
   if constexpr (LATENT_SUM && C::F32) latent_sum_tile<C>(prev, pr, s, lo);
@@ -657,23 +702,22 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const MLA_LDS c
 }
 
 // Steady state for a contiguous 16-bit cache: one basic block per tile.
-// The scores of tile t and the latent sum of tile t - 1 share one MFMA
-// stream, and the nine direct loads of tile t + 2 are spread through it, so
-// the LDS reads, the matrix cores and the load issue overlap. Past the end of
-// the split the loads fetch the last tile again (its rows are still in L2
-// and its slot is not read), which keeps the per-thread load count, and with
-// it the vmcnt wait, the same for every tile.
+// The nine direct loads of tile t + 2 are spread through the score MFMAs of
+// tile t, so the load issue overlaps the LDS reads and the matrix cores; the
+// latent-sum MFMAs of tile t - 1 then run while the vector unit computes the
+// softmax of tile t. Past the end of the split the loads fetch the last tile
+// again (its rows are still in L2 and its slot is not read), which keeps the
+// per-thread load count, and with it the vmcnt wait, the same for every tile.
 template <class C>
 __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const MLA_LDS char* __restrict__ cur,
                                                  const MLA_LDS char* __restrict__ prev,
                                                  MLA_LDS char* __restrict__ fill, MLA_LDS char* __restrict__ pw,
                                                  const MLA_LDS char* __restrict__ pr, const QFrag<C>& q,
                                                  State<C>& s, LaneOffs<C>& lo, DmaOffs& dma, const char* seq_base,
-                                                 int t, int ntiles, int start, int end) {
+                                                 int t, int ntiles, int start, int end, bool first) {
   static_assert(!C::F32 && !C::FP8 && C::LAT_CH == 64 && C::WAVES == 4, "16-bit DeepSeek-V2 layout");
   constexpr int LPT = loads_per_tile<C>();
   constexpr int ROWB = C::DC * C::ESZ;
-  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   refresh<C>(lo);
   asm volatile("" : "+v"(dma.lat), "+v"(dma.rope_chunk));
@@ -690,48 +734,26 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
     load16_to_lds(tile + row * rs + (uint32_t)(dma.lat ^ (16 * (k & 3))),
                   fill + (k * C::WAVES + wave) * ROWB);
   };
-  auto dma_rope = [&]() {           // 8 lanes per row, rows tid / 8
+  auto dma_rope = [&]() {           // 8 lanes per row, rows tid / 8: scalar tile base + 32-bit lane offset
     const int row = min((int)(threadIdx.x >> 3), last);
-    load16_to_lds(tile + row * rs + (uint32_t)dma.rope_chunk, fill + C::LAT_BYTES + wave * 64 * 16);
+    load16_to_lds(tile + (uint32_t)(row * rs + dma.rope_chunk), fill + C::LAT_BYTES + wave * 64 * 16);
   };
 
   Scores<C> sc;
   sc.lat = f32x16{};
   sc.rope = f32x16{};
+  constexpr int LAT_LOADS = C::T / C::WAVES;
+  static_assert(C::NKC >= 4 * LAT_LOADS + 1, "one latent load every four score MFMAs");
   bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
-  constexpr int PV_STEPS = 2 * C::HB * C::NFJ;
-  static_assert(PV_STEPS == 32 && C::NKC == 36, "step schedule");
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    bf16x8 va[C::NFJ];
-#pragma unroll
-    for (int j = 0; j < C::NFJ; ++j) {
-      const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
-      const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
-      va[j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-#pragma unroll
-    for (int hb = 0; hb < C::HB; ++hb) {
-      const bf16x8 pb = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, hb, u));
-#pragma unroll
-      for (int j = 0; j < C::NFJ; ++j) {
-        const int kc = (u * C::HB + hb) * C::NFJ + j;
-        if (kc % 4 == 0) dma_latent(kc / 4);
-        const bf16x8 a3 = qk_operand<C>(cur, lo, kc + 3);
-        qk_mfma<C>(sc, a0, q, kc);
-        a0 = a1; a1 = a2; a2 = a3;
-        pv_mfma<C>(s, j, hb, va[j], pb);
-      }
-    }
-  }
-  dma_rope();
-#pragma unroll
-  for (int kc = PV_STEPS; kc < C::NKC; ++kc) {
+  for (int kc = 0; kc < C::NKC; ++kc) {
+    if (kc % 4 == 0 && kc / 4 < LAT_LOADS) dma_latent(kc / 4);
+    if (kc == 4 * LAT_LOADS) dma_rope();
     const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
     qk_mfma<C>(sc, a0, q, kc);
     a0 = a1; a1 = a2; a2 = a3;
   }
-  softmax_tile<C, false>(cur, pw, prev, pr, sc, s, lo, end - (start + t * C::T), p.scale_log2, false);
+  softmax_tile<C, true>(cur, pw, prev, pr, sc, s, lo, end - (start + t * C::T), p.scale_log2, first);
   wait_vmem_le<LPT>();
   tile_barrier();
 }
@@ -833,31 +855,34 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       s.overflow = false;
     }
     if constexpr (STREAM) {
-      // prologue: every ring slot gets a tile (the last one again where the
-      // split is shorter), tile 0 first, then the query, then tiles 1..3
-      static_assert(C::NBUF == 4, "four-slot ring");
+      // prologue: tiles 0 and 1, and (first pass) the query staged through
+      // slots 2..3 and the P^T buffers in two halves
+      static_assert(C::NBUF == 4 && 4 * QStage<C>::BYTES <= 2 * C::BUF_BYTES + 2 * C::P_BYTES, "query staging");
+      MLA_LDS char* qreg = slot(2) + __builtin_amdgcn_readfirstlane(wave) * QStage<C>::BYTES;
+      if (pass == 0) stage_q_issue<C>(p, b, 0, qreg);
       issue_tile<C, PAGED>(p, sv, dma, slot(0), start, end, st);
-      if (pass == 0) load_q();
-#pragma unroll
-      for (int k = 1; k < C::NBUF; ++k)
-        issue_tile<C, PAGED>(p, sv, dma, slot(k), start + min(k, ntiles - 1) * C::T, end, st);
-      wait_vmem_le<3 * LPT>();
-      tile_barrier();
-      // first step: scores and softmax of tile 0 (no latent sum yet); tile 1
-      // resident at its end, tiles 2 and 3 may still be arriving
-      {
-        refresh<C>(lo);
-        const Scores<C> sc = qk_tile<C>(slot(0), q, lo);
-        softmax_tile<C, false>(slot(0), pslot(0), slot(C::NBUF - 1), pslot(1), sc, s, lo,
-                               end - start, p.scale_log2, pass == 0);
-        wait_vmem_le<2 * LPT>();
-        tile_barrier();
+      if (pass == 0) {
+        wait_vmem_le<LPT>();                      // query half 0
+        stage_q_read<C>(q, 0, qreg);
+        stage_q_issue<C>(p, b, 1, qreg);
       }
-      // step 1 loads tile 3 a second time (its slot is not read before step 3
-      // and receives the same bytes); from step 2 on, each step loads t + 2
-      for (int t = 1; t < ntiles; ++t)
-        tile_step_stream<C>(p, slot(t), slot(t - 1), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma,
-                            seq_base, t, ntiles, start, end);
+      issue_tile<C, PAGED>(p, sv, dma, slot(1), start + min(1, ntiles - 1) * C::T, end, st);
+      wait_vmem_le<LPT>();                        // tile 0 (and query half 1)
+      if (pass == 0) stage_q_read<C>(q, 1, qreg);
+      static_assert(C::P_BYTES == C::THREADS * 32, "two 16-byte zero stores per thread");
+      *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32) = u32x4{};
+      *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32 + 16) = u32x4{};
+      tile_barrier();
+      // step t loads tile t + 2 (the last tile again past the end). Step 0
+      // has no previous tile: its latent sum runs over tile 0's rows with the
+      // zeroed P^T buffer, which adds exactly zero.
+      // one copy of the step for every t: not peeled, not unrolled
+#pragma clang loop unroll(disable)
+      for (int t = 0; t < ntiles; ++t) {
+        const int tp = max(t - 1, 0), first = pass == 0 && t == 0;
+        tile_step_stream<C>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma, seq_base, t,
+                            ntiles, start, end, first != 0);
+      }
       latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
       if constexpr (!C::F32) vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
       __syncthreads();
