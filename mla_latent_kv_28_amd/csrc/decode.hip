@@ -374,12 +374,19 @@ __device__ __forceinline__ void stage_q_issue(const DecodeParams& p, int b, int 
   using Q = QStage<C>;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const char* rows = (const char*)p.q_lat + ((int64_t)b * C::H + 32 * wave) * (C::W * 2) + half * Q::HALF * 16;
-#pragma unroll 1
-  for (int i = 0; i < Q::LOADS; ++i) {     // not unrolled: no address registers kept live
-    const int pos = 64 * i + lane;
-    const int r = pos / Q::PITCH, c = min(pos % Q::PITCH, Q::HALF - 1);   // the pad re-reads a real chunk
-    if (Q::CHUNKS % 64 == 0 || pos < Q::CHUNKS)
-      load16_to_lds(rows + r * (C::W * 2) + c * 16, region + 64 * 16 * i);
+  // LDS chunk 64 i + lane holds padded row r, chunk c; stepping i moves the
+  // position by 64 = STEP_R rows + STEP_C chunks
+  constexpr int STEP_R = 64 / Q::PITCH, STEP_C = 64 % Q::PITCH;
+  int r = lane / Q::PITCH, c = lane % Q::PITCH;
+#pragma unroll
+  for (int i = 0; i < Q::LOADS; ++i) {
+    const uint32_t off = r * (C::W * 2) + min(c, Q::HALF - 1) * 16;   // the pad re-reads a real chunk
+    if (Q::CHUNKS % 64 == 0 || i + 1 < Q::LOADS || lane < Q::CHUNKS - 64 * (Q::LOADS - 1))
+      load16_to_lds(rows + off, region + 64 * 16 * i);
+    r += STEP_R;
+    c += STEP_C;
+    if (c >= Q::PITCH) { c -= Q::PITCH; r += 1; }
+    asm volatile("" : "+v"(r), "+v"(c));   // computed in turn, not all up front
   }
 }
 
@@ -701,6 +708,39 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const MLA_LDS c
   tile_barrier();
 }
 
+// Loads of one tile of a contiguous 16-bit cache (32 consecutive rows): a
+// scalar tile address plus 32-bit lane offsets. Tiles past the end of the
+// split are clamped to its last tile, and rows past the split's end repeat
+// its last row, so every tile costs every thread the same nine loads.
+template <class C>
+struct StreamTile {
+  const char* tile;
+  int last, rs;
+  __device__ __forceinline__ StreamTile(const DecodeParams& p, const char* seq_base, int t, int ntiles, int start,
+                                        int end) {
+    const int tb = start + min(t, ntiles - 1) * C::T;
+    last = min(end - tb, C::T) - 1;
+    rs = (int)(p.row_stride * C::ESZ);
+    tile = seq_base + (int64_t)tb * rs;
+  }
+  // latent row 4k + wave (one 1 KiB row per wave instruction)
+  __device__ __forceinline__ void latent(const DmaOffs& dma, MLA_LDS char* fill, int wave, int k) const {
+    const int row = min(k * C::WAVES + wave, last);
+    load16_to_lds(tile + row * rs + (uint32_t)(dma.lat ^ (16 * (k & 3))),
+                  fill + (k * C::WAVES + wave) * (C::DC * C::ESZ));
+  }
+  // rotary parts: 8 lanes per row, rows tid / 8
+  __device__ __forceinline__ void rope(const DmaOffs& dma, MLA_LDS char* fill, int wave) const {
+    const int row = min((int)(threadIdx.x >> 3), last);
+    load16_to_lds(tile + (uint32_t)(row * rs + dma.rope_chunk), fill + C::LAT_BYTES + wave * 64 * 16);
+  }
+  __device__ __forceinline__ void all(const DmaOffs& dma, MLA_LDS char* fill, int wave) const {
+#pragma unroll
+    for (int k = 0; k < C::T / C::WAVES; ++k) latent(dma, fill, wave, k);
+    rope(dma, fill, wave);
+  }
+};
+
 // Steady state for a contiguous 16-bit cache: one basic block per tile.
 // The nine direct loads of tile t + 2 are spread through the score MFMAs of
 // tile t, so the load issue overlaps the LDS reads and the matrix cores; the
@@ -717,28 +757,12 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
                                                  int t, int ntiles, int start, int end, bool first) {
   static_assert(!C::F32 && !C::FP8 && C::LAT_CH == 64 && C::WAVES == 4, "16-bit DeepSeek-V2 layout");
   constexpr int LPT = loads_per_tile<C>();
-  constexpr int ROWB = C::DC * C::ESZ;
+  static_assert(LPT == C::T / C::WAVES + 1, "nine loads per tile");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   refresh<C>(lo);
   asm volatile("" : "+v"(dma.lat), "+v"(dma.rope_chunk));
 
-  // the tile to load: t + 2, clamped to the last one; rows past its end
-  // repeat its last valid row
-  const int ft = min(t + 2, ntiles - 1);
-  const int tb = start + ft * C::T;
-  const int last = min(end - tb, C::T) - 1;
-  const int rs = (int)(p.row_stride * C::ESZ);
-  const char* tile = seq_base + (int64_t)tb * rs;
-  auto dma_latent = [&](int k) {     // row 4k + wave
-    const int row = min(k * C::WAVES + wave, last);
-    load16_to_lds(tile + row * rs + (uint32_t)(dma.lat ^ (16 * (k & 3))),
-                  fill + (k * C::WAVES + wave) * ROWB);
-  };
-  auto dma_rope = [&]() {           // 8 lanes per row, rows tid / 8: scalar tile base + 32-bit lane offset
-    const int row = min((int)(threadIdx.x >> 3), last);
-    load16_to_lds(tile + (uint32_t)(row * rs + dma.rope_chunk), fill + C::LAT_BYTES + wave * 64 * 16);
-  };
-
+  const StreamTile<C> ld(p, seq_base, t + 2, ntiles, start, end);   // tile t + 2
   Scores<C> sc;
   sc.lat = f32x16{};
   sc.rope = f32x16{};
@@ -747,8 +771,8 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
   bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
 #pragma unroll
   for (int kc = 0; kc < C::NKC; ++kc) {
-    if (kc % 4 == 0 && kc / 4 < LAT_LOADS) dma_latent(kc / 4);
-    if (kc == 4 * LAT_LOADS) dma_rope();
+    if (kc % 4 == 0 && kc / 4 < LAT_LOADS) ld.latent(dma, fill, wave, kc / 4);
+    if (kc == 4 * LAT_LOADS) ld.rope(dma, fill, wave);
     const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
     qk_mfma<C>(sc, a0, q, kc);
     a0 = a1; a1 = a2; a2 = a3;
@@ -771,17 +795,28 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   int w = blockIdx.x;
   if (p.xcd_remap) w = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int b = w / p.num_splits, split = w % p.num_splits;
-  const int L = max(0, min(p.seq_lens[b], p.max_seq_len));
+  const int len_b = p.seq_lens[b];   // a scalar load, requested before the loads into LDS
+  MLA_LDS char* lds = (MLA_LDS char*)smem;
+  auto slot = [&](int x) -> MLA_LDS char* { return lds + (x % C::NBUF) * C::BUF_BYTES; };   // x >= 0
+
+  // Contiguous 16-bit caches stage the query through LDS (slots 2..3 and the
+  // P^T buffers); its first half is requested before anything else, since
+  // it depends on nothing but the sequence.
+  constexpr bool STREAM = !PAGED && !C::F32 && !C::FP8;
+  MLA_LDS char* qreg = slot(2) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * QStage<C>::BYTES;
+  if constexpr (STREAM) stage_q_issue<C>(p, b, 0, qreg);
+
+  const int L = max(0, min(len_b, p.max_seq_len));
   const int start = split * p.chunk;
   const int end = min(start + p.chunk, L);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
   const int head = wave * 32 + r;
-  MLA_LDS char* lds = (MLA_LDS char*)smem;
   MLA_LDS char* pbase = lds + C::NBUF * C::BUF_BYTES;
   const bool f32_out = !p.out_bf16;
 
   if (start >= end) {             // uniform over the workgroup: no tokens
+    if constexpr (STREAM) wait_vmem_le<0>();   // nothing may land in LDS after the workgroup ends
     if (head < C::H) {
       const int64_t row = out_row<C>(p, b, split, head);
       if (hh == 0) p.lse[row] = -INFINITY;
@@ -837,9 +872,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   }
   const int ntiles = (end - start + C::T - 1) / C::T;
   constexpr int LPT = loads_per_tile<C>();
-  constexpr bool STREAM = !PAGED && !C::F32 && !C::FP8;
   const char* seq_base = (const char*)p.latent + sv.seq_row * (p.row_stride * C::ESZ);
-  auto slot = [&](int x) -> MLA_LDS char* { return lds + (x % C::NBUF) * C::BUF_BYTES; };   // x >= 0
   auto pslot = [&](int x) -> MLA_LDS char* { return pbase + (x & 1) * C::P_BYTES; };
 
   if constexpr (!STREAM) load_q();
@@ -855,18 +888,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       s.overflow = false;
     }
     if constexpr (STREAM) {
-      // prologue: tiles 0 and 1, and (first pass) the query staged through
-      // slots 2..3 and the P^T buffers in two halves
+      // prologue: tiles 0 and 1, and (first pass) the second half of the
+      // query once the first is read
       static_assert(C::NBUF == 4 && 4 * QStage<C>::BYTES <= 2 * C::BUF_BYTES + 2 * C::P_BYTES, "query staging");
-      MLA_LDS char* qreg = slot(2) + __builtin_amdgcn_readfirstlane(wave) * QStage<C>::BYTES;
-      if (pass == 0) stage_q_issue<C>(p, b, 0, qreg);
-      issue_tile<C, PAGED>(p, sv, dma, slot(0), start, end, st);
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      StreamTile<C>(p, seq_base, 0, ntiles, start, end).all(dma, slot(0), wv);
       if (pass == 0) {
         wait_vmem_le<LPT>();                      // query half 0
         stage_q_read<C>(q, 0, qreg);
         stage_q_issue<C>(p, b, 1, qreg);
       }
-      issue_tile<C, PAGED>(p, sv, dma, slot(1), start + min(1, ntiles - 1) * C::T, end, st);
+      StreamTile<C>(p, seq_base, 1, ntiles, start, end).all(dma, slot(1), wv);
       wait_vmem_le<LPT>();                        // tile 0 (and query half 1)
       if (pass == 0) stage_q_read<C>(q, 1, qreg);
       static_assert(C::P_BYTES == C::THREADS * 32, "two 16-byte zero stores per thread");
