@@ -545,10 +545,9 @@ __device__ __forceinline__ void latent_sum_tile(const MLA_LDS char* __restrict__
 
 // Streaming softmax of one tile (base 2, fixed reference) and P^T to LDS.
 //
-// Rows past the end of a partial tile hold the tile's first token (a real
-// score of this split), so they may take part in the maxima; only their
-// probabilities are zeroed. `first` (uniform): the first tile of the first
-// pass sets the reference. With LATENT_SUM, the latent-sum products of the
+// Rows past the end of a partial tile hold copies of valid rows; their
+// scores are replaced by -inf. `first` (uniform): the first tile of the
+// first pass sets the reference. With LATENT_SUM, the latent-sum products of the
 // previous tile (`prev`, probabilities in `pr`) are issued between the
 // softmax's vector instructions: they are independent, and the matrix cores
 // work through them while the vector unit runs the softmax.
@@ -580,8 +579,6 @@ __device__ __forceinline__ void softmax_tile(const MLA_LDS char* __restrict__ bu
 #pragma unroll
     for (int j = 0; j < C::NFJ; ++j) pv_mfma<C>(s, j, hb, va[j], pb);
   };
-  if constexpr (INTERLEAVE) { pv_load(0); pv_block(0, 0); }
-
   float tok_scale[16];
   if constexpr (C::FP8) {
     const MLA_LDS float* scl = (const MLA_LDS float*)(buf + C::LAT_BYTES + C::ROPE_BYTES);
@@ -598,11 +595,24 @@ __device__ __forceinline__ void softmax_tile(const MLA_LDS char* __restrict__ bu
     const float v = C::FP8 ? (tok_scale[i] * sc.lat[i] + sc.rope[i]) : sc.lat[i];
     x[i] = v * scale_log2;
   }
+  // tokens past the end of a partial tile (uniform) score -inf: they take
+  // part in neither the maxima nor the sums
+  if (nvalid < C::T) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
+      x[i] = tok < nvalid ? x[i] : -INFINITY;
+    }
+  }
+  // from here on one basic block: the scheduler can interleave the softmax
+  // with the latent-sum MFMAs
+  if constexpr (INTERLEAVE) { pv_load(0); pv_block(0, 0); }
   if constexpr (INTERLEAVE) pv_block(0, 1);
   float mt = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
-  if (first) s.m_ref = wave_max32(mt);    // lanes r and r + 32 hold one head
+  const float m_first = wave_max32(mt);   // lanes r and r + 32 hold one head
+  s.m_ref = first ? m_first : s.m_ref;
   s.m_max = fmaxf(s.m_max, mt);
   s.overflow = s.overflow || (mt > s.m_ref + kHeadroom);
   if constexpr (INTERLEAVE) pv_block(0, 2);
@@ -613,13 +623,6 @@ __device__ __forceinline__ void softmax_tile(const MLA_LDS char* __restrict__ bu
 #pragma unroll
   for (int i = 8; i < 16; ++i) pr_[i] = fast_exp2(x[i] - s.m_ref);
   if constexpr (INTERLEAVE) pv_block(1, 1);
-  if (nvalid < C::T) {    // partial tile (uniform)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
-      pr_[i] = tok < nvalid ? pr_[i] : 0.0f;
-    }
-  }
   float q4[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) q4[j] = (pr_[4 * j] + pr_[4 * j + 1]) + (pr_[4 * j + 2] + pr_[4 * j + 3]);
@@ -708,6 +711,126 @@ __device__ __forceinline__ void tile_step(const DecodeParams& p, const MLA_LDS c
   tile_barrier();
 }
 
+// The partner lane 32 away (lanes r and r + 32 hold the two token halves of
+// one head): v_permlane32_swap, a vector instruction, no LDS round trip.
+__device__ __forceinline__ float lane32_partner(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto sw = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  // lanes 0..31 find the upper half's value in the second result, lanes
+  // 32..63 the lower half's in the first
+  return __builtin_bit_cast(float, (uint32_t)((threadIdx.x & 32) ? sw[0] : sw[1]));
+}
+
+// Phase two of the streaming step: the softmax of tile t on the vector unit,
+// interleaved group by group with the 32 latent-sum MFMAs of tile t - 1. A
+// wave issues in order, so a run of MFMAs holds back the vector work queued
+// behind it; here each MFMA is followed by a few vector instructions that
+// execute while it runs, and scheduling barriers keep the compiler from
+// regrouping them. va[0] (C_KV^T of k step 0) and pb[0] (P^T of head block
+// 0) come in loaded. The arithmetic is that of softmax_tile in the same
+// order, so contiguous and paged caches give identical bits.
+template <class C>
+__device__ __forceinline__ void softmax_pv_stream(const MLA_LDS char* __restrict__ prev,
+                                                  const MLA_LDS char* __restrict__ pr,
+                                                  MLA_LDS char* __restrict__ pw, const Scores<C>& sc, State<C>& s,
+                                                  const LaneOffs<C>& lo, bf16x8 (&va)[2][C::NFJ], bf16x8 (&pb)[2],
+                                                  int nvalid, float scale_log2, bool first) {
+#pragma clang fp contract(off)
+  static_assert(!C::F32 && !C::FP8 && C::NFJ == 4 && C::HB == 4, "32 latent-sum MFMAs, 16 scores per lane");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
+  auto sync = [] { __builtin_amdgcn_sched_barrier(0); };
+  // MFMA m: k step u = m / 16, head block hb = m / 4 % 4, feature fragment j = m % 4;
+  // block m / 4 uses pb[(m / 4) & 1]
+  auto mfma = [&](int m) { pv_mfma<C>(s, m & 3, (m >> 2) & 3, va[m >> 4][m & 3], pb[(m >> 2) & 1]); };
+  auto read_pb = [&](int blk) {
+    pb[blk & 1] = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, blk & 3, blk >> 2));
+  };
+  auto read_va = [&](int u, int j) {
+    const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
+    const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
+    va[u][j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  float x[16], a[8], pv[16];
+  // scaled scores
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    mfma(g);
+    if (g == 0) read_pb(1);
+#pragma unroll
+    for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = sc.lat[i] * scale_log2;
+    sync();
+  }
+  // maximum over this lane's 16 tokens (exact in any order)
+  mfma(4); read_pb(2);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = fmaxf(x[2 * k], x[2 * k + 1]);
+  sync();
+  mfma(5);
+#pragma unroll
+  for (int k = 4; k < 8; ++k) a[k] = fmaxf(x[2 * k], x[2 * k + 1]);
+  sync();
+  mfma(6);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = fmaxf(a[2 * k], a[2 * k + 1]);
+  sync();
+  mfma(7);
+  const float mt = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+  sync();
+  mfma(8); read_pb(3);
+  const float m_first = fmaxf(mt, lane32_partner(mt));
+  s.m_ref = first ? m_first : s.m_ref;
+  s.m_max = fmaxf(s.m_max, mt);
+  s.overflow = s.overflow || (mt > s.m_ref + kHeadroom);
+  sync();
+  // probabilities, two per MFMA; the C_KV^T operands of k step 1 on the way
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    mfma(9 + g);
+    if (g >= 1 && g <= 4) read_va(1, g - 1);
+    if (g == 3) read_pb(4);
+    if (g == 7) read_pb(5);
+    pv[2 * g] = fast_exp2(x[2 * g] - s.m_ref);
+    pv[2 * g + 1] = fast_exp2(x[2 * g + 1] - s.m_ref);
+    sync();
+  }
+  if (nvalid < C::T) {    // partial tile (uniform): tokens past the end weigh nothing
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
+      pv[i] = tok < nvalid ? pv[i] : 0.0f;
+    }
+  }
+  sync();
+  float q4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mfma(17 + j);
+    if (j == 3) read_pb(6);
+    q4[j] = (pv[4 * j] + pv[4 * j + 1]) + (pv[4 * j + 2] + pv[4 * j + 3]);
+    sync();
+  }
+  mfma(21);
+  s.l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
+  sync();
+  // P^T rows of this wave's heads: element e of k step u is token
+  // 16u + 8(e/4) + 4hh + e%4, i.e. pv[8u + e]
+  u32x4 pk[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    mfma(22 + u);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) pk[u][d] = pack_bf16x2(pv[8 * u + 2 * d], pv[8 * u + 2 * d + 1]);
+    sync();
+  }
+  mfma(24); read_pb(7);
+  const int head = 32 * wave + r;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) *(MLA_LDS u32x4*)(pw + p_off<C>(head, 2 * u + hh)) = pk[u];
+  sync();
+#pragma unroll
+  for (int m = 25; m < 32; ++m) mfma(m);
+}
+
 // Loads of one tile of a contiguous 16-bit cache (32 consecutive rows): a
 // scalar tile address plus 32-bit lane offsets. Tiles past the end of the
 // split are clamped to its last tile, and rows past the split's end repeat
@@ -768,16 +891,26 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
   sc.rope = f32x16{};
   constexpr int LAT_LOADS = C::T / C::WAVES;
   static_assert(C::NKC >= 4 * LAT_LOADS + 1, "one latent load every four score MFMAs");
+  bf16x8 va[2][C::NFJ], pb[2];
   bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
 #pragma unroll
   for (int kc = 0; kc < C::NKC; ++kc) {
     if (kc % 4 == 0 && kc / 4 < LAT_LOADS) ld.latent(dma, fill, wave, kc / 4);
     if (kc == 4 * LAT_LOADS) ld.rope(dma, fill, wave);
+    // operands of the first latent-sum MFMAs, read during the last score MFMAs
+    if (kc >= C::NKC - 6 && kc < C::NKC - 2) {
+      const int j = kc - (C::NKC - 6);
+      const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, 0));
+      const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, 0));
+      va[0][j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    if (kc == C::NKC - 2) pb[0] = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, 0, 0));
     const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
     qk_mfma<C>(sc, a0, q, kc);
     a0 = a1; a1 = a2; a2 = a3;
   }
-  softmax_tile<C, true>(cur, pw, prev, pr, sc, s, lo, end - (start + t * C::T), p.scale_log2, first);
+  __builtin_amdgcn_sched_barrier(0);
+  softmax_pv_stream<C>(prev, pr, pw, sc, s, lo, va, pb, end - (start + t * C::T), p.scale_log2, first);
   wait_vmem_le<LPT>();
   tile_barrier();
 }
