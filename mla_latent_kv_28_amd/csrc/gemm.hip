@@ -158,8 +158,11 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(GemmParams p) {
   const int h = blockIdx.x, n0 = blockIdx.y * kAbsNT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, r = lane & 31;
   constexpr int KCW = kAbsK / 16 / 4;                     // 16-wide k blocks per wave (2)
+  constexpr int TAIL_CH = 64 / 8;                         // 16-byte chunks of a 64-wide rotary row
+  const bool do_tail = blockIdx.y == 0 && p.tail != nullptr;
 
-  // weight fragments of this wave's k blocks: all loads issued before any use
+  // Everything the first batch block needs is requested up front, in one
+  // round trip: the weights, this wave's query rows and the rotary rows.
   u32x4 raw[KCW][8];
   const __bf16* wh = (const __bf16*)p.w + (int64_t)h * kAbsK * kAbsN;
 #pragma unroll
@@ -168,6 +171,25 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) raw[q][e] = load16(wh + (int64_t)(k0 + e) * kAbsN + n0 + 8 * r);
   }
+  auto load_a = [&](int b0, bf16x8 (&a)[KCW]) {
+    const int brow = b0 + r;
+    const bool ok = brow < p.batch;
+    const __bf16* arow = (const __bf16*)p.a + ((int64_t)(ok ? brow : 0) * p.heads + h) * p.lda;
+#pragma unroll
+    for (int q = 0; q < KCW; ++q) {
+      a[q] = *(const bf16x8*)(arow + 16 * (wave * KCW + q) + 8 * hh);
+      if (!ok) a[q] = bf16x8{};
+    }
+  };
+  // rotary rows: one 16-byte chunk per thread (32 rows x 8 chunks)
+  auto load_tail = [&](int b0) -> u32x4 {
+    const int row = min(b0 + tid / TAIL_CH, p.batch - 1);
+    return load16((const __bf16*)p.tail + ((int64_t)row * p.heads + h) * 64 + 8 * (tid % TAIL_CH));
+  };
+  bf16x8 a_next[KCW];
+  load_a(0, a_next);
+  u32x4 tail_next = do_tail ? load_tail(0) : u32x4{};
+
   bf16x8 wf[KCW][8];
 #pragma unroll
   for (int q = 0; q < KCW; ++q)
@@ -182,19 +204,21 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(GemmParams p) {
     }
 
   for (int b0 = 0; b0 < p.batch; b0 += 32) {
-    const int brow = b0 + r;
-    const bool ok = brow < p.batch;
-    const __bf16* arow = (const __bf16*)p.a + ((int64_t)(ok ? brow : 0) * p.heads + h) * p.lda;
+    bf16x8 a[KCW];
+#pragma unroll
+    for (int q = 0; q < KCW; ++q) a[q] = a_next[q];
+    const u32x4 tail = tail_next;
+    if (b0 + 32 < p.batch) {          // the next block's rows go out before this block's math
+      load_a(b0 + 32, a_next);
+      if (do_tail) tail_next = load_tail(b0 + 32);
+    }
     f32x16 acc[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[m] = f32x16{};
 #pragma unroll
-    for (int q = 0; q < KCW; ++q) {
-      bf16x8 a = *(const bf16x8*)(arow + 16 * (wave * KCW + q) + 8 * hh);
-      if (!ok) a = bf16x8{};
+    for (int q = 0; q < KCW; ++q)
 #pragma unroll
-      for (int m = 0; m < 8; ++m) acc[m] = mfma32x32x16(a, wf[q][m], acc[m]);
-    }
+      for (int m = 0; m < 8; ++m) acc[m] = mfma32x32x16(a[q], wf[q][m], acc[m]);
     // accumulator i of lane (hh, c): row 8(i/4) + 4hh + i%4, columns n0 + 8c + m
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -224,16 +248,11 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(GemmParams p) {
         *(u32x4*)((__bf16*)p.c + ((int64_t)row * p.heads + h) * p.ldc + n0 + 8 * (ln & 31)) = o;
       }
     }
-    // the rotary query goes after the latent part (one 16-byte chunk per thread)
-    if (blockIdx.y == 0 && p.tail != nullptr) {
-      const int cpr = p.n_tail / 8;                        // 16-byte chunks per row
-      for (int c = tid; c < 32 * cpr; c += 256) {
-        const int row = b0 + c / cpr, j = c % cpr;
-        if (row < p.batch) {
-          const u32x4 x = load16((const __bf16*)p.tail + ((int64_t)row * p.heads + h) * p.n_tail + 8 * j);
-          *(u32x4*)((__bf16*)p.c + ((int64_t)row * p.heads + h) * p.ldc + kAbsN + 8 * j) = x;
-        }
-      }
+    // the rotary query goes after the latent part
+    if (do_tail) {
+      const int row = b0 + tid / TAIL_CH;
+      if (row < p.batch)
+        *(u32x4*)((__bf16*)p.c + ((int64_t)row * p.heads + h) * p.ldc + kAbsN + 8 * (tid % TAIL_CH)) = tail;
     }
     __syncthreads();
   }
@@ -242,6 +261,7 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(GemmParams p) {
 // ---- bf16 out-proj: W [N=128][K=512] per head, one workgroup per (head, 32 columns)
 constexpr int kOutK = 512, kOutN = 128, kOutNT = 32;
 
+template <bool A_F32>
 __global__ __launch_bounds__(256, 2) void outproj_bf16_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) float part[4 * 64 * 16];   // [wave][lane][i]
   const int h = blockIdx.x, n0 = blockIdx.y * kOutNT;
@@ -262,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void outproj_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int q = 0; q < KCW; ++q) {
       const int k0 = 16 * (wave * KCW + q) + 8 * hh;
-      a[q] = load_a_bf16((const char*)p.a + aoff * (p.a_f32 ? 4 : 2), k0, ok, p.a_f32);
+      a[q] = load_a_bf16((const char*)p.a + aoff * (A_F32 ? 4 : 2), k0, ok, A_F32);
     }
     f32x16 acc = f32x16{};
 #pragma unroll
@@ -311,6 +331,7 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_absorb_dsv2_bf16(const GemmParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
+  if (p.tail != nullptr && p.n_tail != 64) return hipErrorInvalidValue;   // 64-wide rotary rows
   hipLaunchKernelGGL(absorb_bf16_kernel, dim3(p.heads, kAbsN / kAbsNT), dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -319,7 +340,10 @@ hipError_t launch_absorb_tiny_f32(const GemmParams& p, hipStream_t s) {
 }
 hipError_t launch_outproj_dsv2_bf16(const GemmParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(outproj_bf16_kernel, dim3(p.heads, kOutN / kOutNT), dim3(256), 0, s, p);
+  if (p.a_f32)
+    hipLaunchKernelGGL(outproj_bf16_kernel<true>, dim3(p.heads, kOutN / kOutNT), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(outproj_bf16_kernel<false>, dim3(p.heads, kOutN / kOutNT), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 hipError_t launch_outproj_tiny_f32(const GemmParams& p, hipStream_t s) {
