@@ -165,6 +165,27 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const void* o_lat,
                         int32_t o_dtype, const void* w_uv, int32_t w_dtype,
                         void* out, int32_t out_dtype, mla_stream stream);
 
+/*
+ * mla_combine followed by mla_out_proj in one pass, without the merged
+ * latent output going to memory: for every (b, h) the split partials are
+ * merged in fp32 with the weights exp(lse_part - lse), rounded to bf16 (the
+ * values a bf16 mla_combine output would hold) and multiplied by W_UV with
+ * fp32 accumulation.
+ *   o_part [B, S, H, d_latent] in part_dtype, lse_part [B, S, H] f32 (as
+ *          written by mla_decode with S > 1),
+ *   w_uv   [H, d_v, d_latent] in w_dtype,
+ *   out    [B, H, d_v] in out_dtype (MLA_BF16 or MLA_F32),
+ *   lse    [B, H] f32, the merged log-sum-exp (may be NULL).
+ * Parts with lse = -inf contribute nothing; if all do, out = 0, lse = -inf.
+ * Only the DeepSeek-V2 head shape with bf16 partials and bf16 weights
+ * (MLA_ERR_UNSUPPORTED for other shapes, MLA_ERR_DTYPE for other dtypes);
+ * num_splits at most 64 (MLA_ERR_UNSUPPORTED above; mla_combine takes more).
+ */
+mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num_splits,
+                                const void* o_part, int32_t part_dtype, const float* lse_part,
+                                const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype,
+                                float* lse, mla_stream stream);
+
 /* Tokens per split chunk that mla_decode uses for (max_seq_len, num_splits):
  * ceil(max_seq_len / num_splits) rounded up to a multiple of 32. */
 int32_t mla_split_chunk(int32_t max_seq_len, int32_t num_splits);

@@ -20,8 +20,8 @@ _STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DT
            -4: "MLA_ERR_UNSUPPORTED", -5: "MLA_ERR_ALIGN", -6: "MLA_ERR_HIP"}
 
 # Every symbol include/mla.h declares.
-EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_split_chunk",
-           "mla_suggest_splits", "mla_status_string", "mla_last_hip_error")
+EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
+           "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error")
 
 
 class MLAError(RuntimeError):
@@ -62,6 +62,7 @@ def lib():
         L.mla_decode.argtypes = [pd, i32, vp, ctypes.POINTER(KVCache), vp, i32, f32, i32, vp, vp, i32, vp]
         L.mla_combine.argtypes = [pd, i32, i32, vp, i32, vp, vp, vp, i32, vp]
         L.mla_out_proj.argtypes = [pd, i32, vp, i32, vp, i32, vp, i32, vp]
+        L.mla_combine_out_proj.argtypes = [pd, i32, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp]
         L.mla_split_chunk.argtypes = [i32, i32]
         L.mla_suggest_splits.argtypes = [i32, i32, i64, i32]
         L.mla_status_string.argtypes = [i32]
@@ -175,6 +176,22 @@ def mla_out_proj(dims, batch, o_lat, o_dtype, w_uv, w_dtype, out, out_dtype, str
         _dev(out, "out", _TORCH_DTYPE.get(out_dtype), batch * H * d.d_v), out_dtype,
         _stream(stream))
     _check(st, "mla_out_proj")
+
+
+def mla_combine_out_proj(dims, batch, num_splits, o_part, part_dtype, lse_part, w_uv, w_dtype, out,
+                         out_dtype, lse, stream=None):
+    d = dims_of(dims)
+    H = d.num_heads
+    st = lib().mla_combine_out_proj(
+        ctypes.byref(d), batch, num_splits,
+        _dev(o_part, "o_part", _TORCH_DTYPE.get(part_dtype), batch * num_splits * H * d.d_latent),
+        part_dtype,
+        _dev(lse_part, "lse_part", torch.float32, batch * num_splits * H),
+        _dev(w_uv, "w_uv", _TORCH_DTYPE.get(w_dtype), H * d.d_v * d.d_latent), w_dtype,
+        _dev(out, "out", _TORCH_DTYPE.get(out_dtype), batch * H * d.d_v), out_dtype,
+        _dev(lse, "lse", torch.float32, batch * H),
+        _stream(stream))
+    _check(st, "mla_combine_out_proj")
 
 
 def mla_split_chunk(max_seq_len, num_splits):

@@ -439,8 +439,11 @@ __device__ __forceinline__ bf16x8 qk_operand(const MLA_LDS char* buf, const Lane
 // product for the last fragment is therefore issued with VGPR operands.
 // Dependent products that accumulate into exactly the same registers need no
 // wait states; VALU reads of the result wait for vgpr_acc_drain().
+// The compiler inserts no wait states before inline asm, so the MFMA is
+// preceded by enough of them for operands that vector instructions wrote just
+// before (an MFMA reading such a register at once gets its old value).
 __device__ __forceinline__ void mfma_vgpr_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  asm("s_nop 5\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 // More wait states than the longest MFMA needs before VALU reads its result.
 __device__ __forceinline__ void vgpr_acc_drain(f32x16& acc) {
@@ -721,47 +724,69 @@ __device__ __forceinline__ float lane32_partner(float v) {
   return __builtin_bit_cast(float, (uint32_t)((threadIdx.x & 32) ? sw[0] : sw[1]));
 }
 
-// Phase two of the streaming step: the softmax of tile t on the vector unit,
-// interleaved group by group with the 32 latent-sum MFMAs of tile t - 1. A
-// wave issues in order, so a run of MFMAs holds back the vector work queued
-// behind it; here each MFMA is followed by a few vector instructions that
-// execute while it runs, and scheduling barriers keep the compiler from
-// regrouping them. va[0] (C_KV^T of k step 0) and pb[0] (P^T of head block
-// 0) come in loaded. The arithmetic is that of softmax_tile in the same
-// order, so contiguous and paged caches give identical bits.
+// The 32 latent-sum MFMAs of one tile, m = 0..31 (k step u = m / 16, head
+// block hb = m / 4 % 4, feature fragment j = m % 4), with their operand reads
+// scheduled ahead of use: the P^T operand of head block b + 1 at MFMA 4b, the
+// C_KV^T operands of k step 1 at MFMAs 10..13. va[0] and pb[0] are read by the
+// caller before MFMA 0.
 template <class C>
-__device__ __forceinline__ void softmax_pv_stream(const MLA_LDS char* __restrict__ prev,
-                                                  const MLA_LDS char* __restrict__ pr,
-                                                  MLA_LDS char* __restrict__ pw, const Scores<C>& sc, State<C>& s,
-                                                  const LaneOffs<C>& lo, bf16x8 (&va)[2][C::NFJ], bf16x8 (&pb)[2],
-                                                  int nvalid, float scale_log2, bool first) {
+struct PvSched {
+  State<C>& s;
+  bf16x8 (&va)[2][C::NFJ];
+  bf16x8 (&pb)[2];
+  const MLA_LDS char* __restrict__ prev;
+  const MLA_LDS char* __restrict__ pr;
+  const LaneOffs<C>& lo;
+  __device__ __forceinline__ void read_pb(int blk) {
+    pb[blk & 1] = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, blk & 3, blk >> 2));
+  }
+  __device__ __forceinline__ void read_va(int u, int j) {
+    const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
+    const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
+    va[u][j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __device__ __forceinline__ void step(int m) {
+    if (m % 4 == 0 && m / 4 + 1 < 8) read_pb(m / 4 + 1);
+    if (m >= 10 && m < 14) read_va(1, m - 10);
+    pv_mfma<C>(s, m & 3, (m >> 2) & 3, va[m >> 4][m & 3], pb[(m >> 2) & 1]);
+  }
+};
+
+// Latent-sum MFMAs of tile t - 1 issued in the score phase of tile t, which
+// is bound by LDS reads and leaves the matrix cores room; the rest run in
+// phase two.
+constexpr int kPvEarly = 0;
+
+// Phase two of the streaming step: the softmax of tile t on the vector unit,
+// interleaved group by group with the remaining latent-sum MFMAs of tile
+// t - 1. A wave issues in order, so a run of MFMAs holds back the vector work
+// queued behind it; here each MFMA is followed by a few vector instructions
+// that execute while it runs, and scheduling barriers keep the compiler from
+// regrouping them. The arithmetic is that of softmax_tile in the same order,
+// so contiguous and paged caches give identical bits.
+template <class C>
+__device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char* __restrict__ pw,
+                                                  const Scores<C>& sc, State<C>& s, int nvalid, float scale_log2,
+                                                  bool first) {
 #pragma clang fp contract(off)
   static_assert(!C::F32 && !C::FP8 && C::NFJ == 4 && C::HB == 4, "32 latent-sum MFMAs, 16 scores per lane");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
   auto sync = [] { __builtin_amdgcn_sched_barrier(0); };
-  // MFMA m: k step u = m / 16, head block hb = m / 4 % 4, feature fragment j = m % 4;
-  // block m / 4 uses pb[(m / 4) & 1]
-  auto mfma = [&](int m) { pv_mfma<C>(s, m & 3, (m >> 2) & 3, va[m >> 4][m & 3], pb[(m >> 2) & 1]); };
-  auto read_pb = [&](int blk) {
-    pb[blk & 1] = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, blk & 3, blk >> 2));
-  };
-  auto read_va = [&](int u, int j) {
-    const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
-    const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
-    va[u][j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  // vector group g runs beside latent-sum MFMA kPvEarly + g (if any is left)
+  auto mfma = [&](int g) {
+    if (kPvEarly + g < 32) pvs.step(kPvEarly + g);
   };
   float x[16], a[8], pv[16];
   // scaled scores
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     mfma(g);
-    if (g == 0) read_pb(1);
 #pragma unroll
     for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = sc.lat[i] * scale_log2;
     sync();
   }
   // maximum over this lane's 16 tokens (exact in any order)
-  mfma(4); read_pb(2);
+  mfma(4);
 #pragma unroll
   for (int k = 0; k < 4; ++k) a[k] = fmaxf(x[2 * k], x[2 * k + 1]);
   sync();
@@ -776,19 +801,16 @@ __device__ __forceinline__ void softmax_pv_stream(const MLA_LDS char* __restrict
   mfma(7);
   const float mt = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
   sync();
-  mfma(8); read_pb(3);
+  mfma(8);
   const float m_first = fmaxf(mt, lane32_partner(mt));
   s.m_ref = first ? m_first : s.m_ref;
   s.m_max = fmaxf(s.m_max, mt);
   s.overflow = s.overflow || (mt > s.m_ref + kHeadroom);
   sync();
-  // probabilities, two per MFMA; the C_KV^T operands of k step 1 on the way
+  // probabilities, two per MFMA
 #pragma unroll
   for (int g = 0; g < 8; ++g) {
     mfma(9 + g);
-    if (g >= 1 && g <= 4) read_va(1, g - 1);
-    if (g == 3) read_pb(4);
-    if (g == 7) read_pb(5);
     pv[2 * g] = fast_exp2(x[2 * g] - s.m_ref);
     pv[2 * g + 1] = fast_exp2(x[2 * g + 1] - s.m_ref);
     sync();
@@ -805,7 +827,6 @@ __device__ __forceinline__ void softmax_pv_stream(const MLA_LDS char* __restrict
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     mfma(17 + j);
-    if (j == 3) read_pb(6);
     q4[j] = (pv[4 * j] + pv[4 * j + 1]) + (pv[4 * j + 2] + pv[4 * j + 3]);
     sync();
   }
@@ -822,13 +843,13 @@ __device__ __forceinline__ void softmax_pv_stream(const MLA_LDS char* __restrict
     for (int d = 0; d < 4; ++d) pk[u][d] = pack_bf16x2(pv[8 * u + 2 * d], pv[8 * u + 2 * d + 1]);
     sync();
   }
-  mfma(24); read_pb(7);
+  mfma(24);
   const int head = 32 * wave + r;
 #pragma unroll
   for (int u = 0; u < 2; ++u) *(MLA_LDS u32x4*)(pw + p_off<C>(head, 2 * u + hh)) = pk[u];
   sync();
 #pragma unroll
-  for (int m = 25; m < 32; ++m) mfma(m);
+  for (int g = 25; g < 32; ++g) mfma(g);
 }
 
 // Loads of one tile of a contiguous 16-bit cache (32 consecutive rows): a
@@ -892,25 +913,25 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
   constexpr int LAT_LOADS = C::T / C::WAVES;
   static_assert(C::NKC >= 4 * LAT_LOADS + 1, "one latent load every four score MFMAs");
   bf16x8 va[2][C::NFJ], pb[2];
+  PvSched<C> pvs{s, va, pb, prev, pr, lo};
+  // operands of the first latent-sum MFMAs are read during the score MFMAs
+  constexpr int PV0 = C::NKC - kPvEarly;      // score step of the first early latent-sum MFMA
+  constexpr int PF = PV0 - 8;                 // score step of the first operand read
+  static_assert(PF >= 0, "room for the operand reads");
   bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
 #pragma unroll
   for (int kc = 0; kc < C::NKC; ++kc) {
     if (kc % 4 == 0 && kc / 4 < LAT_LOADS) ld.latent(dma, fill, wave, kc / 4);
     if (kc == 4 * LAT_LOADS) ld.rope(dma, fill, wave);
-    // operands of the first latent-sum MFMAs, read during the last score MFMAs
-    if (kc >= C::NKC - 6 && kc < C::NKC - 2) {
-      const int j = kc - (C::NKC - 6);
-      const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, 0));
-      const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, 0));
-      va[0][j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    if (kc == C::NKC - 2) pb[0] = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, 0, 0));
+    if (kc >= PF + 2 && kc < PF + 6) pvs.read_va(0, kc - (PF + 2));
+    if (kc == PF + 6) pvs.read_pb(0);
     const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
     qk_mfma<C>(sc, a0, q, kc);
     a0 = a1; a1 = a2; a2 = a3;
+    if (kc >= PV0) pvs.step(kc - PV0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  softmax_pv_stream<C>(prev, pr, pw, sc, s, lo, va, pb, end - (start + t * C::T), p.scale_log2, first);
+  softmax_pv_stream<C>(pvs, pw, sc, s, end - (start + t * C::T), p.scale_log2, first);
   wait_vmem_le<LPT>();
   tile_barrier();
 }

@@ -318,6 +318,165 @@ __global__ __launch_bounds__(256, 2) void outproj_bf16_kernel(GemmParams p) {
   }
 }
 
+// ---- split merge + out-proj in one pass: W [N=128][K=512] per head, bf16
+// partials, at most kCoMaxSplits splits. One 512-thread workgroup per (head,
+// 64 columns), per 32-row batch block:
+//   1. merge weights e^(lse_s - max) / z per (row, split) into LDS;
+//   2. the merge: wave w takes rows w, w + 8, w + 16, w + 24, each wave
+//      instruction reading one split's whole 1 KiB row (64 lanes x 16 bytes),
+//      so the weights are wave-uniform; fp32 sums, times 1/z, rounded to
+//      bf16 (the values a bf16 mla_combine output would hold) and stored to
+//      LDS with 16-byte chunks XOR-swizzled by the row;
+//   3. wave w reads its k range (64w .. 64w + 63) of all 32 rows as MFMA A
+//      fragments, multiplies by W_UV and the eight K-partials are added
+//      through LDS.
+// The merged latent rows never go to memory.
+constexpr int kCoK = 512, kCoN = 128, kCoNT = 64, kCoWaves = 8, kCoMaxSplits = 64;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(CombineOutParams p) {
+  __shared__ __attribute__((aligned(16))) float part[kCoWaves * 64 * 32];   // [wave][lane][fragment][16]
+  __shared__ __attribute__((aligned(16))) uint16_t olat[32 * kCoK];         // merged rows, bf16, swizzled
+  __shared__ float wts[32 * kCoMaxSplits];                                  // [row][split]
+  __shared__ float inv_z[32];
+  const int h = blockIdx.x, n0 = blockIdx.y * kCoNT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, r = lane & 31;
+  constexpr int KCW = kCoK / 16 / kCoWaves;               // 16-wide k blocks per wave (4)
+  const int S = p.splits, H = p.heads;
+  const int kw = 16 * KCW * wave + 8 * hh;                // this lane's first k in the products
+
+  // W_UV fragments of the two 32-column fragments: W[h][n0 + 32f + r][kw + 16q ..]
+  bf16x8 wf[2][KCW];
+  {
+    const __bf16* wrow = (const __bf16*)p.w + ((int64_t)h * kCoN + n0 + r) * kCoK + kw;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int q = 0; q < KCW; ++q) wf[f][q] = *(const bf16x8*)(wrow + (int64_t)32 * f * kCoK + 16 * q);
+  }
+  const int64_t split_stride = (int64_t)H * kCoK * 2;      // bytes between two splits of one (b, h)
+  const int64_t row_stride = (int64_t)S * split_stride;    // bytes between two batch rows
+
+  for (int b0 = 0; b0 < p.batch; b0 += 32) {
+    // 1. merge weights: thread (row = tid / 16, lane group s16 = tid % 16)
+    //    takes splits s16, s16 + 16, ...
+    {
+      const int row = tid >> 4, s16 = tid & 15;
+      const int b = min(b0 + row, p.batch - 1);
+      const float* lse_row = p.lse_part + (int64_t)b * S * H + h;
+      float l[kCoMaxSplits / 16];
+      float m = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kCoMaxSplits / 16; ++k) {
+        const int sp = s16 + 16 * k;
+        l[k] = sp < S ? lse_row[(int64_t)sp * H] : -INFINITY;
+        m = fmaxf(m, l[k]);
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const bool empty = (m == -INFINITY);
+      float z = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kCoMaxSplits / 16; ++k) {
+        const int sp = s16 + 16 * k;
+        const float w = (empty || l[k] == -INFINITY) ? 0.0f : fast_exp2((l[k] - m) * kLog2e);
+        if (sp < S) wts[row * kCoMaxSplits + sp] = w;
+        z += w;
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+      if (s16 == 0) {
+        inv_z[row] = empty ? 0.0f : 1.0f / z;
+        if (blockIdx.y == 0 && b0 + row < p.batch && p.lse != nullptr)
+          p.lse[(int64_t)(b0 + row) * H + h] = empty ? -INFINITY : m + fast_log2(z) * kLn2;
+      }
+    }
+    __syncthreads();
+
+    // 2. merge: wave w, rows w + 8j; lane = 16-byte chunk of the row
+    {
+      const char* base = (const char*)p.o_part + (int64_t)h * kCoK * 2 + lane * 16;
+      float acc[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+      constexpr int SC = 4;                                // splits in flight
+      for (int s0 = 0; s0 < S; s0 += SC) {
+        u32x4 x[SC][4];
+#pragma unroll
+        for (int i = 0; i < SC; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int b = min(b0 + wave + 8 * j, p.batch - 1);
+            x[i][j] = load16(base + b * row_stride + min(s0 + i, S - 1) * split_stride);
+          }
+#pragma unroll
+        for (int i = 0; i < SC; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            // a split with weight 0 (empty, or past S) has its words zeroed,
+            // so whatever it holds cannot reach the sum
+            const float w = s0 + i < S ? wts[(wave + 8 * j) * kCoMaxSplits + s0 + i] : 0.0f;
+            const bool skip = (w == 0.0f);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t v = skip ? 0u : (uint32_t)x[i][j][d];
+              acc[j][2 * d] = fmaf(w, __builtin_bit_cast(float, v << 16), acc[j][2 * d]);
+              acc[j][2 * d + 1] = fmaf(w, __builtin_bit_cast(float, v & 0xffff0000u), acc[j][2 * d + 1]);
+            }
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = wave + 8 * j;
+        const float inv = inv_z[row];
+        u32x4 o;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[j][2 * d] * inv, acc[j][2 * d + 1] * inv);
+        *(u32x4*)(olat + row * kCoK + 8 * (lane ^ (row & 15))) = o;
+      }
+    }
+    __syncthreads();
+
+    // 3. products: A fragment (row r, k block q) of this wave's k range
+    f32x16 c[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int q = 0; q < KCW; ++q) {
+      const int chunk = (kw + 16 * q) >> 3;
+      const bf16x8 a = *(const bf16x8*)(olat + r * kCoK + 8 * (chunk ^ (r & 15)));
+#pragma unroll
+      for (int f = 0; f < 2; ++f) c[f] = mfma32x32x16(a, wf[f][q], c[f]);
+    }
+    float* dst = part + (wave * 64 + lane) * 32;
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(dst + 16 * f + 4 * g) = f32x4{c[f][4 * g], c[f][4 * g + 1], c[f][4 * g + 2], c[f][4 * g + 3]};
+    __syncthreads();
+    {
+      // thread t: lane t % 64, fragment f and accumulator group j from t / 64;
+      // accumulator 4j + i of lane (hh, c) is row 8j + 4hh + i, column n0 + 32f + c
+      const int ln = tid & 63, grp = tid >> 6, f = grp >> 2, j = grp & 3;
+      f32x4 v = f32x4{};
+#pragma unroll
+      for (int w = 0; w < kCoWaves; ++w) v += *(const f32x4*)(part + (w * 64 + ln) * 32 + 16 * f + 4 * j);
+      const int col = n0 + 32 * f + (ln & 31);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = b0 + 8 * j + 4 * (ln >> 5) + i;
+        if (row < p.batch) {
+          const int64_t o = ((int64_t)row * H + h) * kCoN + col;
+          if constexpr (OUT_F32) ((float*)p.out)[o] = v[i];
+          else ((__bf16*)p.out)[o] = (__bf16)v[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <bool F32, bool W_KN, int K, int N>
 hipError_t launch(const GemmParams& p, hipStream_t s) {
   using G = GemmCfg<F32, W_KN, K, N>;
@@ -348,6 +507,17 @@ hipError_t launch_outproj_dsv2_bf16(const GemmParams& p, hipStream_t s) {
 }
 hipError_t launch_outproj_tiny_f32(const GemmParams& p, hipStream_t s) {
   return launch<true, false, 32, 32>(p, s);
+}
+int combine_outproj_max_splits() { return kCoMaxSplits; }
+hipError_t launch_combine_outproj_dsv2_bf16(const CombineOutParams& p, hipStream_t s) {
+  if (p.batch == 0) return hipSuccess;
+  if (p.splits > kCoMaxSplits) return hipErrorInvalidValue;
+  const dim3 grid(p.heads, kCoN / kCoNT), block(64 * kCoWaves);
+  if (p.out_f32)
+    hipLaunchKernelGGL(combine_outproj_kernel<true>, grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL(combine_outproj_kernel<false>, grid, block, 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace mla

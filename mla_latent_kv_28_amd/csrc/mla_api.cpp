@@ -232,4 +232,32 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const void* o_lat, 
                                        : mla::launch_outproj_tiny_f32(p, s));
 }
 
+mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num_splits, const void* o_part,
+                                int32_t part_dtype, const float* lse_part, const void* w_uv, int32_t w_dtype,
+                                void* out, int32_t out_dtype, float* lse, mla_stream stream) {
+  if (dims == nullptr) return MLA_ERR_NULL;
+  if (batch < 0 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (!valid_dtype(part_dtype) || !valid_dtype(w_dtype) || !valid_dtype(out_dtype)) return MLA_ERR_DTYPE;
+  const Shape sh = shape_of(dims);
+  if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
+  if (sh != Shape::kDsv2) return MLA_ERR_UNSUPPORTED;                  // the 16-bit DeepSeek-V2 shape only
+  if (part_dtype != MLA_BF16 || w_dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (out_dtype != MLA_BF16 && out_dtype != MLA_F32) return MLA_ERR_DTYPE;
+  if (num_splits > mla::combine_outproj_max_splits()) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!o_part || !lse_part || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  mla::CombineOutParams p{};
+  p.o_part = o_part;
+  p.lse_part = lse_part;
+  p.w = w_uv;
+  p.out = out;
+  p.lse = lse;
+  p.batch = batch;
+  p.splits = num_splits;
+  p.heads = dims->num_heads;
+  p.out_f32 = out_dtype == MLA_F32;
+  return hip_status(mla::launch_combine_outproj_dsv2_bf16(p, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

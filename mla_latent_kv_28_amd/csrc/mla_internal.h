@@ -65,4 +65,17 @@ hipError_t launch_absorb_tiny_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_outproj_dsv2_bf16(const GemmParams& p, hipStream_t s);
 hipError_t launch_outproj_tiny_f32(const GemmParams& p, hipStream_t s);
 
+// Split merge and out-projection in one pass (DeepSeek-V2 shapes, bf16).
+struct CombineOutParams {
+  const void* o_part;    // [B, S, H, DC] bf16
+  const float* lse_part; // [B, S, H]
+  const void* w;         // W_UV [H, DV, DC] bf16
+  void* out;             // [B, H, DV] (bf16 | f32)
+  float* lse;            // [B, H] or null
+  int32_t batch, splits, heads;
+  int32_t out_f32;
+};
+hipError_t launch_combine_outproj_dsv2_bf16(const CombineOutParams& p, hipStream_t s);
+int combine_outproj_max_splits();
+
 }  // namespace mla

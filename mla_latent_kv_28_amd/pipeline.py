@@ -6,8 +6,8 @@ the current stream. Allocation happens once, in the constructor.
 
 import torch
 
-from . import (BF16, F32, FP8_E4M3, kv_cache, mla_absorb_q, mla_combine, mla_decode,
-               mla_out_proj, mla_suggest_splits)
+from . import (BF16, F32, FP8_E4M3, kv_cache, mla_absorb_q, mla_combine, mla_combine_out_proj,
+               mla_decode, mla_out_proj, mla_suggest_splits)
 
 NUM_CUS = 256
 
@@ -21,9 +21,13 @@ class DecodePipeline:
     o_lat_dtype: precision of the merged latent output handed to out-proj, and
                  of the split partials when there is more than one split.
     out_dtype:   precision of the final per-head output.
+    fuse:        with several splits of bf16 partials at the DeepSeek-V2 shape,
+                 run merge and out-proj as one call (mla_combine_out_proj; o_lat
+                 is then not written).
     """
 
-    def __init__(self, inp, num_splits=None, o_lat_dtype=None, out_dtype=None, device="cuda"):
+    def __init__(self, inp, num_splits=None, o_lat_dtype=None, out_dtype=None, device="cuda",
+                 fuse=True):
         d = inp.dims
         self.dims = d
         self.batch = inp.batch
@@ -70,6 +74,8 @@ class DecodePipeline:
         else:
             self.o_part = self.lse_part = None
         self.o_lat = torch.empty((B, H, d.d_latent), dtype=odt, device=dev)
+        self.fused = (fuse and 1 < S <= 64 and self.o_lat_dtype == BF16 and self.compute == BF16
+                      and (d.num_heads, d.d_latent, d.d_rope, d.d_nope, d.d_v) == (128, 512, 64, 128, 128))
         self.lse = torch.empty((B, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((B, H, d.d_v), dtype=fdt, device=dev)
 
@@ -96,9 +102,17 @@ class DecodePipeline:
         mla_out_proj(self.dims, self.batch, self.o_lat, self.o_lat_dtype, self.w_uv,
                      self.compute, self.out, self.out_dtype, stream)
 
+    def combine_out_proj(self, stream=None):
+        mla_combine_out_proj(self.dims, self.batch, self.num_splits, self.o_part, self.o_lat_dtype,
+                             self.lse_part, self.w_uv, self.compute, self.out, self.out_dtype, self.lse,
+                             stream)
+
     def run(self, stream=None):
         self.absorb(stream)
         self.decode(stream)
-        self.combine(stream)
-        self.out_proj(stream)
+        if self.fused:
+            self.combine_out_proj(stream)
+        else:
+            self.combine(stream)
+            self.out_proj(stream)
         return self.out, self.lse

@@ -155,6 +155,24 @@ def test_absorb_combine_outproj_argument_errors(L):
     assert L.mla_out_proj(d, 0, None, mla.BF16, None, mla.BF16, None, mla.BF16, None) == 0
 
 
+@no_gpu
+def test_combine_out_proj_argument_errors(L):
+    d = ctypes.byref(DSV2)
+    f = L.mla_combine_out_proj
+    assert f(None, 1, 2, P, mla.BF16, P, P, mla.BF16, P, mla.BF16, P, None) == -1
+    assert f(d, -1, 2, P, mla.BF16, P, P, mla.BF16, P, mla.BF16, P, None) == -2
+    assert f(d, 1, 0, P, mla.BF16, P, P, mla.BF16, P, mla.BF16, P, None) == -2
+    assert f(ctypes.byref(TINY), 1, 2, P, mla.BF16, P, P, mla.BF16, P, mla.BF16, P, None) == -4
+    assert f(d, 1, 2, P, mla.F32, P, P, mla.BF16, P, mla.BF16, P, None) == -3      # bf16 partials only
+    assert f(d, 1, 2, P, mla.BF16, P, P, mla.F32, P, mla.BF16, P, None) == -3      # bf16 weights only
+    assert f(d, 1, 2, P, mla.BF16, P, P, mla.BF16, P, mla.FP8_E4M3, P, None) == -3
+    assert f(d, 1, 65, P, mla.BF16, P, P, mla.BF16, P, mla.BF16, P, None) == -4      # at most 64 splits
+    assert f(d, 1, 2, None, mla.BF16, P, P, mla.BF16, P, mla.BF16, P, None) == -1
+    assert f(d, 1, 2, P, mla.BF16, P, None, mla.BF16, P, mla.BF16, P, None) == -1
+    assert f(d, 1, 2, P, mla.BF16, P, P, mla.BF16, P + 8, mla.BF16, P, None) == -5
+    assert f(d, 0, 2, None, mla.BF16, None, None, mla.BF16, None, mla.BF16, None, None) == 0
+
+
 def test_binding_refuses_host_tensors(L):
     # the binding never hands a host pointer to the library
     x = torch.zeros(4)

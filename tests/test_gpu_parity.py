@@ -281,3 +281,51 @@ def test_combine_against_oracle_merge(splits, part_dtype):
     np.testing.assert_allclose(got, ref_o, rtol=0, atol=2e-5 * max(1.0, np.abs(ref_o).max()))
     fin = np.isfinite(ref_l)
     np.testing.assert_allclose(lse_out.double().cpu().numpy()[fin], ref_l[fin], rtol=0, atol=2e-5 * 8)
+
+
+@pytest.mark.parametrize("splits,out_dtype", [(2, 0), (3, 0), (8, 0), (8, 1), (13, 0), (64, 0)])
+def test_combine_out_proj_against_oracle_and_separate_calls(splits, out_dtype):
+    # merge + out-proj in one call: the oracle's LSE merge followed by the
+    # W_UV product, and the same result as mla_combine (bf16 latent output)
+    # followed by mla_out_proj; 33 rows cover a second, ragged batch block
+    import mla_latent_kv_28_amd as mla
+    from mla_synth import DSV2
+    B, H, D, V = 33, DSV2.num_heads, DSV2.d_latent, DSV2.d_v
+    rng = np.random.default_rng(23 + splits)
+    o = rng.standard_normal((B, splits, H, D)).astype(np.float32)
+    lse = (rng.standard_normal((B, splits, H)) * 3.0).astype(np.float32)
+    lse[0, :, :5] = -np.inf                          # heads with no tokens at all
+    lse[1, 1, :] = -np.inf                           # an empty split holding garbage
+    o[1, 1] = np.nan
+    w = (rng.standard_normal((H, V, D)) / math.sqrt(D)).astype(np.float32)
+    o_dev = torch.from_numpy(o).to(torch.bfloat16).cuda()
+    lse_dev = torch.from_numpy(lse).cuda()
+    w_dev = torch.from_numpy(w).to(torch.bfloat16).cuda()
+    odt = torch.float32 if out_dtype == mla.F32 else torch.bfloat16
+    out = torch.empty((B, H, V), dtype=odt, device="cuda")
+    lse_out = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    print("case: combine_out_proj S=%d out_dtype=%d" % (splits, out_dtype), flush=True)
+    mla.mla_combine_out_proj(DSV2, B, splits, o_dev, mla.BF16, lse_dev, w_dev, mla.BF16, out, out_dtype,
+                             lse_out)
+    o_lat = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
+    lse_sep = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out_sep = torch.empty((B, H, V), dtype=odt, device="cuda")
+    mla.mla_combine(DSV2, B, splits, o_dev, mla.BF16, lse_dev, o_lat, lse_sep, mla.BF16)
+    mla.mla_out_proj(DSV2, B, o_lat, mla.BF16, w_dev, mla.BF16, out_sep, out_dtype)
+    torch.cuda.synchronize()
+
+    o_in = np.nan_to_num(o_dev.double().cpu().numpy(), nan=0.0)
+    w_in = w_dev.double().cpu().numpy()
+    ref_o, ref_l = oracle.lse_merge(np.moveaxis(o_in, 1, 0), np.moveaxis(lse.astype(np.float64), 1, 0))
+    ref = np.einsum("bhc,hvc->bhv", ref_o, w_in)
+    got = out.double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.all(got[0, :5] == 0) and np.all(lse_out[0, :5].cpu().numpy() == -np.inf)
+    _check(got, ref, BF16_REL, BF16_ABS)
+    fin = np.isfinite(ref_l)
+    np.testing.assert_allclose(lse_out.double().cpu().numpy()[fin], ref_l[fin], rtol=0, atol=2e-5 * 8)
+    # the separate calls round the same merged rows to bf16; only the order of
+    # the weight sum differs, so the two agree to a few bf16 steps of the rows
+    sep = out_sep.double().cpu().numpy()
+    scale = np.abs(ref).max()
+    assert np.abs(got - sep).max() <= 4e-3 * scale
