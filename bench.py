@@ -188,12 +188,13 @@ def main():
         del src, dst
 
     def in_step_kernel_times(n):
-        """HIP events on the stream around the decode and combine launches of n
-        whole steps launched eagerly (absorb -> decode -> combine -> out-proj):
-        each kernel's duration in the step's own context. A spin kernel of
-        about 10 ms goes first, so that all n steps are queued before the GPU
-        reaches them and no host launch gap falls between an event and its
-        kernel (each event still adds a few microseconds of its own)."""
+        """HIP events on the stream around the decode launch and around the rest
+        of the step (split merge and out-projection, one fused call where the
+        pipeline uses it) in n whole steps launched eagerly: each part's
+        duration in the step's own context. A spin kernel of about 10 ms goes
+        first, so that all n steps are queued before the GPU reaches them and
+        no host launch gap falls between an event and its kernel (each event
+        still adds a few microseconds of its own)."""
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
         with torch.cuda.stream(stream):
             for i in range(2 * nbuf):
@@ -205,17 +206,20 @@ def main():
                 ev[i][0].record(stream)
                 pipe.decode()
                 ev[i][1].record(stream)
-                pipe.combine()
+                if pipe.fused:
+                    pipe.combine_out_proj()
+                else:
+                    pipe.combine()
+                    pipe.out_proj()
                 ev[i][2].record(stream)
-                pipe.out_proj()
         torch.cuda.synchronize()
         dec = sum(e[0].elapsed_time(e[1]) for e in ev) / n
-        dc = sum(e[0].elapsed_time(e[2]) for e in ev) / n
-        return dec, dc
+        rest = sum(e[1].elapsed_time(e[2]) for e in ev) / n
+        return dec, rest
 
     torch.cuda.synchronize()
     ms_step, nsteps = timed("step", step, args.steps, args.warmup)
-    ms_dec, ms_dc = in_step_kernel_times(max(args.steps, 10))
+    ms_dec, ms_rest = in_step_kernel_times(max(args.steps, 10))
 
     q_step = B / (ms_step * 1e-3)
     gbps_step = cache_bytes / (ms_step * 1e-3) / 1e9
@@ -243,7 +247,8 @@ def main():
         },
         "cache_GBps": round(gbps_step, 1),
         "cache_GBps_frac_of_8TBps": round(gbps_step / HBM_PEAK_GBPS, 4),
-        "decode_plus_combine_queries_per_s": round(B / (ms_dc * 1e-3), 1),
+        "merge_out_proj_us": round(ms_rest * 1e3, 3),
+        "merge_out_proj_fused": bool(pipe.fused),
         "roofline": {
             "kernel": "mla_decode",
             "bound": "hbm",

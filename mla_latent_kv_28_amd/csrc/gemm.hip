@@ -320,160 +320,206 @@ __global__ __launch_bounds__(256, 2) void outproj_bf16_kernel(GemmParams p) {
 
 // ---- split merge + out-proj in one pass: W [N=128][K=512] per head, bf16
 // partials, at most kCoMaxSplits splits. One 512-thread workgroup per (head,
-// 64 columns), per 32-row batch block:
-//   1. merge weights e^(lse_s - max) / z per (row, split) into LDS;
-//   2. the merge: wave w takes rows w, w + 8, w + 16, w + 24, each wave
-//      instruction reading one split's whole 1 KiB row (64 lanes x 16 bytes),
-//      so the weights are wave-uniform; fp32 sums, times 1/z, rounded to
-//      bf16 (the values a bf16 mla_combine output would hold) and stored to
-//      LDS with 16-byte chunks XOR-swizzled by the row;
-//   3. wave w reads its k range (64w .. 64w + 63) of all 32 rows as MFMA A
-//      fragments, multiplies by W_UV and the eight K-partials are added
+// block of 16 batch rows), so every partial row is read once and the merge
+// work spreads over twice as many compute units as heads:
+//   1. all loads are requested at once: the partial LSEs, the first eight
+//      splits' partial rows (wave w takes rows w and w + 8, each wave
+//      instruction one split's whole 1 KiB row through a buffer descriptor
+//      with the row and split in the scalar offset) and the head's W_UV rows
+//      (wave w takes rows 16w .. 16w + 15, one 1 KiB row per instruction);
+//   2. merge weights e^(lse_s - max) per (row, split) stay in the lanes that
+//      computed them (lane 16j + s of wave w: row w + 8j, split s) and are
+//      read with readlane;
+//   3. the merge: fp32 sums, times 1/z, rounded to bf16 (the values a bf16
+//      mla_combine output would hold) and stored to LDS, as are the W_UV rows;
+//   4. wave w multiplies the merged rows by columns 32(w % 4) .. + 31 of
+//      W_UV over k half w / 4 (a 32-row MFMA whose rows 16..31 are not
+//      stored), both operands read from LDS; the two k halves are added
 //      through LDS.
-// The merged latent rows never go to memory.
-constexpr int kCoK = 512, kCoN = 128, kCoNT = 64, kCoWaves = 8, kCoMaxSplits = 64;
+// LDS rows of 1 KiB (W_UV rows and merged rows) have their 16-byte chunks
+// XOR-swizzled by the row, so 16 consecutive rows read at one chunk hit 16
+// different bank groups.
+constexpr int kCoK = 512, kCoN = 128, kCoWaves = 8, kCoMaxSplits = 64, kCoSC = 8, kCoRows = 16;
+static_assert(kCoMaxSplits % kCoSC == 0 && kCoMaxSplits % 16 == 0 && 16 % kCoSC == 0, "split chunks");
+static_assert(kCoRows == 2 * kCoWaves, "two merged rows per wave");
+constexpr int kCoRow = kCoK * 2;                          // bytes of one bf16 row
+constexpr int kCoLds = kCoN * kCoRow + 32 * kCoRow;      // W_UV rows + 32 MFMA rows: 160 KiB
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ int co_chunk(int row, int chunk) { return row * kCoRow + 16 * (chunk ^ (row & 15)); }
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {   // in-row lane permutation (every source lane valid)
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// Reduction over each row of 16 lanes by DPP (swap neighbours, swap pairs,
+// mirror halves, mirror the row); every lane of the row gets the same value.
+template <class Op>
+__device__ __forceinline__ float row16_reduce(float v, Op op) {
+  v = op(v, dpp_move<0xb1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4e>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));   // row_half_mirror
+  return op(v, dpp_move<0x140>(v));   // row_mirror
+}
 
 template <bool OUT_F32>
 __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(CombineOutParams p) {
-  __shared__ __attribute__((aligned(16))) float part[kCoWaves * 64 * 32];   // [wave][lane][fragment][16]
-  __shared__ __attribute__((aligned(16))) uint16_t olat[32 * kCoK];         // merged rows, bf16, swizzled
-  __shared__ float wts[32 * kCoMaxSplits];                                  // [row][split]
-  __shared__ float inv_z[32];
-  const int h = blockIdx.x, n0 = blockIdx.y * kCoNT;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, r = lane & 31;
-  constexpr int KCW = kCoK / 16 / kCoWaves;               // 16-wide k blocks per wave (4)
+  __shared__ __attribute__((aligned(16))) char smem[kCoLds];
+  MLA_LDS char* wl = (MLA_LDS char*)smem;                 // W_UV rows of the head
+  MLA_LDS char* ol = wl + kCoN * kCoRow;                  // merged rows; then the k-half sums
+  const int h = blockIdx.x, b0 = blockIdx.y * kCoRows, rows = min(kCoRows, p.batch - b0);
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, r = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = p.splits, H = p.heads;
-  const int kw = 16 * KCW * wave + 8 * hh;                // this lane's first k in the products
+  const int split_stride = H * kCoRow;                    // bytes between two splits of one (b, h)
+  const int row_stride = S * split_stride;                // bytes between two batch rows
+  const int j16 = lane >> 4, s16 = lane & 15;             // weight lanes: row wave + 8 j16, split s16 + 16k
+  const int lrow = wave + 8 * (j16 & 1);                  // lanes 32..63 repeat rows of lanes 0..31
 
-  // W_UV fragments of the two 32-column fragments: W[h][n0 + 32f + r][kw + 16q ..]
-  bf16x8 wf[2][KCW];
+  // 1. partial LSEs (splits past S read split S - 1 and are masked after
+  //    the load, so no branch surrounds it)
+  float l[kCoMaxSplits / 16];
   {
-    const __bf16* wrow = (const __bf16*)p.w + ((int64_t)h * kCoN + n0 + r) * kCoK + kw;
+    const float* lse_row = p.lse_part + (int64_t)(b0 + min(lrow, rows - 1)) * S * H + h;
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int q = 0; q < KCW; ++q) wf[f][q] = *(const bf16x8*)(wrow + (int64_t)32 * f * kCoK + 16 * q);
+    for (int k = 0; k < kCoMaxSplits / 16; ++k) {
+      const int sp = s16 + 16 * k;
+      const float v = lse_row[(int64_t)min(sp, S - 1) * H];
+      l[k] = sp < S ? v : -INFINITY;
+    }
   }
-  const int64_t split_stride = (int64_t)H * kCoK * 2;      // bytes between two splits of one (b, h)
-  const int64_t row_stride = (int64_t)S * split_stride;    // bytes between two batch rows
+  // partial rows of the block: byte offset row * row_stride + split *
+  // split_stride from the head's first row (below 2^31 for 16 rows of at
+  // most 64 splits of 128 heads)
+  const __amdgpu_buffer_rsrc_t part_rs =
+      buffer_rsrc((const char*)p.o_part + ((int64_t)b0 * S * H + h) * kCoRow, rows * row_stride - h * kCoRow);
+  u32x4 x[kCoSC][2];
+  auto issue = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < kCoSC; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rr = min(wave + 8 * j, rows - 1), sp = min(s0 + i, S - 1);
+        x[i][j] = __builtin_amdgcn_raw_buffer_load_b128(part_rs, lane * 16, rr * row_stride + sp * split_stride, 0);
+      }
+  };
+  issue(0);
+  u32x4 wrow[kCoN / kCoWaves];
+  {
+    const char* wh = (const char*)p.w + ((int64_t)h * kCoN + wave * (kCoN / kCoWaves)) * kCoRow + lane * 16;
+#pragma unroll
+    for (int k = 0; k < kCoN / kCoWaves; ++k) wrow[k] = load16(wh + k * kCoRow);
+  }
 
-  for (int b0 = 0; b0 < p.batch; b0 += 32) {
-    // 1. merge weights: thread (row = tid / 16, lane group s16 = tid % 16)
-    //    takes splits s16, s16 + 16, ...
-    {
-      const int row = tid >> 4, s16 = tid & 15;
-      const int b = min(b0 + row, p.batch - 1);
-      const float* lse_row = p.lse_part + (int64_t)b * S * H + h;
-      float l[kCoMaxSplits / 16];
-      float m = -INFINITY;
+  // 2. merge weights of (row lrow, splits s16 + 16k)
+  float wk[kCoMaxSplits / 16], inv;
+  {
+    float m = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < kCoMaxSplits / 16; ++k) {
-        const int sp = s16 + 16 * k;
-        l[k] = sp < S ? lse_row[(int64_t)sp * H] : -INFINITY;
-        m = fmaxf(m, l[k]);
-      }
+    for (int k = 0; k < kCoMaxSplits / 16; ++k) m = fmaxf(m, l[k]);
+    m = row16_reduce(m, [](float u, float v) { return fmaxf(u, v); });
+    const bool empty = (m == -INFINITY);
+    float z = 0.0f;
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      const bool empty = (m == -INFINITY);
-      float z = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kCoMaxSplits / 16; ++k) {
-        const int sp = s16 + 16 * k;
-        const float w = (empty || l[k] == -INFINITY) ? 0.0f : fast_exp2((l[k] - m) * kLog2e);
-        if (sp < S) wts[row * kCoMaxSplits + sp] = w;
-        z += w;
-      }
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-      if (s16 == 0) {
-        inv_z[row] = empty ? 0.0f : 1.0f / z;
-        if (blockIdx.y == 0 && b0 + row < p.batch && p.lse != nullptr)
-          p.lse[(int64_t)(b0 + row) * H + h] = empty ? -INFINITY : m + fast_log2(z) * kLn2;
-      }
+    for (int k = 0; k < kCoMaxSplits / 16; ++k) {
+      wk[k] = (empty || l[k] == -INFINITY) ? 0.0f : fast_exp2((l[k] - m) * kLog2e);
+      z += wk[k];
     }
-    __syncthreads();
+    z = row16_reduce(z, [](float u, float v) { return u + v; });
+    inv = empty ? 0.0f : 1.0f / z;
+    if (s16 == 0 && j16 < 2 && lrow < rows && p.lse != nullptr)
+      p.lse[(int64_t)(b0 + lrow) * H + h] = empty ? -INFINITY : m + fast_log2(z) * kLn2;
+  }
 
-    // 2. merge: wave w, rows w + 8j; lane = 16-byte chunk of the row
-    {
-      const char* base = (const char*)p.o_part + (int64_t)h * kCoK * 2 + lane * 16;
-      float acc[4][8];
+  // 3. merge: wave w, rows w + 8j; lane = 16-byte chunk of the row
+  float acc[2][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
-      constexpr int SC = 4;                                // splits in flight
-      for (int s0 = 0; s0 < S; s0 += SC) {
-        u32x4 x[SC][4];
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+  auto merge = [&](int s0) {
+    // splits s0 .. s0 + kCoSC - 1 share one weight register: s0 / 16
+    const int kk = s0 >> 4, lo = s0 & 15;
+    const float wsel = kk == 0 ? wk[0] : kk == 1 ? wk[1] : kk == 2 ? wk[2] : wk[3];
 #pragma unroll
-        for (int i = 0; i < SC; ++i)
+    for (int i = 0; i < kCoSC; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int b = min(b0 + wave + 8 * j, p.batch - 1);
-            x[i][j] = load16(base + b * row_stride + min(s0 + i, S - 1) * split_stride);
-          }
+      for (int j = 0; j < 2; ++j) {
+        // a split with weight 0 (empty, or past S) has its words zeroed,
+        // so whatever it holds cannot reach the sum: the byte selectors and
+        // the mask are wave-uniform
+        const float w = lane_value(wsel, 16 * j + lo + i);
+        const bool skip = (w == 0.0f);
+        const uint32_t sel_lo = skip ? 0x0c0c0c0cu : 0x01000c0cu;   // (v & 0xffff) << 16, or 0
+        const uint32_t mask_hi = skip ? 0u : 0xffff0000u;
 #pragma unroll
-        for (int i = 0; i < SC; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            // a split with weight 0 (empty, or past S) has its words zeroed,
-            // so whatever it holds cannot reach the sum
-            const float w = s0 + i < S ? wts[(wave + 8 * j) * kCoMaxSplits + s0 + i] : 0.0f;
-            const bool skip = (w == 0.0f);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              const uint32_t v = skip ? 0u : (uint32_t)x[i][j][d];
-              acc[j][2 * d] = fmaf(w, __builtin_bit_cast(float, v << 16), acc[j][2 * d]);
-              acc[j][2 * d + 1] = fmaf(w, __builtin_bit_cast(float, v & 0xffff0000u), acc[j][2 * d + 1]);
-            }
-          }
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t v = x[i][j][d];
+          acc[j][2 * d] = fmaf(w, __builtin_bit_cast(float, __builtin_amdgcn_perm(v, v, sel_lo)), acc[j][2 * d]);
+          acc[j][2 * d + 1] = fmaf(w, __builtin_bit_cast(float, v & mask_hi), acc[j][2 * d + 1]);
+        }
       }
+  };
+  merge(0);
+  for (int s0 = kCoSC; s0 < S; s0 += kCoSC) {
+    issue(s0);
+    merge(s0);
+  }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wave + 8 * j;
-        const float inv = inv_z[row];
-        u32x4 o;
+  for (int j = 0; j < 2; ++j) {
+    const int row = wave + 8 * j;
+    const float iv = lane_value(inv, 16 * j);
+    u32x4 o;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[j][2 * d] * inv, acc[j][2 * d + 1] * inv);
-        *(u32x4*)(olat + row * kCoK + 8 * (lane ^ (row & 15))) = o;
-      }
-    }
-    __syncthreads();
+    for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[j][2 * d] * iv, acc[j][2 * d + 1] * iv);
+    *(MLA_LDS u32x4*)(ol + co_chunk(row, lane)) = o;
+  }
+#pragma unroll
+  for (int k = 0; k < kCoN / kCoWaves; ++k) {
+    const int n = wave * (kCoN / kCoWaves) + k;
+    *(MLA_LDS u32x4*)(wl + co_chunk(n, lane)) = wrow[k];
+  }
+  __syncthreads();
 
-    // 3. products: A fragment (row r, k block q) of this wave's k range
-    f32x16 c[2] = {f32x16{}, f32x16{}};
+  // 4. products: columns 32f .. 32f + 31 over k blocks 16kq .. 16kq + 15
+  //    (rows 16..31 of the A operand are never written; their results are
+  //    dropped)
+  const int f = wave & 3, kq = wave >> 2, n = 32 * f + r;
+  f32x16 c = f32x16{};
 #pragma unroll
-    for (int q = 0; q < KCW; ++q) {
-      const int chunk = (kw + 16 * q) >> 3;
-      const bf16x8 a = *(const bf16x8*)(olat + r * kCoK + 8 * (chunk ^ (r & 15)));
+  for (int q = 0; q < kCoK / 32; ++q) {
+    const int chunk = 2 * (16 * kq + q) + hh;
+    const bf16x8 a = *(const MLA_LDS bf16x8*)(ol + co_chunk(r, chunk));
+    const bf16x8 bw = *(const MLA_LDS bf16x8*)(wl + co_chunk(n, chunk));
+    c = mfma32x32x16(a, bw, c);
+  }
+  __syncthreads();
+  MLA_LDS f32x4* red = (MLA_LDS f32x4*)ol;                // [f][g][lane]: 8 KiB
+  if (kq == 1) {
 #pragma unroll
-      for (int f = 0; f < 2; ++f) c[f] = mfma32x32x16(a, wf[f][q], c[f]);
-    }
-    float* dst = part + (wave * 64 + lane) * 32;
+    for (int g = 0; g < 2; ++g) red[(f * 2 + g) * 64 + lane] = f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+  }
+  __syncthreads();
+  if (kq == 0) {
+    // accumulator 4g + i of lane (hh, r) is row 8g + 4hh + i, column 32f + r
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(f32x4*)(dst + 16 * f + 4 * g) = f32x4{c[f][4 * g], c[f][4 * g + 1], c[f][4 * g + 2], c[f][4 * g + 3]};
-    __syncthreads();
-    {
-      // thread t: lane t % 64, fragment f and accumulator group j from t / 64;
-      // accumulator 4j + i of lane (hh, c) is row 8j + 4hh + i, column n0 + 32f + c
-      const int ln = tid & 63, grp = tid >> 6, f = grp >> 2, j = grp & 3;
-      f32x4 v = f32x4{};
-#pragma unroll
-      for (int w = 0; w < kCoWaves; ++w) v += *(const f32x4*)(part + (w * 64 + ln) * 32 + 16 * f + 4 * j);
-      const int col = n0 + 32 * f + (ln & 31);
+    for (int g = 0; g < 2; ++g) {
+      const f32x4 o = red[(f * 2 + g) * 64 + lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = b0 + 8 * j + 4 * (ln >> 5) + i;
-        if (row < p.batch) {
-          const int64_t o = ((int64_t)row * H + h) * kCoN + col;
-          if constexpr (OUT_F32) ((float*)p.out)[o] = v[i];
-          else ((__bf16*)p.out)[o] = (__bf16)v[i];
+        const int row = 8 * g + 4 * hh + i;
+        const float v = c[4 * g + i] + o[i];
+        if (row < rows) {
+          const int64_t off = ((int64_t)(b0 + row) * H + h) * kCoN + n;
+          if constexpr (OUT_F32) ((float*)p.out)[off] = v;
+          else ((__bf16*)p.out)[off] = (__bf16)v;
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -512,7 +558,7 @@ int combine_outproj_max_splits() { return kCoMaxSplits; }
 hipError_t launch_combine_outproj_dsv2_bf16(const CombineOutParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   if (p.splits > kCoMaxSplits) return hipErrorInvalidValue;
-  const dim3 grid(p.heads, kCoN / kCoNT), block(64 * kCoWaves);
+  const dim3 grid(p.heads, (p.batch + kCoRows - 1) / kCoRows), block(64 * kCoWaves);
   if (p.out_f32)
     hipLaunchKernelGGL(combine_outproj_kernel<true>, grid, block, 0, s, p);
   else
