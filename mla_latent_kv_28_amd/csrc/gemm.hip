@@ -150,35 +150,40 @@ __global__ __launch_bounds__(64) void head_gemm(GemmParams p) {
 }
 
 // ---- bf16 absorb: W [K=128][N=512] per head, one workgroup per (head, 256 columns)
+//
+// The workgroup's 128 x 256 block of W_UK goes to LDS with direct loads (two
+// 512-byte rows per wave instruction). Wave w then owns columns n0 + 64w ..
+// + 63 over the whole k range: its B operands (8 consecutive k of one column
+// per lane) come from transposing LDS reads, so no k-partials have to be
+// added across waves. Row k's 16-byte chunks are XOR-swizzled by 4 (k & 3):
+// the eight rows and four chunks of one transposing read then cover every
+// bank group exactly twice. Results go through LDS so that every global
+// store writes 16 bytes.
 constexpr int kAbsK = 128, kAbsN = 512, kAbsNT = 256;
+constexpr int kAbsRow = kAbsNT * 2;                      // bytes of one staged W row
+
+__device__ __forceinline__ int abs_w_off(int k, int chunk) { return k * kAbsRow + 16 * (chunk ^ (4 * (k & 3))); }
 
 __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(GemmParams p) {
-  // K-partials of the four waves: [wave][i][lane][m] fp32, m = fragment
-  __shared__ __attribute__((aligned(16))) float part[4 * 16 * 64 * 8];
+  __shared__ __attribute__((aligned(16))) char smem[kAbsK * kAbsRow + 32 * kAbsRow];   // W block + result tile
+  MLA_LDS char* wl = (MLA_LDS char*)smem;
+  MLA_LDS char* cl = wl + kAbsK * kAbsRow;
   const int h = blockIdx.x, n0 = blockIdx.y * kAbsNT;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, r = lane & 31;
-  constexpr int KCW = kAbsK / 16 / 4;                     // 16-wide k blocks per wave (2)
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, r = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int KB = kAbsK / 16;                          // 16-wide k blocks
   constexpr int TAIL_CH = 64 / 8;                         // 16-byte chunks of a 64-wide rotary row
   const bool do_tail = blockIdx.y == 0 && p.tail != nullptr;
 
-  // Everything the first batch block needs is requested up front, in one
-  // round trip: the weights, this wave's query rows and the rotary rows.
-  u32x4 raw[KCW][8];
-  const __bf16* wh = (const __bf16*)p.w + (int64_t)h * kAbsK * kAbsN;
-#pragma unroll
-  for (int q = 0; q < KCW; ++q) {
-    const int k0 = 16 * (wave * KCW + q) + 8 * hh;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) raw[q][e] = load16(wh + (int64_t)(k0 + e) * kAbsN + n0 + 8 * r);
-  }
-  auto load_a = [&](int b0, bf16x8 (&a)[KCW]) {
+  // A operands: lane (hh, r) holds row b0 + r, k = 16 kb + 8 hh .. + 7
+  auto load_a = [&](int b0, bf16x8 (&a)[KB]) {
     const int brow = b0 + r;
     const bool ok = brow < p.batch;
-    const __bf16* arow = (const __bf16*)p.a + ((int64_t)(ok ? brow : 0) * p.heads + h) * p.lda;
+    const __bf16* arow = (const __bf16*)p.a + ((int64_t)(ok ? brow : 0) * p.heads + h) * p.lda + 8 * hh;
 #pragma unroll
-    for (int q = 0; q < KCW; ++q) {
-      a[q] = *(const bf16x8*)(arow + 16 * (wave * KCW + q) + 8 * hh);
-      if (!ok) a[q] = bf16x8{};
+    for (int kb = 0; kb < KB; ++kb) {
+      a[kb] = *(const bf16x8*)(arow + 16 * kb);
+      if (!ok) a[kb] = bf16x8{};
     }
   };
   // rotary rows: one 16-byte chunk per thread (32 rows x 8 chunks)
@@ -186,67 +191,61 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(GemmParams p) {
     const int row = min(b0 + tid / TAIL_CH, p.batch - 1);
     return load16((const __bf16*)p.tail + ((int64_t)row * p.heads + h) * 64 + 8 * (tid % TAIL_CH));
   };
-  bf16x8 a_next[KCW];
+  bf16x8 a_next[KB];
   load_a(0, a_next);
   u32x4 tail_next = do_tail ? load_tail(0) : u32x4{};
-
-  bf16x8 wf[KCW][8];
+  {
+    // W rows k = 2i, 2i + 1: lane c of the instruction fills physical chunk
+    // c & 31 of row 2i + c / 32 with the logical chunk it stands for
+    const char* wsrc = (const char*)p.w + (int64_t)h * kAbsK * kAbsN * 2 + n0 * 2;
 #pragma unroll
-  for (int q = 0; q < KCW; ++q)
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      u32x4 f;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        f[d] = (m & 1) ? pack_hi16(raw[q][2 * d][m >> 1], raw[q][2 * d + 1][m >> 1])
-                       : pack_lo16(raw[q][2 * d][m >> 1], raw[q][2 * d + 1][m >> 1]);
-      wf[q][m] = __builtin_bit_cast(bf16x8, f);
+    for (int i = 0; i < kAbsK / 2 / 4; ++i) {
+      const int pair = wave * (kAbsK / 8) + i, k = 2 * pair + hh;
+      load16_to_lds(wsrc + (int64_t)k * kAbsN * 2 + 16 * ((lane & 31) ^ (4 * (k & 3))), wl + 2 * pair * kAbsRow);
     }
+  }
+  // transposing reads: source lane (a4, e4) of 16-lane group (hh, sub)
+  // points at row 16 kb + 8 hh + 4 q + e4, columns 64w + 32f + 16 sub + 4 a4
+  // .. + 3; lane (hh, r) receives column 64w + 32f + r, rows 8 hh + 4 q .. + 3
+  const int s16 = lane & 15, a4 = s16 & 3, e4 = s16 >> 2, sub = (lane >> 4) & 1;
+  auto w_frag = [&](int kb, int f) -> bf16x8 {
+    const int lc = 8 * wave + 4 * f + 2 * sub + (a4 >> 1);
+    const bf16x4 v0 = lds_read_tr16(wl + abs_w_off(16 * kb + 8 * hh + e4, lc) + 8 * (a4 & 1));
+    const bf16x4 v1 = lds_read_tr16(wl + abs_w_off(16 * kb + 8 * hh + 4 + e4, lc) + 8 * (a4 & 1));
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  wait_vmem();
+  __syncthreads();
 
   for (int b0 = 0; b0 < p.batch; b0 += 32) {
-    bf16x8 a[KCW];
+    bf16x8 a[KB];
 #pragma unroll
-    for (int q = 0; q < KCW; ++q) a[q] = a_next[q];
+    for (int kb = 0; kb < KB; ++kb) a[kb] = a_next[kb];
     const u32x4 tail = tail_next;
     if (b0 + 32 < p.batch) {          // the next block's rows go out before this block's math
       load_a(b0 + 32, a_next);
       if (do_tail) tail_next = load_tail(b0 + 32);
     }
-    f32x16 acc[8];
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int q = 0; q < KCW; ++q)
+      for (int f = 0; f < 2; ++f) acc[f] = mfma32x32x16(a[kb], w_frag(kb, f), acc[f]);
+    // accumulator i of lane (hh, r): row 8(i/4) + 4hh + i%4, column 64w + 32f + r
 #pragma unroll
-      for (int m = 0; m < 8; ++m) acc[m] = mfma32x32x16(a[q], wf[q][m], acc[m]);
-    // accumulator i of lane (hh, c): row 8(i/4) + 4hh + i%4, columns n0 + 8c + m
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float* dst = part + ((wave * 16 + i) * 64 + lane) * 8;
-      *(f32x4*)dst = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-      *(f32x4*)(dst + 4) = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * hh + (i & 3);
+        *(MLA_LDS __bf16*)(cl + row * kAbsRow + 2 * (64 * wave + 32 * f + r)) = (__bf16)acc[f][i];
+      }
     __syncthreads();
-    // each thread sums four (i, lane) pairs over the waves: eight consecutive
-    // columns of one row, one 16-byte store
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int pr = k * 256 + tid, i = pr >> 6, ln = pr & 63;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float* src = part + ((w * 16 + i) * 64 + ln) * 8;
-        const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { v[e] += x0[e]; v[4 + e] += x1[e]; }
-      }
-      const int row = b0 + 8 * (i >> 2) + 4 * (ln >> 5) + (i & 3);
-      if (row < p.batch) {
-        u32x4 o;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(v[2 * d], v[2 * d + 1]);
-        *(u32x4*)((__bf16*)p.c + ((int64_t)row * p.heads + h) * p.ldc + n0 + 8 * (ln & 31)) = o;
-      }
+    for (int j = 0; j < 32 * kAbsRow / 16 / 256; ++j) {
+      const int c = j * 256 + tid, row = c / (kAbsRow / 16), ch = c % (kAbsRow / 16);
+      const u32x4 v = *(const MLA_LDS u32x4*)(cl + row * kAbsRow + 16 * ch);
+      if (b0 + row < p.batch)
+        *(u32x4*)((__bf16*)p.c + ((int64_t)(b0 + row) * p.heads + h) * p.ldc + n0 + 8 * ch) = v;
     }
     // the rotary query goes after the latent part
     if (do_tail) {
