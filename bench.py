@@ -11,7 +11,8 @@ cannot hold it between steps.
 
 Prints one JSON line: queries/s of the step (value), the decode kernel's
 latent-cache bandwidth against the 8 TB/s HBM peak (roofline; its duration
-from HIP events around each decode launch within eagerly launched steps), and
+from the event pair each decode launch carries within eagerly launched
+steps), and
 the CPU oracle timed on a bounded sample on this host (cpu_baseline).
 """
 
@@ -188,14 +189,21 @@ def main():
         del src, dst
 
     def in_step_kernel_times(n):
-        """HIP events on the stream around the decode launch and around the rest
-        of the step (split merge and out-projection, one fused call where the
-        pipeline uses it) in n whole steps launched eagerly: each part's
-        duration in the step's own context. A spin kernel of about 10 ms goes
-        first, so that all n steps are queued before the GPU reaches them and
-        no host launch gap falls between an event and its kernel (each event
-        still adds a few microseconds of its own)."""
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        """The decode kernel's execution time, and that of the rest of the step
+        (split merge and out-projection, one fused call where the pipeline uses
+        it), in n whole steps launched eagerly on the bench stream: each timed
+        launch carries its HIP event pair (mla_time_next_launch, i.e.
+        hipExtLaunchKernel). A spin kernel of about 10 ms goes first, so that
+        all n steps are queued before the GPU reaches them and run back to
+        back. The events' own packets add a few microseconds per interval (the
+        start timestamp is taken as the previous kernel ends), so the figure
+        is slightly above the kernel's execution interval as a profiler reports
+        it: a conservative duration."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for row in ev:
+            for e in row:
+                e.record(stream)          # torch creates its events lazily
+        torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             for i in range(2 * nbuf):
                 step(i)
@@ -203,18 +211,19 @@ def main():
             for i in range(n):
                 pipe.cache = caches[i % nbuf]
                 pipe.absorb()
-                ev[i][0].record(stream)
+                mla.mla_time_next_launch(ev[i][0], ev[i][1])
                 pipe.decode()
-                ev[i][1].record(stream)
                 if pipe.fused:
+                    mla.mla_time_next_launch(ev[i][2], ev[i][3])
                     pipe.combine_out_proj()
                 else:
+                    mla.mla_time_next_launch(ev[i][2], None)
                     pipe.combine()
+                    mla.mla_time_next_launch(None, ev[i][3])
                     pipe.out_proj()
-                ev[i][2].record(stream)
         torch.cuda.synchronize()
         dec = sum(e[0].elapsed_time(e[1]) for e in ev) / n
-        rest = sum(e[1].elapsed_time(e[2]) for e in ev) / n
+        rest = sum(e[2].elapsed_time(e[3]) for e in ev) / n
         return dec, rest
 
     torch.cuda.synchronize()
@@ -258,7 +267,7 @@ def main():
             "frac": round(gbps_dec / HBM_PEAK_GBPS, 4),
             "traffic": hbm_traffic(inp.name) if S == 8 else None,
             "us_per_launch": round(ms_dec * 1e3, 3),
-            "timing": "HIP events around each decode launch within whole steps",
+            "timing": "event pair carried by each decode launch (hipExtLaunchKernel) within whole steps",
             "algorithmic_bytes_per_launch": cache_bytes,
             "mfma_tflops": round(flops_dec / (ms_dec * 1e-3) / 1e12, 1),
             "mfma_frac_of_bf16_dense_peak": round(flops_dec / (ms_dec * 1e-3) / 2.5e15, 4),

@@ -197,6 +197,19 @@ int32_t mla_split_chunk(int32_t max_seq_len, int32_t num_splits);
 int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tokens,
                            int32_t num_cus);
 
+/*
+ * Measurement hook. The next kernel that an entry point of this library
+ * launches from the calling thread records `start_event` when it begins
+ * executing and `stop_event` when it ends (hipExtLaunchKernel's event pair),
+ * so hipEventElapsedTime on the two gives that kernel's own duration, without
+ * the gaps that events recorded separately on the stream add. Each entry
+ * point launches one kernel. The events are hipEvent_t handles created by
+ * the caller with timing enabled; either may be NULL. The pair is consumed
+ * by that one launch; a call that fails validation launches nothing and
+ * leaves it pending. Always returns MLA_OK.
+ */
+mla_status mla_time_next_launch(void* start_event, void* stop_event);
+
 /* Static, never-NULL description of a status code. */
 const char* mla_status_string(mla_status status);
 

@@ -21,7 +21,8 @@ _STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DT
 
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
-           "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error")
+           "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error",
+           "mla_time_next_launch")
 
 
 class MLAError(RuntimeError):
@@ -68,8 +69,10 @@ def lib():
         L.mla_status_string.argtypes = [i32]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_last_hip_error.argtypes = []
+        L.mla_time_next_launch.argtypes = [vp, vp]
         for name in ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_split_chunk",
-                     "mla_suggest_splits", "mla_last_hip_error"):
+                     "mla_suggest_splits", "mla_last_hip_error", "mla_combine_out_proj",
+                     "mla_time_next_launch"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -200,6 +203,22 @@ def mla_split_chunk(max_seq_len, num_splits):
 
 def mla_suggest_splits(batch, max_seq_len, total_tokens, num_cus):
     return lib().mla_suggest_splits(batch, max_seq_len, total_tokens, num_cus)
+
+
+def mla_time_next_launch(start, stop):
+    """The library's next kernel launch from this thread records `start` and
+    `stop` around its own execution: raw hipEvent_t handles (int), or
+    torch.cuda.Event objects made with enable_timing=True, or None. A torch
+    event must exist already: record it once before handing it over."""
+    def handle(e):
+        if e is None:
+            return None
+        if isinstance(e, int):
+            return ctypes.c_void_p(e)
+        if not e.cuda_event:
+            raise ValueError("record the event once before passing it (torch creates events lazily)")
+        return ctypes.c_void_p(e.cuda_event)
+    return lib().mla_time_next_launch(handle(start), handle(stop))
 
 
 def status_string(status):

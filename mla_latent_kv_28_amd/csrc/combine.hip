@@ -158,9 +158,9 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   const int waves = p.batch * p.heads;
   const dim3 grid((waves + kWaves - 1) / kWaves);
   if (p.part_bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(64 * kWaves), 0, s, p);
+    launch_kernel(combine_kernel<true>, grid, dim3(64 * kWaves), s, p);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(64 * kWaves), 0, s, p);
+    launch_kernel(combine_kernel<false>, grid, dim3(64 * kWaves), s, p);
   return hipGetLastError();
 }
 

@@ -1179,9 +1179,9 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   DecodeParams q = p;
   q.xcd_remap = (grid % 8 == 0 && p.num_splits > 1) ? 1 : 0;
   if (p.page_shift >= 0)
-    hipLaunchKernelGGL((decode_kernel<C, true>), dim3(grid), dim3(C::THREADS), 0, stream, q);
+    launch_kernel((decode_kernel<C, true>), dim3(grid), dim3(C::THREADS), stream, q);
   else
-    hipLaunchKernelGGL((decode_kernel<C, false>), dim3(grid), dim3(C::THREADS), 0, stream, q);
+    launch_kernel((decode_kernel<C, false>), dim3(grid), dim3(C::THREADS), stream, q);
   return hipGetLastError();
 }
 

@@ -527,7 +527,7 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
   using G = GemmCfg<F32, W_KN, K, N>;
   if (p.batch == 0) return hipSuccess;
   dim3 grid(p.heads, N / G::NT, (p.batch + 31) / 32);
-  hipLaunchKernelGGL((head_gemm<F32, W_KN, K, N>), grid, dim3(64), 0, s, p);
+  launch_kernel((head_gemm<F32, W_KN, K, N>), grid, dim3(64), s, p);
   return hipGetLastError();
 }
 
@@ -536,7 +536,7 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 hipError_t launch_absorb_dsv2_bf16(const GemmParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   if (p.tail != nullptr && p.n_tail != 64) return hipErrorInvalidValue;   // 64-wide rotary rows
-  hipLaunchKernelGGL(absorb_bf16_kernel, dim3(p.heads, kAbsN / kAbsNT), dim3(256), 0, s, p);
+  launch_kernel(absorb_bf16_kernel, dim3(p.heads, kAbsN / kAbsNT), dim3(256), s, p);
   return hipGetLastError();
 }
 hipError_t launch_absorb_tiny_f32(const GemmParams& p, hipStream_t s) {
@@ -545,9 +545,9 @@ hipError_t launch_absorb_tiny_f32(const GemmParams& p, hipStream_t s) {
 hipError_t launch_outproj_dsv2_bf16(const GemmParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   if (p.a_f32)
-    hipLaunchKernelGGL(outproj_bf16_kernel<true>, dim3(p.heads, kOutN / kOutNT), dim3(256), 0, s, p);
+    launch_kernel(outproj_bf16_kernel<true>, dim3(p.heads, kOutN / kOutNT), dim3(256), s, p);
   else
-    hipLaunchKernelGGL(outproj_bf16_kernel<false>, dim3(p.heads, kOutN / kOutNT), dim3(256), 0, s, p);
+    launch_kernel(outproj_bf16_kernel<false>, dim3(p.heads, kOutN / kOutNT), dim3(256), s, p);
   return hipGetLastError();
 }
 hipError_t launch_outproj_tiny_f32(const GemmParams& p, hipStream_t s) {
@@ -559,9 +559,9 @@ hipError_t launch_combine_outproj_dsv2_bf16(const CombineOutParams& p, hipStream
   if (p.splits > kCoMaxSplits) return hipErrorInvalidValue;
   const dim3 grid(p.heads, (p.batch + kCoRows - 1) / kCoRows), block(64 * kCoWaves);
   if (p.out_f32)
-    hipLaunchKernelGGL(combine_outproj_kernel<true>, grid, block, 0, s, p);
+    launch_kernel(combine_outproj_kernel<true>, grid, block, s, p);
   else
-    hipLaunchKernelGGL(combine_outproj_kernel<false>, grid, block, 0, s, p);
+    launch_kernel(combine_outproj_kernel<false>, grid, block, s, p);
   return hipGetLastError();
 }
 

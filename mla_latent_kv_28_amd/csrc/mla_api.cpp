@@ -16,6 +16,7 @@ int combine_max_splits();
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
+thread_local hipEvent_t g_next_start = nullptr, g_next_stop = nullptr;   // mla_time_next_launch
 
 enum class Shape { kNone, kDsv2, kTiny };
 
@@ -261,3 +262,17 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
 }
 
 }  // extern "C"
+
+namespace mla {
+void take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = g_next_start;
+  *stop = g_next_stop;
+  g_next_start = g_next_stop = nullptr;
+}
+}  // namespace mla
+
+extern "C" mla_status mla_time_next_launch(void* start_event, void* stop_event) {
+  g_next_start = static_cast<hipEvent_t>(start_event);
+  g_next_stop = static_cast<hipEvent_t>(stop_event);
+  return MLA_OK;
+}

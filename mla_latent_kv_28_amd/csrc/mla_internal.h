@@ -1,6 +1,7 @@
 // Host-side launch interface between the C ABI (mla_api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,5 +78,23 @@ struct CombineOutParams {
 };
 hipError_t launch_combine_outproj_dsv2_bf16(const CombineOutParams& p, hipStream_t s);
 int combine_outproj_max_splits();
+
+
+// Measurement: an event pair that the next kernel launch records around its
+// own execution (set with mla_time_next_launch, taken by one launch).
+void take_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through this: with a pending event
+// pair the launch carries it (hipExtLaunchKernel), otherwise a plain launch.
+template <typename K, typename... Args>
+inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  take_launch_events(&e0, &e1);
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
 
 }  // namespace mla

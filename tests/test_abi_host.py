@@ -46,6 +46,13 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
+def test_time_next_launch_host_side(L):
+    # setting (and clearing) the event pair needs no GPU; a pair is only
+    # consumed by a launch, so the test leaves none pending
+    assert L.mla_time_next_launch(None, None) == 0
+    assert mla.mla_time_next_launch(None, None) == 0
+
+
 def test_status_strings(L):
     for code in (0, -1, -2, -3, -4, -5, -6):
         s = mla.status_string(code)

@@ -201,6 +201,36 @@ def test_determinism():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_timed_launch_records_the_kernel_and_changes_nothing():
+    # mla_time_next_launch: the next launch carries the event pair; the
+    # results are the same bits as an untimed launch, and the pair is used
+    # by exactly one launch
+    import mla_latent_kv_28_amd as mla
+    from mla_latent_kv_28_amd.pipeline import DecodePipeline
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=[1000, 517, 64, 2048])
+    pipe = DecodePipeline(inp, num_splits=4)
+    pipe.absorb()
+    pipe.decode()
+    torch.cuda.synchronize()
+    ref_o, ref_l = pipe.o_part.clone(), pipe.lse_part.clone()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    print("case: timed decode launch", flush=True)
+    assert mla.mla_time_next_launch(ev[0], ev[1]) == 0
+    pipe.o_part.zero_()
+    pipe.decode()
+    pipe.decode()                     # untimed: must not touch the events again
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1])
+    print("timed decode %.3f us" % (ms * 1e3), flush=True)
+    assert 0.0 < ms < 100.0
+    assert torch.equal(pipe.o_part, ref_o) and torch.equal(pipe.lse_part, ref_l)
+    with pytest.raises(ValueError):
+        mla.mla_time_next_launch(torch.cuda.Event(enable_timing=True), None)
+
+
 # --- full workload sizes, in the launch configuration the benchmark times ---------
 
 def _sampled(inp, out, lse, pairs, rel, absb=None, fp8_reference="dequantised"):
