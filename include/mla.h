@@ -190,10 +190,16 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
  * ceil(max_seq_len / num_splits) rounded up to a multiple of 32. */
 int32_t mla_split_chunk(int32_t max_seq_len, int32_t num_splits);
 
-/* A split count for mla_decode: chunks of about total_tokens / num_cus tokens
- * (at least 256), so that the non-empty (sequence, split) items spread evenly
- * over `num_cus` compute units. total_tokens <= 0 means batch * max_seq_len.
- * Returns at least 1 and at most the largest count mla_combine accepts. */
+/* A split count for mla_decode, from a cost model of this GPU. The non-empty
+ * (sequence, split) items run one workgroup per compute unit, in rounds of
+ * `num_cus`; each item costs its chunk of tokens plus a fixed start-up and
+ * write-out of about six tiles, and every (sequence, split) pair adds a
+ * partial for the merge to read. The count returned has the smallest total;
+ * the number of items is exact when every sequence has max_seq_len tokens and
+ * estimated from total_tokens (about total / chunk + half an item per
+ * sequence, with a small margin) otherwise. Chunks are at least 256 tokens.
+ * total_tokens <= 0 means batch * max_seq_len. Returns at least 1 and at most
+ * the largest count mla_combine accepts. */
 int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tokens,
                            int32_t num_cus);
 

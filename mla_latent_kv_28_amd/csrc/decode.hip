@@ -852,20 +852,37 @@ __device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char*
   for (int g = 25; g < 32; ++g) mfma(g);
 }
 
-// Loads of one tile of a contiguous 16-bit cache (32 consecutive rows): a
-// scalar tile address plus 32-bit lane offsets. Tiles past the end of the
-// split are clamped to its last tile, and rows past the split's end repeat
-// its last row, so every tile costs every thread the same nine loads.
+// Where the streamed tiles of one split start. A contiguous cache adds the
+// tile's first token to the sequence's first row. A paged cache with pages of
+// at least 32 tokens (so that no tile straddles two pages) looks the page up
+// in `pages`, which holds the split's physical page ids one per lane (lane i:
+// logical page lp0 + i), loaded once per workgroup and read with readlane.
+struct TileBase {
+  const char* base;   // contiguous: the sequence's first row; paged: the pool's
+  int shift, lp0;     // paged: log2(page size), the split's first logical page
+  int pages;          // paged: this lane's physical page id
+};
+
+// Loads of one tile of a 16-bit cache (32 consecutive rows): a scalar tile
+// address plus 32-bit lane offsets. Tiles past the end of the split are
+// clamped to its last tile, and rows past the split's end repeat its last
+// row, so every tile costs every thread the same nine loads.
 template <class C>
 struct StreamTile {
   const char* tile;
   int last, rs;
-  __device__ __forceinline__ StreamTile(const DecodeParams& p, const char* seq_base, int t, int ntiles, int start,
-                                        int end) {
+  template <bool PAGED>
+  __device__ __forceinline__ StreamTile(const DecodeParams& p, const TileBase& tbase, int t, int ntiles, int start,
+                                        int end, std::integral_constant<bool, PAGED>) {
     const int tb = start + min(t, ntiles - 1) * C::T;
     last = min(end - tb, C::T) - 1;
     rs = (int)(p.row_stride * C::ESZ);
-    tile = seq_base + (int64_t)tb * rs;
+    if constexpr (PAGED) {
+      const int64_t pg = __builtin_amdgcn_readlane(tbase.pages, (tb >> tbase.shift) - tbase.lp0);
+      tile = tbase.base + ((pg << tbase.shift) + (tb & ((1 << tbase.shift) - 1))) * rs;
+    } else {
+      tile = tbase.base + (int64_t)tb * rs;
+    }
   }
   // latent row 4k + wave (one 1 KiB row per wave instruction)
   __device__ __forceinline__ void latent(const DmaOffs& dma, MLA_LDS char* fill, int wave, int k) const {
@@ -892,12 +909,12 @@ struct StreamTile {
 // softmax of tile t. Past the end of the split the loads fetch the last tile
 // again (its rows are still in L2 and its slot is not read), which keeps the
 // per-thread load count, and with it the vmcnt wait, the same for every tile.
-template <class C>
+template <class C, bool PAGED>
 __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const MLA_LDS char* __restrict__ cur,
                                                  const MLA_LDS char* __restrict__ prev,
                                                  MLA_LDS char* __restrict__ fill, MLA_LDS char* __restrict__ pw,
                                                  const MLA_LDS char* __restrict__ pr, const QFrag<C>& q,
-                                                 State<C>& s, LaneOffs<C>& lo, DmaOffs& dma, const char* seq_base,
+                                                 State<C>& s, LaneOffs<C>& lo, DmaOffs& dma, const TileBase& tbase,
                                                  int t, int ntiles, int start, int end, bool first) {
   static_assert(!C::F32 && !C::FP8 && C::LAT_CH == 64 && C::WAVES == 4, "16-bit DeepSeek-V2 layout");
   constexpr int LPT = loads_per_tile<C>();
@@ -906,7 +923,7 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
   refresh<C>(lo);
   asm volatile("" : "+v"(dma.lat), "+v"(dma.rope_chunk));
 
-  const StreamTile<C> ld(p, seq_base, t + 2, ntiles, start, end);   // tile t + 2
+  const StreamTile<C> ld(p, tbase, t + 2, ntiles, start, end, std::integral_constant<bool, PAGED>{});   // tile t + 2
   Scores<C> sc;
   sc.lat = f32x16{};
   sc.rope = f32x16{};
@@ -942,7 +959,7 @@ __device__ __forceinline__ int64_t out_row(const DecodeParams& p, int b, int spl
                           : ((int64_t)b * C::H + head);
 }
 
-template <class C, bool PAGED>
+template <class C, bool PAGED, bool PSTREAM>
 __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
@@ -953,12 +970,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   MLA_LDS char* lds = (MLA_LDS char*)smem;
   auto slot = [&](int x) -> MLA_LDS char* { return lds + (x % C::NBUF) * C::BUF_BYTES; };   // x >= 0
 
-  // Contiguous 16-bit caches stage the query through LDS (slots 2..3 and the
+  // 16-bit caches, contiguous or with pages of at least 32 tokens (PSTREAM),
+  // stream whole tiles and stage the query through LDS (slots 2..3 and the
   // P^T buffers); its first half is requested before anything else, since
-  // it depends on nothing but the sequence.
-  constexpr bool STREAM = !PAGED && !C::F32 && !C::FP8;
+  // it depends on nothing but the sequence. A paged split's page ids follow.
+  constexpr bool STREAM = !C::F32 && !C::FP8 && (!PAGED || PSTREAM);
+  static_assert(!PSTREAM || PAGED, "PSTREAM is the paged streaming form");
   MLA_LDS char* qreg = slot(2) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * QStage<C>::BYTES;
   if constexpr (STREAM) stage_q_issue<C>(p, b, 0, qreg);
+  TileBase tbase{(const char*)p.latent, 0, 0, 0};
+  if constexpr (PAGED && STREAM) {
+    tbase.shift = p.page_shift;
+    tbase.lp0 = (split * p.chunk) >> p.page_shift;
+    const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+    tbase.pages = bt[min(tbase.lp0 + (int)(threadIdx.x & 63), p.max_pages - 1)];
+  }
 
   const int L = max(0, min(len_b, p.max_seq_len));
   const int start = split * p.chunk;
@@ -1026,7 +1052,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   }
   const int ntiles = (end - start + C::T - 1) / C::T;
   constexpr int LPT = loads_per_tile<C>();
-  const char* seq_base = (const char*)p.latent + sv.seq_row * (p.row_stride * C::ESZ);
+  if constexpr (!PAGED) tbase.base = (const char*)p.latent + sv.seq_row * (p.row_stride * C::ESZ);
   auto pslot = [&](int x) -> MLA_LDS char* { return pbase + (x & 1) * C::P_BYTES; };
 
   if constexpr (!STREAM) load_q();
@@ -1046,13 +1072,13 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       // query once the first is read
       static_assert(C::NBUF == 4 && 4 * QStage<C>::BYTES <= 2 * C::BUF_BYTES + 2 * C::P_BYTES, "query staging");
       const int wv = __builtin_amdgcn_readfirstlane(wave);
-      StreamTile<C>(p, seq_base, 0, ntiles, start, end).all(dma, slot(0), wv);
+      StreamTile<C>(p, tbase, 0, ntiles, start, end, std::integral_constant<bool, PAGED>{}).all(dma, slot(0), wv);
       if (pass == 0) {
         wait_vmem_le<LPT>();                      // query half 0
         stage_q_read<C>(q, 0, qreg);
         stage_q_issue<C>(p, b, 1, qreg);
       }
-      StreamTile<C>(p, seq_base, 1, ntiles, start, end).all(dma, slot(1), wv);
+      StreamTile<C>(p, tbase, 1, ntiles, start, end, std::integral_constant<bool, PAGED>{}).all(dma, slot(1), wv);
       wait_vmem_le<LPT>();                        // tile 0 (and query half 1)
       if (pass == 0) stage_q_read<C>(q, 1, qreg);
       static_assert(C::P_BYTES == C::THREADS * 32, "two 16-byte zero stores per thread");
@@ -1066,7 +1092,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
 #pragma clang loop unroll(disable)
       for (int t = 0; t < ntiles; ++t) {
         const int tp = max(t - 1, 0), first = pass == 0 && t == 0;
-        tile_step_stream<C>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma, seq_base, t,
+        tile_step_stream<C, PAGED>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma, tbase, t,
                             ntiles, start, end, first != 0);
       }
       latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
@@ -1178,10 +1204,16 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   DecodeParams q = p;
   q.xcd_remap = (grid % 8 == 0 && p.num_splits > 1) ? 1 : 0;
-  if (p.page_shift >= 0)
-    launch_kernel((decode_kernel<C, true>), dim3(grid), dim3(C::THREADS), stream, q);
-  else
-    launch_kernel((decode_kernel<C, false>), dim3(grid), dim3(C::THREADS), stream, q);
+  if (p.page_shift >= 0) {
+    // pages of at least one tile, a split's pages within one wave's lanes
+    const bool stream_pages = p.page_shift >= 5 && ((p.chunk + (1 << p.page_shift) - 1) >> p.page_shift) + 1 <= 64;
+    if constexpr (C::KIND == kBF16) {
+      if (stream_pages) return launch_kernel((decode_kernel<C, true, true>), dim3(grid), dim3(C::THREADS), stream, q);
+    }
+    launch_kernel((decode_kernel<C, true, false>), dim3(grid), dim3(C::THREADS), stream, q);
+  } else {
+    launch_kernel((decode_kernel<C, false, false>), dim3(grid), dim3(C::THREADS), stream, q);
+  }
   return hipGetLastError();
 }
 

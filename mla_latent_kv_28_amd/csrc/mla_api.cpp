@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -52,15 +53,38 @@ int32_t mla_split_chunk(int32_t max_seq_len, int32_t num_splits) {
 
 int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tokens, int32_t num_cus) {
   if (batch <= 0 || max_seq_len <= 0 || num_cus <= 0) return 1;
-  if (total_tokens <= 0) total_tokens = static_cast<int64_t>(batch) * max_seq_len;
-  // Aim for about one (sequence, split) item of equal length per compute unit,
-  // with chunks of at least 256 tokens.
-  int64_t chunk = (total_tokens + num_cus - 1) / num_cus;
-  if (chunk < 256) chunk = 256;
-  int64_t s = (max_seq_len + chunk - 1) / chunk;
-  if (s < 1) s = 1;
-  if (s > mla::combine_max_splits()) s = mla::combine_max_splits();
-  return static_cast<int32_t>(s);
+  const int64_t all_full = static_cast<int64_t>(batch) * max_seq_len;
+  if (total_tokens <= 0 || total_tokens > all_full) total_tokens = all_full;
+  // The (sequence, split) items run one workgroup per compute unit, in rounds
+  // of num_cus; an item costs its chunk of tokens plus a fixed start-up and
+  // write-out of about six tiles (192 tokens of streaming). Every (sequence,
+  // split) pair also writes a partial that the merge reads back, about half a
+  // token's streaming time each on this GPU. Pick the split count with the
+  // smallest total. Items per split count: exact when every sequence is full
+  // length, else total / chunk plus half an item per sequence (the partly
+  // filled last chunk), with 3% + 2 of margin so that an estimate just under
+  // a round boundary does not pick a count whose items spill into one more
+  // round. Chunks are at least 256 tokens.
+  constexpr double kItemOverhead = 192.0, kPartialCost = 0.43;
+  int32_t best_s = 1;
+  double best = 0.0;
+  for (int32_t s = 1; s <= mla::combine_max_splits(); ++s) {
+    const int64_t chunk = mla_split_chunk(max_seq_len, s);
+    if (s > 1 && chunk < 256) break;
+    const int64_t per_seq = (max_seq_len + chunk - 1) / chunk;
+    const double most = static_cast<double>(batch) * per_seq;
+    const double items = total_tokens == all_full
+                             ? most
+                             : std::min(most, 1.03 * (static_cast<double>(total_tokens) / chunk + 0.5 * batch) + 2.0);
+    const double rounds = std::ceil(items / num_cus);
+    const double cost = rounds * (static_cast<double>(chunk) + kItemOverhead) +
+                        kPartialCost * batch * (s > 1 ? s : 0);
+    if (s == 1 || cost < best) {
+      best = cost;
+      best_s = s;
+    }
+  }
+  return best_s;
 }
 
 const char* mla_status_string(mla_status status) {
