@@ -902,6 +902,102 @@ struct StreamTile {
   }
 };
 
+// An e4m3 cache streamed through the 16-bit tile loop. Each tile's codes and
+// per-token scales land in one of two landing buffers; at the end of the
+// step before the tile is scored, every thread widens the code chunks it
+// loaded itself to bf16 times the token's scale (the dequantised value,
+// rounded to bf16) into one of three 16-bit tile slots; the rotary keys, bf16
+// already, go straight to their slot. LDS: slot, landing, slot, slot,
+// landing, P^T buffers, so that the staged query (from the second slot on)
+// avoids the first slot and the first landing buffer, where tile 0 arrives.
+template <class C>
+struct E4m3Ring {
+  static constexpr int SLOT = C::BUF_BYTES;
+  static constexpr int CODES = C::T * C::DC;                // one byte per code
+  static constexpr int SCALES = C::WAVES * 256;             // one 256-byte scale row per wave
+  static constexpr int LAND = CODES + SCALES;
+  static constexpr int S0 = 0, L0 = SLOT, S1 = L0 + LAND, S2 = S1 + SLOT, L1 = S2 + SLOT, P = L1 + LAND;
+  static constexpr int BYTES = P + 2 * C::P_BYTES;
+  static constexpr int LPT = 6;                             // per thread: 4 code chunks, scales, rotary
+  static_assert(!C::F32 && !C::FP8 && C::WAVES == 4 && C::T == 32, "16-bit DeepSeek-V2 slots");
+  static_assert(BYTES <= C::LDS_BYTES, "LDS budget");
+  static_assert(S1 + 4 * QStage<C>::BYTES <= P, "the staged query ends before the P^T buffers");
+  static_assert(CODES == C::THREADS * 4 * 16, "four 16-code chunks per thread");
+};
+
+struct NoE4m3Ring {   // stands in where no e4m3 ring is used
+  static constexpr int S0 = 0, L0 = 0, S1 = 0, S2 = 0, L1 = 0, P = 0, LPT = 0;
+};
+
+// Loads of one e4m3 tile: wave w, lane i loads code chunk i % 32 of rows
+// 8w + 2k + i / 32 (k = 0..3: two whole 512-byte rows per instruction) and,
+// in one more instruction, the scales of rows 8w .. 8w + 7 (lanes 0..7).
+// Every code and scale a thread widens was loaded by its own wave. Rows past
+// the split's end repeat its last row; tiles past the end repeat the last.
+template <class C>
+struct E4m3Tile {
+  const DecodeParams& p;
+  int64_t row0;         // the tile's first cache row
+  int last;
+  __device__ __forceinline__ E4m3Tile(const DecodeParams& p_, int64_t seq_row, int t, int ntiles, int start,
+                                      int end)
+      : p(p_) {
+    const int tb = start + min(t, ntiles - 1) * C::T;
+    last = min(end - tb, C::T) - 1;
+    row0 = seq_row + tb;
+  }
+  // rows r0 = 8w + 2k (lanes 0..31) and r0 + 1 (lanes 32..63), both clamped
+  // to `last`: a scalar row address plus a 32-bit lane offset
+  __device__ __forceinline__ void issue_codes(MLA_LDS char* land, int wave, int k) const {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int r0 = 8 * wave + 2 * k, rs = (int)p.row_stride;
+    const int step = r0 + 1 <= last ? rs : 0;
+    const char* row = (const char*)p.latent + (row0 + min(r0, last)) * p.row_stride;
+    load16_to_lds(row + (uint32_t)((lane >> 5) * step + 16 * (lane & 31)), land + (4 * wave + k) * 1024);
+  }
+  __device__ __forceinline__ void issue_scales(MLA_LDS char* land, int wave) const {
+    const int row = min(8 * wave + (int)(threadIdx.x & 7), last);
+    __builtin_amdgcn_global_load_lds((const char*)(p.scale + row0) + (uint32_t)(4 * row),
+                                     land + E4m3Ring<C>::CODES + wave * 256, 4, 0, 0);
+  }
+  // rotary parts into the slot, as the 16-bit loader places them
+  __device__ __forceinline__ void issue_rope(const DmaOffs& dma, MLA_LDS char* slot, int wave) const {
+    const int row = min((int)(threadIdx.x >> 3), last);
+    const char* r = (const char*)p.rope + row0 * (p.rope_stride * 2);
+    load16_to_lds(r + (uint32_t)(row * (int)(p.rope_stride * 2) + (dma.rope_chunk - C::DC * C::ESZ)),
+                  slot + C::LAT_BYTES + wave * 64 * 16);
+  }
+};
+
+// Widen this thread's code chunks of one landed tile: 16 codes -> 16 bf16
+// values code * scale, two 16-byte chunks of the slot's latent row.
+template <class C>
+__device__ __forceinline__ void e4m3_widen(const MLA_LDS char* __restrict__ land, MLA_LDS char* __restrict__ slot,
+                                           int wave) {
+  // opaque, so that the offsets below are computed here and not kept live
+  // across the whole tile loop
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int t = 8 * wave + 2 * k + (lane >> 5), c = lane & 31;
+    const u32x4 w = *(const MLA_LDS u32x4*)(land + (4 * wave + k) * 1024 + 16 * lane);
+    const float sc = *(const MLA_LDS float*)(land + E4m3Ring<C>::CODES + wave * 256 + 4 * (2 * k + (lane >> 5)));
+    uint32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[d], 1.0f, false);
+      const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[d], 1.0f, true);
+      const float a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+      o[2 * d] = pack_bf16x2(a0 * sc, a1 * sc);
+      o[2 * d + 1] = pack_bf16x2(b0 * sc, b1 * sc);
+    }
+    *(MLA_LDS u32x4*)(slot + lat_off<C>(t, 32 * c)) = u32x4{o[0], o[1], o[2], o[3]};
+    *(MLA_LDS u32x4*)(slot + lat_off<C>(t, 32 * c + 16)) = u32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+
 // Steady state for a contiguous 16-bit cache: one basic block per tile.
 // The nine direct loads of tile t + 2 are spread through the score MFMAs of
 // tile t, so the load issue overlaps the LDS reads and the matrix cores; the
@@ -909,21 +1005,25 @@ struct StreamTile {
 // softmax of tile t. Past the end of the split the loads fetch the last tile
 // again (its rows are still in L2 and its slot is not read), which keeps the
 // per-thread load count, and with it the vmcnt wait, the same for every tile.
-template <class C, bool PAGED>
+template <class C, bool PAGED, bool E4M3>
 __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const MLA_LDS char* __restrict__ cur,
                                                  const MLA_LDS char* __restrict__ prev,
                                                  MLA_LDS char* __restrict__ fill, MLA_LDS char* __restrict__ pw,
                                                  const MLA_LDS char* __restrict__ pr, const QFrag<C>& q,
                                                  State<C>& s, LaneOffs<C>& lo, DmaOffs& dma, const TileBase& tbase,
-                                                 int t, int ntiles, int start, int end, bool first) {
+                                                 int t, int ntiles, int start, int end, bool first,
+                                                 MLA_LDS char* __restrict__ land_fill = nullptr,
+                                                 const MLA_LDS char* __restrict__ land_next = nullptr,
+                                                 MLA_LDS char* __restrict__ next = nullptr, int64_t seq_row = 0) {
   static_assert(!C::F32 && !C::FP8 && C::LAT_CH == 64 && C::WAVES == 4, "16-bit DeepSeek-V2 layout");
-  constexpr int LPT = loads_per_tile<C>();
-  static_assert(LPT == C::T / C::WAVES + 1, "nine loads per tile");
+  constexpr int LPT = E4M3 ? E4m3Ring<C>::LPT : loads_per_tile<C>();
+  static_assert(E4M3 || LPT == C::T / C::WAVES + 1, "nine loads per tile");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   refresh<C>(lo);
   asm volatile("" : "+v"(dma.lat), "+v"(dma.rope_chunk));
 
   const StreamTile<C> ld(p, tbase, t + 2, ntiles, start, end, std::integral_constant<bool, PAGED>{});   // tile t + 2
+  const E4m3Tile<C> ld8(p, seq_row, t + 2, ntiles, start, end);
   Scores<C> sc;
   sc.lat = f32x16{};
   sc.rope = f32x16{};
@@ -938,8 +1038,10 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
   bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
 #pragma unroll
   for (int kc = 0; kc < C::NKC; ++kc) {
-    if (kc % 4 == 0 && kc / 4 < LAT_LOADS) ld.latent(dma, fill, wave, kc / 4);
-    if (kc == 4 * LAT_LOADS) ld.rope(dma, fill, wave);
+    if constexpr (!E4M3) {
+      if (kc % 4 == 0 && kc / 4 < LAT_LOADS) ld.latent(dma, fill, wave, kc / 4);
+      if (kc == 4 * LAT_LOADS) ld.rope(dma, fill, wave);
+    }
     if (kc >= PF + 2 && kc < PF + 6) pvs.read_va(0, kc - (PF + 2));
     if (kc == PF + 6) pvs.read_pb(0);
     const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
@@ -948,8 +1050,17 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
     if (kc >= PV0) pvs.step(kc - PV0);
   }
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (E4M3) {
+    // e4m3: tile t + 2 is requested after the score MFMAs (spread through
+    // them, its address arithmetic made the loop spill)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ld8.issue_codes(land_fill, wave, k);
+    ld8.issue_scales(land_fill, wave);
+    ld8.issue_rope(dma, fill, wave);
+  }
   softmax_pv_stream<C>(pvs, pw, sc, s, end - (start + t * C::T), p.scale_log2, first);
   wait_vmem_le<LPT>();
+  if constexpr (E4M3) e4m3_widen<C>(land_next, next, wave);   // tile t + 1, landed
   tile_barrier();
 }
 
@@ -959,16 +1070,26 @@ __device__ __forceinline__ int64_t out_row(const DecodeParams& p, int b, int spl
                           : ((int64_t)b * C::H + head);
 }
 
-template <class C, bool PAGED, bool PSTREAM>
+template <class C, bool PAGED, bool PSTREAM, bool E4M3 = false>
 __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  static_assert(!E4M3 || (!PAGED && !C::F32 && !C::FP8), "e4m3 tiles stream through the contiguous 16-bit loop");
+  using R8 = typename std::conditional<E4M3, E4m3Ring<C>, NoE4m3Ring>::type;
 
   int w = blockIdx.x;
   if (p.xcd_remap) w = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
   const int b = w / p.num_splits, split = w % p.num_splits;
   const int len_b = p.seq_lens[b];   // a scalar load, requested before the loads into LDS
   MLA_LDS char* lds = (MLA_LDS char*)smem;
-  auto slot = [&](int x) -> MLA_LDS char* { return lds + (x % C::NBUF) * C::BUF_BYTES; };   // x >= 0
+  auto slot = [&](int x) -> MLA_LDS char* {   // x >= 0
+    if constexpr (E4M3) {
+      const int k = x % 3;
+      return lds + (k == 0 ? R8::S0 : k == 1 ? R8::S1 : R8::S2);
+    } else {
+      return lds + (x % C::NBUF) * C::BUF_BYTES;
+    }
+  };
+  auto land = [&](int x) -> MLA_LDS char* { return lds + ((x & 1) ? R8::L1 : R8::L0); };   // e4m3 landing
 
   // 16-bit caches, contiguous or with pages of at least 32 tokens (PSTREAM),
   // stream whole tiles and stage the query through LDS (slots 2..3 and the
@@ -976,7 +1097,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   // it depends on nothing but the sequence. A paged split's page ids follow.
   constexpr bool STREAM = !C::F32 && !C::FP8 && (!PAGED || PSTREAM);
   static_assert(!PSTREAM || PAGED, "PSTREAM is the paged streaming form");
-  MLA_LDS char* qreg = slot(2) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * QStage<C>::BYTES;
+  MLA_LDS char* qreg =
+      (E4M3 ? lds + R8::S1 : slot(2)) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * QStage<C>::BYTES;
   if constexpr (STREAM) stage_q_issue<C>(p, b, 0, qreg);
   TileBase tbase{(const char*)p.latent, 0, 0, 0};
   if constexpr (PAGED && STREAM) {
@@ -992,7 +1114,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
   const int head = wave * 32 + r;
-  MLA_LDS char* pbase = lds + C::NBUF * C::BUF_BYTES;
+  MLA_LDS char* pbase = lds + (E4M3 ? R8::P : C::NBUF * C::BUF_BYTES);
   const bool f32_out = !p.out_bf16;
 
   if (start >= end) {             // uniform over the workgroup: no tokens
@@ -1067,7 +1189,45 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       s.m_ref = fmaxf(s.m_max, __shfl_xor(s.m_max, 32));
       s.overflow = false;
     }
-    if constexpr (STREAM) {
+    if constexpr (STREAM && E4M3) {
+      // prologue: tile 0 lands beside the staged query; tile 1's rotary
+      // part goes to a slot the query occupies, so tile 1 is requested once
+      // every wave has read the query; tile 0 is widened meanwhile
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      auto issue8 = [&](int x) {
+        const E4m3Tile<C> t8(p, sv.seq_row, x, ntiles, start, end);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) t8.issue_codes(land(x), wv, k);
+        t8.issue_scales(land(x), wv);
+        t8.issue_rope(dma, slot(x), wv);
+      };
+      issue8(0);
+      if (pass == 0) {
+        wait_vmem_le<R8::LPT>();                  // query half 0
+        stage_q_read<C>(q, 0, qreg);
+        stage_q_issue<C>(p, b, 1, qreg);
+        wait_vmem_le<0>();                        // tile 0 and query half 1
+        stage_q_read<C>(q, 1, qreg);
+        tile_barrier();                           // every wave is done with the staged query
+      }
+      issue8(1);
+      if (pass != 0) wait_vmem_le<R8::LPT>();    // tile 0
+      e4m3_widen<C>(land(0), slot(0), wv);
+      static_assert(C::P_BYTES == C::THREADS * 32, "two 16-byte zero stores per thread");
+      *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32) = u32x4{};
+      *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32 + 16) = u32x4{};
+      tile_barrier();
+#pragma clang loop unroll(disable)
+      for (int t = 0; t < ntiles; ++t) {
+        const int tp = max(t - 1, 0), first = pass == 0 && t == 0;
+        tile_step_stream<C, false, true>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma,
+                                         tbase, t, ntiles, start, end, first != 0, land(t), land(t + 1),
+                                         slot(t + 1), sv.seq_row);
+      }
+      latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
+      vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
+      __syncthreads();
+    } else if constexpr (STREAM) {
       // prologue: tiles 0 and 1, and (first pass) the second half of the
       // query once the first is read
       static_assert(C::NBUF == 4 && 4 * QStage<C>::BYTES <= 2 * C::BUF_BYTES + 2 * C::P_BYTES, "query staging");
@@ -1092,7 +1252,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
 #pragma clang loop unroll(disable)
       for (int t = 0; t < ntiles; ++t) {
         const int tp = max(t - 1, 0), first = pass == 0 && t == 0;
-        tile_step_stream<C, PAGED>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma, tbase, t,
+        tile_step_stream<C, PAGED, false>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma, tbase, t,
                             ntiles, start, end, first != 0);
       }
       latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
@@ -1212,6 +1372,11 @@ hipError_t launch(const DecodeParams& p, hipStream_t stream) {
     }
     launch_kernel((decode_kernel<C, true, false>), dim3(grid), dim3(C::THREADS), stream, q);
   } else {
+    if constexpr (C::FP8 && C::H == 128 && C::DC == 512 && C::DR == 64) {
+      // contiguous e4m3: widened on the fly into the 16-bit streaming loop
+      using CB = Cfg<C::H, C::DC, C::DR, kBF16>;
+      return launch_kernel((decode_kernel<CB, false, false, true>), dim3(grid), dim3(CB::THREADS), stream, q);
+    }
     launch_kernel((decode_kernel<C, false, false>), dim3(grid), dim3(C::THREADS), stream, q);
   }
   return hipGetLastError();
