@@ -143,6 +143,21 @@ def test_dsv2_paged_other_page_sizes(page_size):
     _check(out, ref, BF16_REL, BF16_ABS)
 
 
+def test_dsv2_paged_split_over_many_pages_equals_contiguous():
+    # a split spanning more pages than one wave has lanes takes the per-row
+    # loader; its bits equal the contiguous streaming loop's
+    lens = [3000, 77]
+    common = dict(seq_lens=lens, pad_fill=float("nan"))
+    cont = make_inputs("dsv2_b32_l4096", **common)
+    paged = make_inputs("dsv2_b32_l4096", layout="paged", page_size=32, **common)
+    _, out_c, lse_c = _run(cont, num_splits=1)
+    _, out_p, lse_p = _run(paged, num_splits=1)
+    assert np.array_equal(out_c, out_p) and np.array_equal(lse_c, lse_p)
+    ref, ref_lse = oracle.decode(**oracle_args(paged))
+    _check(out_p, ref, BF16_REL, BF16_ABS)
+    _lse_check(lse_p, ref_lse, 2e-2)
+
+
 def test_dsv2_peaked_attention():
     # q x 30: logits spread over tens of units, so the reference maximum of the
     # first tile is overtaken and the recompute path runs
@@ -185,6 +200,27 @@ def test_dsv2_fp8_against_both_oracles(splits):
     _check(out, ref_q, BF16_REL, BF16_ABS)
     _lse_check(lse, ref_q_lse, 2e-2)
     _check(out, ref_b, FP8_REL)
+
+
+def test_dsv2_fp8_ragged_nan_padding():
+    # rows no sequence owns hold NaN codes and scales; tiles past a split's
+    # end repeat its last row, so none of them reaches the result
+    inp = make_inputs("fp8_b128_l8192", seq_lens=[1000, 33, 0, 65, 255], pad_fill=float("nan"))
+    _, out, lse = _run(inp, num_splits=3)
+    ref, ref_lse = oracle.decode(**oracle_args(inp, "dequantised"))
+    _check(out, ref, BF16_REL, BF16_ABS)
+    _lse_check(lse, ref_lse, 2e-2)
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_dsv2_fp8_paged(page_size):
+    # paged e4m3 runs the per-row loader (codes staged in registers)
+    inp = make_inputs("fp8_b128_l8192", seq_lens=[600, 97, 130], layout="paged", page_size=page_size,
+                      pad_fill=float("nan"))
+    _, out, lse = _run(inp, num_splits=2)
+    ref, ref_lse = oracle.decode(**oracle_args(inp, "dequantised"))
+    _check(out, ref, BF16_REL, BF16_ABS)
+    _lse_check(lse, ref_lse, 2e-2)
 
 
 def test_bf16_final_output_dtype():
