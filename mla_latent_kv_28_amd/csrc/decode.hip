@@ -752,9 +752,10 @@ struct PvSched {
   }
 };
 
-// Latent-sum MFMAs of tile t - 1 issued in the score phase of tile t, which
-// is bound by LDS reads and leaves the matrix cores room; the rest run in
-// phase two.
+// Latent-sum MFMAs of tile t - 1 that may be issued in the tail of the score
+// phase of tile t (bound by LDS reads, so the matrix cores have room); the
+// rest run in phase two. Measured on MI355X, moving some of them early was no
+// faster than none, so none are.
 constexpr int kPvEarly = 0;
 
 // Phase two of the streaming step: the softmax of tile t on the vector unit,
