@@ -193,7 +193,7 @@ def main():
         (split merge and out-projection, one fused call where the pipeline uses
         it), in n whole steps launched eagerly on the bench stream: each timed
         launch carries its HIP event pair (mla_time_next_launch, i.e.
-        hipExtLaunchKernel). A spin kernel of about 10 ms goes first, so that
+        hipExtLaunchKernel). A spin kernel of about 20 ms goes first, so that
         all n steps are queued before the GPU reaches them and run back to
         back. The events' own packets add a few microseconds per interval (the
         start timestamp is taken as the previous kernel ends), so the figure
@@ -207,7 +207,7 @@ def main():
         with torch.cuda.stream(stream):
             for i in range(2 * nbuf):
                 step(i)
-            torch.cuda._sleep(int(2e7))
+            torch.cuda._sleep(int(4e7))
             for i in range(n):
                 pipe.cache = caches[i % nbuf]
                 pipe.absorb()
@@ -222,13 +222,14 @@ def main():
                     mla.mla_time_next_launch(None, ev[i][3])
                     pipe.out_proj()
         torch.cuda.synchronize()
-        dec = sum(e[0].elapsed_time(e[1]) for e in ev) / n
+        decs = sorted(e[0].elapsed_time(e[1]) for e in ev)
         rest = sum(e[2].elapsed_time(e[3]) for e in ev) / n
-        return dec, rest
+        pct = {q: decs[min(n - 1, int(round(q / 100.0 * (n - 1))))] for q in (10, 50, 90)}
+        return sum(decs) / n, rest, pct
 
     torch.cuda.synchronize()
     ms_step, nsteps = timed("step", step, args.steps, args.warmup)
-    ms_dec, ms_rest = in_step_kernel_times(max(args.steps, 10))
+    ms_dec, ms_rest, dec_pct = in_step_kernel_times(max(args.steps, 100))
 
     q_step = B / (ms_step * 1e-3)
     gbps_step = cache_bytes / (ms_step * 1e-3) / 1e9
@@ -267,6 +268,7 @@ def main():
             "frac": round(gbps_dec / HBM_PEAK_GBPS, 4),
             "traffic": hbm_traffic(inp.name) if S == 8 else None,
             "us_per_launch": round(ms_dec * 1e3, 3),
+            "us_per_launch_p10_p50_p90": [round(dec_pct[q] * 1e3, 3) for q in (10, 50, 90)],
             "timing": "event pair carried by each decode launch (hipExtLaunchKernel) within whole steps",
             "algorithmic_bytes_per_launch": cache_bytes,
             "mfma_tflops": round(flops_dec / (ms_dec * 1e-3) / 1e12, 1),
