@@ -319,28 +319,29 @@ __global__ __launch_bounds__(256, 2) void outproj_bf16_kernel(GemmParams p) {
 
 // ---- split merge + out-proj in one pass: W [N=128][K=512] per head, bf16
 // partials, at most kCoMaxSplits splits. One 512-thread workgroup per (head,
-// block of 16 batch rows), so every partial row is read once and the merge
-// work spreads over twice as many compute units as heads:
-//   1. all loads are requested at once: the partial LSEs, the first eight
-//      splits' partial rows (wave w takes rows w and w + 8, each wave
-//      instruction one split's whole 1 KiB row through a buffer descriptor
-//      with the row and split in the scalar offset) and the head's W_UV rows
-//      (wave w takes rows 16w .. 16w + 15, one 1 KiB row per instruction);
+// block of batch rows): 16 rows up to batch 32, else about half the batch
+// rounded up to 32-row passes, so that there are about 256 workgroups, every
+// partial row is read once and the head's W_UV once per block. Per pass:
+//   1. the loads are requested at once: the partial LSEs, the first splits'
+//      partial rows (wave w takes rows w + 8j, each wave instruction one
+//      split's whole 1 KiB row through a buffer descriptor with the row and
+//      split in the scalar offset) and, in the first pass, the head's W_UV
+//      rows (wave w takes rows 16w .. 16w + 15, one 1 KiB row per instruction);
 //   2. merge weights e^(lse_s - max) per (row, split) stay in the lanes that
 //      computed them (lane 16j + s of wave w: row w + 8j, split s) and are
 //      read with readlane;
 //   3. the merge: fp32 sums, times 1/z, rounded to bf16 (the values a bf16
-//      mla_combine output would hold) and stored to LDS, as are the W_UV rows;
-//   4. wave w multiplies the merged rows by columns 32(w % 4) .. + 31 of
-//      W_UV over k half w / 4 (a 32-row MFMA whose rows 16..31 are not
-//      stored), both operands read from LDS; the two k halves are added
-//      through LDS.
+//      mla_combine output would hold) and stored to LDS, as are the W_UV rows
+//      in the first pass;
+//   4. wave w multiplies the pass's rows by columns 32(w % 4) .. + 31 of
+//      W_UV over k half w / 4 (a 32-row MFMA; in a 16-row pass rows 16..31
+//      are not stored), both operands read from LDS; the two k halves are
+//      added through LDS.
 // LDS rows of 1 KiB (W_UV rows and merged rows) have their 16-byte chunks
 // XOR-swizzled by the row, so 16 consecutive rows read at one chunk hit 16
 // different bank groups.
-constexpr int kCoK = 512, kCoN = 128, kCoWaves = 8, kCoMaxSplits = 64, kCoSC = 8, kCoRows = 16;
-static_assert(kCoMaxSplits % kCoSC == 0 && kCoMaxSplits % 16 == 0 && 16 % kCoSC == 0, "split chunks");
-static_assert(kCoRows == 2 * kCoWaves, "two merged rows per wave");
+constexpr int kCoK = 512, kCoN = 128, kCoWaves = 8, kCoMaxSplits = 64;
+static_assert(kCoMaxSplits % 16 == 0, "split chunks");
 constexpr int kCoRow = kCoK * 2;                          // bytes of one bf16 row
 constexpr int kCoLds = kCoN * kCoRow + 32 * kCoRow;      // W_UV rows + 32 MFMA rows: 160 KiB
 
@@ -365,24 +366,29 @@ __device__ __forceinline__ float row16_reduce(float v, Op op) {
   return op(v, dpp_move<0x140>(v));   // row_mirror
 }
 
-template <bool OUT_F32>
+// RPW merged rows per wave and pass: 2 (16-row passes) or 4 (32-row passes).
+template <bool OUT_F32, int RPW>
 __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(CombineOutParams p) {
+  static_assert(RPW == 2 || RPW == 4, "16- or 32-row passes");
+  constexpr int PR = kCoWaves * RPW;                      // rows per pass
+  constexpr int SC = 16 / RPW;                            // splits in flight per row
+  static_assert(kCoMaxSplits % SC == 0 && 16 % SC == 0, "split chunks");
   __shared__ __attribute__((aligned(16))) char smem[kCoLds];
   MLA_LDS char* wl = (MLA_LDS char*)smem;                 // W_UV rows of the head
   MLA_LDS char* ol = wl + kCoN * kCoRow;                  // merged rows; then the k-half sums
-  const int h = blockIdx.x, b0 = blockIdx.y * kCoRows, rows = min(kCoRows, p.batch - b0);
+  const int h = blockIdx.x, b_first = blockIdx.y * p.rows_per_block;
+  const int b_end = min(b_first + p.rows_per_block, p.batch);
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, r = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = p.splits, H = p.heads;
   const int split_stride = H * kCoRow;                    // bytes between two splits of one (b, h)
   const int row_stride = S * split_stride;                // bytes between two batch rows
   const int j16 = lane >> 4, s16 = lane & 15;             // weight lanes: row wave + 8 j16, split s16 + 16k
-  const int lrow = wave + 8 * (j16 & 1);                  // lanes 32..63 repeat rows of lanes 0..31
+  const int lrow = wave + 8 * (RPW == 2 ? (j16 & 1) : j16);   // (16-row passes: lanes 32..63 repeat)
 
-  // 1. partial LSEs (splits past S read split S - 1 and are masked after
-  //    the load, so no branch surrounds it)
-  float l[kCoMaxSplits / 16];
-  {
+  // partial LSEs of a pass (splits past S read split S - 1 and are masked
+  // after the load, so no branch surrounds it)
+  auto issue_lse = [&](float (&l)[kCoMaxSplits / 16], int b0, int rows) {
     const float* lse_row = p.lse_part + (int64_t)(b0 + min(lrow, rows - 1)) * S * H + h;
 #pragma unroll
     for (int k = 0; k < kCoMaxSplits / 16; ++k) {
@@ -390,23 +396,29 @@ __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(Combi
       const float v = lse_row[(int64_t)min(sp, S - 1) * H];
       l[k] = sp < S ? v : -INFINITY;
     }
-  }
-  // partial rows of the block: byte offset row * row_stride + split *
-  // split_stride from the head's first row (below 2^31 for 16 rows of at
+  };
+  // partial rows of a pass: byte offset row * row_stride + split *
+  // split_stride from the head's first row (below 2^31 for 32 rows of at
   // most 64 splits of 128 heads)
-  const __amdgpu_buffer_rsrc_t part_rs =
-      buffer_rsrc((const char*)p.o_part + ((int64_t)b0 * S * H + h) * kCoRow, rows * row_stride - h * kCoRow);
-  u32x4 x[kCoSC][2];
-  auto issue = [&](int s0) {
+  auto part_rsrc = [&](int b0, int rows) {
+    return buffer_rsrc((const char*)p.o_part + ((int64_t)b0 * S * H + h) * kCoRow, rows * row_stride - h * kCoRow);
+  };
+  auto issue = [&](u32x4 (&x)[SC][RPW], const __amdgpu_buffer_rsrc_t& rs, int rows, int s0) {
 #pragma unroll
-    for (int i = 0; i < kCoSC; ++i)
+    for (int i = 0; i < SC; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < RPW; ++j) {
         const int rr = min(wave + 8 * j, rows - 1), sp = min(s0 + i, S - 1);
-        x[i][j] = __builtin_amdgcn_raw_buffer_load_b128(part_rs, lane * 16, rr * row_stride + sp * split_stride, 0);
+        x[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, rr * row_stride + sp * split_stride, 0);
       }
   };
-  issue(0);
+
+  // 1. the first pass's loads, then the head's W_UV rows (coalesced 1 KiB rows
+  //    into registers, requested last: needed last)
+  float l[kCoMaxSplits / 16];
+  u32x4 x[SC][RPW];
+  issue_lse(l, b_first, min(PR, b_end - b_first));
+  issue(x, part_rsrc(b_first, min(PR, b_end - b_first)), min(PR, b_end - b_first), 0);
   u32x4 wrow[kCoN / kCoWaves];
   {
     const char* wh = (const char*)p.w + ((int64_t)h * kCoN + wave * (kCoN / kCoWaves)) * kCoRow + lane * 16;
@@ -414,111 +426,126 @@ __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(Combi
     for (int k = 0; k < kCoN / kCoWaves; ++k) wrow[k] = load16(wh + k * kCoRow);
   }
 
-  // 2. merge weights of (row lrow, splits s16 + 16k)
-  float wk[kCoMaxSplits / 16], inv;
-  {
-    float m = -INFINITY;
+  // one pass over rows b0 .. b0 + rows - 1 whose LSEs and first splits are in l, x
+  auto pass_body = [&](auto first_pass, int b0, int rows) {
+    constexpr bool FIRST = decltype(first_pass)::value;
+    const __amdgpu_buffer_rsrc_t part_rs = part_rsrc(b0, rows);
+    // 2. merge weights of (row lrow, splits s16 + 16k)
+    float wk[kCoMaxSplits / 16], inv;
+    {
+      float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kCoMaxSplits / 16; ++k) m = fmaxf(m, l[k]);
-    m = row16_reduce(m, [](float u, float v) { return fmaxf(u, v); });
-    const bool empty = (m == -INFINITY);
-    float z = 0.0f;
+      for (int k = 0; k < kCoMaxSplits / 16; ++k) m = fmaxf(m, l[k]);
+      m = row16_reduce(m, [](float u, float v) { return fmaxf(u, v); });
+      const bool empty = (m == -INFINITY);
+      float z = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kCoMaxSplits / 16; ++k) {
-      wk[k] = (empty || l[k] == -INFINITY) ? 0.0f : fast_exp2((l[k] - m) * kLog2e);
-      z += wk[k];
+      for (int k = 0; k < kCoMaxSplits / 16; ++k) {
+        wk[k] = (empty || l[k] == -INFINITY) ? 0.0f : fast_exp2((l[k] - m) * kLog2e);
+        z += wk[k];
+      }
+      z = row16_reduce(z, [](float u, float v) { return u + v; });
+      inv = empty ? 0.0f : 1.0f / z;
+      if (s16 == 0 && j16 < RPW && lrow < rows && p.lse != nullptr)
+        p.lse[(int64_t)(b0 + lrow) * H + h] = empty ? -INFINITY : m + fast_log2(z) * kLn2;
     }
-    z = row16_reduce(z, [](float u, float v) { return u + v; });
-    inv = empty ? 0.0f : 1.0f / z;
-    if (s16 == 0 && j16 < 2 && lrow < rows && p.lse != nullptr)
-      p.lse[(int64_t)(b0 + lrow) * H + h] = empty ? -INFINITY : m + fast_log2(z) * kLn2;
-  }
 
-  // 3. merge: wave w, rows w + 8j; lane = 16-byte chunk of the row
-  float acc[2][8];
+    // 3. merge: wave w, rows w + 8j; lane = 16-byte chunk of the row
+    float acc[RPW][8];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < RPW; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
-  auto merge = [&](int s0) {
-    // splits s0 .. s0 + kCoSC - 1 share one weight register: s0 / 16
-    const int kk = s0 >> 4, lo = s0 & 15;
-    const float wsel = kk == 0 ? wk[0] : kk == 1 ? wk[1] : kk == 2 ? wk[2] : wk[3];
+      for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+    auto merge = [&](int s0) {
+      // splits s0 .. s0 + SC - 1 share one weight register: s0 / 16
+      const int kk = s0 >> 4, lo = s0 & 15;
+      const float wsel = kk == 0 ? wk[0] : kk == 1 ? wk[1] : kk == 2 ? wk[2] : wk[3];
 #pragma unroll
-    for (int i = 0; i < kCoSC; ++i)
+      for (int i = 0; i < SC; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // a split with weight 0 (empty, or past S) has its words zeroed,
-        // so whatever it holds cannot reach the sum: the byte selectors and
-        // the mask are wave-uniform
-        const float w = lane_value(wsel, 16 * j + lo + i);
-        const bool skip = (w == 0.0f);
-        const uint32_t sel_lo = skip ? 0x0c0c0c0cu : 0x01000c0cu;   // (v & 0xffff) << 16, or 0
-        const uint32_t mask_hi = skip ? 0u : 0xffff0000u;
+        for (int j = 0; j < RPW; ++j) {
+          // a split with weight 0 (empty, or past S) has its words zeroed,
+          // so whatever it holds cannot reach the sum: the byte selectors and
+          // the mask are wave-uniform
+          const float w = lane_value(wsel, 16 * j + lo + i);
+          const bool skip = (w == 0.0f);
+          const uint32_t sel_lo = skip ? 0x0c0c0c0cu : 0x01000c0cu;   // (v & 0xffff) << 16, or 0
+          const uint32_t mask_hi = skip ? 0u : 0xffff0000u;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t v = x[i][j][d];
-          acc[j][2 * d] = fmaf(w, __builtin_bit_cast(float, __builtin_amdgcn_perm(v, v, sel_lo)), acc[j][2 * d]);
-          acc[j][2 * d + 1] = fmaf(w, __builtin_bit_cast(float, v & mask_hi), acc[j][2 * d + 1]);
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t v = x[i][j][d];
+            acc[j][2 * d] = fmaf(w, __builtin_bit_cast(float, __builtin_amdgcn_perm(v, v, sel_lo)), acc[j][2 * d]);
+            acc[j][2 * d + 1] = fmaf(w, __builtin_bit_cast(float, v & mask_hi), acc[j][2 * d + 1]);
+          }
+        }
+    };
+    merge(0);
+    for (int s0 = SC; s0 < S; s0 += SC) {
+      issue(x, part_rs, rows, s0);
+      merge(s0);
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int row = wave + 8 * j;
+      const float iv = lane_value(inv, 16 * j);
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[j][2 * d] * iv, acc[j][2 * d + 1] * iv);
+      *(MLA_LDS u32x4*)(ol + co_chunk(row, lane)) = o;
+    }
+    if constexpr (FIRST) {
+#pragma unroll
+      for (int k = 0; k < kCoN / kCoWaves; ++k) {
+        const int n = wave * (kCoN / kCoWaves) + k;
+        *(MLA_LDS u32x4*)(wl + co_chunk(n, lane)) = wrow[k];
+      }
+    }
+    __syncthreads();
+
+    // 4. products: columns 32f .. 32f + 31 over k blocks 16kq .. 16kq + 15
+    const int f = wave & 3, kq = wave >> 2, n = 32 * f + r;
+    f32x16 c = f32x16{};
+#pragma unroll
+    for (int q = 0; q < kCoK / 32; ++q) {
+      const int chunk = 2 * (16 * kq + q) + hh;
+      const bf16x8 a = *(const MLA_LDS bf16x8*)(ol + co_chunk(r, chunk));
+      const bf16x8 bw = *(const MLA_LDS bf16x8*)(wl + co_chunk(n, chunk));
+      c = mfma32x32x16(a, bw, c);
+    }
+    __syncthreads();
+    constexpr int G = PR / 8;                                // accumulator groups holding pass rows
+    MLA_LDS f32x4* red = (MLA_LDS f32x4*)ol;                // [f][g][lane]
+    if (kq == 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) red[(f * G + g) * 64 + lane] = f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+    }
+    __syncthreads();
+    if (kq == 0) {
+      // accumulator 4g + i of lane (hh, r) is row 8g + 4hh + i, column 32f + r
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const f32x4 o = red[(f * G + g) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 8 * g + 4 * hh + i;
+          const float v = c[4 * g + i] + o[i];
+          if (row < rows) {
+            const int64_t off = ((int64_t)(b0 + row) * H + h) * kCoN + n;
+            if constexpr (OUT_F32) ((float*)p.out)[off] = v;
+            else ((__bf16*)p.out)[off] = (__bf16)v;
+          }
         }
       }
+    }
+    __syncthreads();   // the merged-row area is refilled by the next pass
   };
-  merge(0);
-  for (int s0 = kCoSC; s0 < S; s0 += kCoSC) {
-    issue(s0);
-    merge(s0);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = wave + 8 * j;
-    const float iv = lane_value(inv, 16 * j);
-    u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] = pack_bf16x2(acc[j][2 * d] * iv, acc[j][2 * d + 1] * iv);
-    *(MLA_LDS u32x4*)(ol + co_chunk(row, lane)) = o;
-  }
-#pragma unroll
-  for (int k = 0; k < kCoN / kCoWaves; ++k) {
-    const int n = wave * (kCoN / kCoWaves) + k;
-    *(MLA_LDS u32x4*)(wl + co_chunk(n, lane)) = wrow[k];
-  }
-  __syncthreads();
 
-  // 4. products: columns 32f .. 32f + 31 over k blocks 16kq .. 16kq + 15
-  //    (rows 16..31 of the A operand are never written; their results are
-  //    dropped)
-  const int f = wave & 3, kq = wave >> 2, n = 32 * f + r;
-  f32x16 c = f32x16{};
-#pragma unroll
-  for (int q = 0; q < kCoK / 32; ++q) {
-    const int chunk = 2 * (16 * kq + q) + hh;
-    const bf16x8 a = *(const MLA_LDS bf16x8*)(ol + co_chunk(r, chunk));
-    const bf16x8 bw = *(const MLA_LDS bf16x8*)(wl + co_chunk(n, chunk));
-    c = mfma32x32x16(a, bw, c);
-  }
-  __syncthreads();
-  MLA_LDS f32x4* red = (MLA_LDS f32x4*)ol;                // [f][g][lane]: 8 KiB
-  if (kq == 1) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) red[(f * 2 + g) * 64 + lane] = f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
-  }
-  __syncthreads();
-  if (kq == 0) {
-    // accumulator 4g + i of lane (hh, r) is row 8g + 4hh + i, column 32f + r
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const f32x4 o = red[(f * 2 + g) * 64 + lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 8 * g + 4 * hh + i;
-        const float v = c[4 * g + i] + o[i];
-        if (row < rows) {
-          const int64_t off = ((int64_t)(b0 + row) * H + h) * kCoN + n;
-          if constexpr (OUT_F32) ((float*)p.out)[off] = v;
-          else ((__bf16*)p.out)[off] = (__bf16)v;
-        }
-      }
-    }
+  pass_body(std::true_type{}, b_first, min(PR, b_end - b_first));
+  for (int b0 = b_first + PR; b0 < b_end; b0 += PR) {
+    const int rows = min(PR, b_end - b0);
+    issue_lse(l, b0, rows);
+    issue(x, part_rsrc(b0, rows), rows, 0);
+    pass_body(std::false_type{}, b0, rows);
   }
 }
 
@@ -557,11 +584,18 @@ int combine_outproj_max_splits() { return kCoMaxSplits; }
 hipError_t launch_combine_outproj_dsv2_bf16(const CombineOutParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   if (p.splits > kCoMaxSplits) return hipErrorInvalidValue;
-  const dim3 grid(p.heads, (p.batch + kCoRows - 1) / kCoRows), block(64 * kCoWaves);
-  if (p.out_f32)
-    launch_kernel(combine_outproj_kernel<true>, grid, block, s, p);
-  else
-    launch_kernel(combine_outproj_kernel<false>, grid, block, s, p);
+  // rows per workgroup: 16 up to batch 32; else half the batch rounded up to
+  // whole 32-row passes (about 256 workgroups, W_UV read once per block)
+  CombineOutParams q = p;
+  q.rows_per_block = p.batch <= 32 ? 16 : (((p.batch + 1) / 2 + 31) / 32) * 32;
+  const dim3 grid(p.heads, (p.batch + q.rows_per_block - 1) / q.rows_per_block), block(64 * kCoWaves);
+  if (q.rows_per_block == 16) {
+    if (p.out_f32) launch_kernel(combine_outproj_kernel<true, 2>, grid, block, s, q);
+    else launch_kernel(combine_outproj_kernel<false, 2>, grid, block, s, q);
+  } else {
+    if (p.out_f32) launch_kernel(combine_outproj_kernel<true, 4>, grid, block, s, q);
+    else launch_kernel(combine_outproj_kernel<false, 4>, grid, block, s, q);
+  }
   return hipGetLastError();
 }
 

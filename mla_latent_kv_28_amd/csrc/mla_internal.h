@@ -75,6 +75,7 @@ struct CombineOutParams {
   float* lse;            // [B, H] or null
   int32_t batch, splits, heads;
   int32_t out_f32;
+  int32_t rows_per_block;  // set by the launcher
 };
 hipError_t launch_combine_outproj_dsv2_bf16(const CombineOutParams& p, hipStream_t s);
 int combine_outproj_max_splits();

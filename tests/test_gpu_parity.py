@@ -350,13 +350,13 @@ def test_combine_against_oracle_merge(splits, part_dtype):
 
 
 @pytest.mark.parametrize("splits,out_dtype", [(2, 0), (3, 0), (8, 0), (8, 1), (13, 0), (64, 0)])
-def test_combine_out_proj_against_oracle_and_separate_calls(splits, out_dtype):
+def test_combine_out_proj_against_oracle_and_separate_calls(splits, out_dtype, B=33):
     # merge + out-proj in one call: the oracle's LSE merge followed by the
     # W_UV product, and the same result as mla_combine (bf16 latent output)
     # followed by mla_out_proj; 33 rows cover a second, ragged batch block
     import mla_latent_kv_28_amd as mla
     from mla_synth import DSV2
-    B, H, D, V = 33, DSV2.num_heads, DSV2.d_latent, DSV2.d_v
+    H, D, V = DSV2.num_heads, DSV2.d_latent, DSV2.d_v
     rng = np.random.default_rng(23 + splits)
     o = rng.standard_normal((B, splits, H, D)).astype(np.float32)
     lse = (rng.standard_normal((B, splits, H)) * 3.0).astype(np.float32)
@@ -370,7 +370,7 @@ def test_combine_out_proj_against_oracle_and_separate_calls(splits, out_dtype):
     odt = torch.float32 if out_dtype == mla.F32 else torch.bfloat16
     out = torch.empty((B, H, V), dtype=odt, device="cuda")
     lse_out = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    print("case: combine_out_proj S=%d out_dtype=%d" % (splits, out_dtype), flush=True)
+    print("case: combine_out_proj B=%d S=%d out_dtype=%d" % (B, splits, out_dtype), flush=True)
     mla.mla_combine_out_proj(DSV2, B, splits, o_dev, mla.BF16, lse_dev, w_dev, mla.BF16, out, out_dtype,
                              lse_out)
     o_lat = torch.empty((B, H, D), dtype=torch.bfloat16, device="cuda")
@@ -395,3 +395,11 @@ def test_combine_out_proj_against_oracle_and_separate_calls(splits, out_dtype):
     sep = out_sep.double().cpu().numpy()
     scale = np.abs(ref).max()
     assert np.abs(got - sep).max() <= 4e-3 * scale
+
+
+@pytest.mark.parametrize("B,splits", [(16, 8), (100, 13), (130, 3)])
+def test_combine_out_proj_batch_blocks(B, splits):
+    # 16-row passes up to batch 32, then blocks of about half the batch in
+    # 32-row passes (several passes per workgroup, a ragged last block)
+    import mla_latent_kv_28_amd as mla
+    test_combine_out_proj_against_oracle_and_separate_calls(splits, mla.BF16, B=B)
