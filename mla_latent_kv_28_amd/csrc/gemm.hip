@@ -383,8 +383,16 @@ __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(Combi
   const int S = p.splits, H = p.heads;
   const int split_stride = H * kCoRow;                    // bytes between two splits of one (b, h)
   const int row_stride = S * split_stride;                // bytes between two batch rows
+  // A block of at most 4 rows with more splits than one chunk runs split-
+  // parallel: slot (wave w, j) takes row (w + 8j) & 3 and split group
+  // (w + 8j) >> 2, i.e. every fourth chunk of SC splits; the four groups'
+  // fp32 sums of a row are added through LDS before the rounding.
+  const bool spm = RPW == 2 && b_end - b_first <= 4 && S > SC;
+  auto real_row = [&](int vrow) { return spm ? (vrow & 3) : vrow; };
+  auto group = [&](int vrow) { return spm ? (vrow >> 2) : 0; };
+  const int chunk_step = spm ? 4 * SC : SC;               // splits between a slot's chunks
   const int j16 = lane >> 4, s16 = lane & 15;             // weight lanes: row wave + 8 j16, split s16 + 16k
-  const int lrow = wave + 8 * (RPW == 2 ? (j16 & 1) : j16);   // (16-row passes: lanes 32..63 repeat)
+  const int lrow = real_row(wave + 8 * (RPW == 2 ? (j16 & 1) : j16));   // (16-row passes: lanes 32..63 repeat)
 
   // partial LSEs of a pass (splits past S read split S - 1 and are masked
   // after the load, so no branch surrounds it)
@@ -408,7 +416,8 @@ __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(Combi
     for (int i = 0; i < SC; ++i)
 #pragma unroll
       for (int j = 0; j < RPW; ++j) {
-        const int rr = min(wave + 8 * j, rows - 1), sp = min(s0 + i, S - 1);
+        const int vrow = wave + 8 * j;
+        const int rr = min(real_row(vrow), rows - 1), sp = min(s0 + group(vrow) * SC + i, S - 1);
         x[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, rr * row_stride + sp * split_stride, 0);
       }
   };
@@ -446,7 +455,7 @@ __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(Combi
       }
       z = row16_reduce(z, [](float u, float v) { return u + v; });
       inv = empty ? 0.0f : 1.0f / z;
-      if (s16 == 0 && j16 < RPW && lrow < rows && p.lse != nullptr)
+      if (s16 == 0 && j16 < RPW && wave + 8 * j16 < rows && p.lse != nullptr)   // each real row once
         p.lse[(int64_t)(b0 + lrow) * H + h] = empty ? -INFINITY : m + fast_log2(z) * kLn2;
     }
 
@@ -457,17 +466,17 @@ __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(Combi
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
     auto merge = [&](int s0) {
-      // splits s0 .. s0 + SC - 1 share one weight register: s0 / 16
-      const int kk = s0 >> 4, lo = s0 & 15;
-      const float wsel = kk == 0 ? wk[0] : kk == 1 ? wk[1] : kk == 2 ? wk[2] : wk[3];
 #pragma unroll
-      for (int i = 0; i < SC; ++i)
+      for (int j = 0; j < RPW; ++j) {
+        // splits c0 .. c0 + SC - 1 of this slot share one weight register, c0 / 16
+        const int c0 = s0 + group(wave + 8 * j) * SC, kk = c0 >> 4, lo = c0 & 15;
+        const float wsel = kk == 0 ? wk[0] : kk == 1 ? wk[1] : kk == 2 ? wk[2] : wk[3];
 #pragma unroll
-        for (int j = 0; j < RPW; ++j) {
+        for (int i = 0; i < SC; ++i) {
           // a split with weight 0 (empty, or past S) has its words zeroed,
           // so whatever it holds cannot reach the sum: the byte selectors and
           // the mask are wave-uniform
-          const float w = lane_value(wsel, 16 * j + lo + i);
+          const float w = c0 + i < S ? lane_value(wsel, 16 * j + lo + i) : 0.0f;
           const bool skip = (w == 0.0f);
           const uint32_t sel_lo = skip ? 0x0c0c0c0cu : 0x01000c0cu;   // (v & 0xffff) << 16, or 0
           const uint32_t mask_hi = skip ? 0u : 0xffff0000u;
@@ -478,11 +487,32 @@ __global__ __launch_bounds__(64 * kCoWaves, 1) void combine_outproj_kernel(Combi
             acc[j][2 * d + 1] = fmaf(w, __builtin_bit_cast(float, v & mask_hi), acc[j][2 * d + 1]);
           }
         }
+      }
     };
     merge(0);
-    for (int s0 = SC; s0 < S; s0 += SC) {
+    for (int s0 = chunk_step; s0 < S; s0 += chunk_step) {
       issue(x, part_rs, rows, s0);
       merge(s0);
+    }
+    if (FIRST && spm) {   // (a block of at most 4 rows has one pass)
+      // add the four split groups of each row (slot sums through the W_UV
+      // area, still free): rows 0..3 end up in slot 0 of waves 0..3
+      MLA_LDS f32x4* sum = (MLA_LDS f32x4*)wl;               // [vrow][lane][2]
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        sum[((wave + 8 * j) * 64 + lane) * 2] = f32x4{acc[j][0], acc[j][1], acc[j][2], acc[j][3]};
+        sum[((wave + 8 * j) * 64 + lane) * 2 + 1] = f32x4{acc[j][4], acc[j][5], acc[j][6], acc[j][7]};
+      }
+      __syncthreads();
+      if (wave < 4) {
+#pragma unroll
+        for (int g = 1; g < 4; ++g) {
+          const f32x4 u0 = sum[((wave + 4 * g) * 64 + lane) * 2], u1 = sum[((wave + 4 * g) * 64 + lane) * 2 + 1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { acc[0][e] += u0[e]; acc[0][4 + e] += u1[e]; }
+        }
+      }
+      __syncthreads();
     }
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {

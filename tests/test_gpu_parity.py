@@ -397,9 +397,11 @@ def test_combine_out_proj_against_oracle_and_separate_calls(splits, out_dtype, B
     assert np.abs(got - sep).max() <= 4e-3 * scale
 
 
-@pytest.mark.parametrize("B,splits", [(16, 8), (100, 13), (130, 3)])
+@pytest.mark.parametrize("B,splits", [(16, 8), (100, 13), (130, 3), (4, 64), (3, 40), (18, 20)])
 def test_combine_out_proj_batch_blocks(B, splits):
     # 16-row passes up to batch 32, then blocks of about half the batch in
-    # 32-row passes (several passes per workgroup, a ragged last block)
+    # 32-row passes (several passes per workgroup, a ragged last block);
+    # blocks of at most 4 rows merge their splits in four parallel groups
+    # (batch 4 and 3, and the 2-row second block of batch 18)
     import mla_latent_kv_28_amd as mla
     test_combine_out_proj_against_oracle_and_separate_calls(splits, mla.BF16, B=B)
