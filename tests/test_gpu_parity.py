@@ -212,6 +212,16 @@ def test_dsv2_fp8_ragged_nan_padding():
     _lse_check(lse, ref_lse, 2e-2)
 
 
+def test_dsv2_fp8_peaked_attention():
+    # q x 30 on the e4m3 streaming loop: the first tile's maximum is
+    # overtaken, and the recompute pass reloads and widens its tiles again
+    inp = make_inputs("fp8_b128_l8192", seq_lens=[900, 257], q_scale=30.0)
+    _, out, lse = _run(inp, num_splits=1)
+    ref, ref_lse = oracle.decode(**oracle_args(inp, "dequantised"))
+    _check(out, ref, BF16_REL)
+    _lse_check(lse, ref_lse, 5e-2)
+
+
 @pytest.mark.parametrize("page_size", [16, 64])
 def test_dsv2_fp8_paged(page_size):
     # paged e4m3 runs the per-row loader (codes staged in registers)
