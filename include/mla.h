@@ -123,7 +123,10 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch,
  *            times any length-extension factor).
  *   num_splits S >= 1 cuts the token range [0, max_seq_len) into S chunks
  *            of mla_split_chunk(max_seq_len, S) tokens; each (b, split) is
- *            computed independently.
+ *            computed independently (by one workgroup; when there are more
+ *            of them than compute units, full chunks are handed out first,
+ *            then the partly filled ones, largest first, which changes no
+ *            result).
  *   S == 1: out [B, H, d_latent] in out_dtype (MLA_BF16 or MLA_F32),
  *           lse [B, H] f32 (natural log).
  *   S  > 1: out [B, S, H, d_latent] partials in out_dtype (MLA_BF16 or

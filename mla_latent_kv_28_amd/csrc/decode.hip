@@ -26,6 +26,7 @@
 // The softmax is the streaming form in fp32 and base 2 against a fixed
 // per-head reference maximum (see kHeadroom), so the accumulators are never
 // rescaled inside the loop.
+#include <atomic>
 #include <type_traits>
 
 #include "mla_device.h"
@@ -1065,22 +1066,122 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
   tile_barrier();
 }
 
+// Which (sequence, split) item a workgroup takes. Workgroups reach the XCDs
+// round-robin and, within one XCD, its compute units in index order, one per
+// compute unit at a time.
+//  kOrderPlain: index = b * S + split.
+//  kOrderXcd:   a sequence's splits on one XCD (one round of equal items).
+//  kOrderLongestFirst (grids of several rounds): every full chunk first
+//    (sequence-major), then the partly filled last chunks in eight bands of
+//    remainder, largest first, then the empty items; longest-first list
+//    scheduling, which keeps uneven lengths from leaving a ragged last round.
+//    Every wave derives the same item from the lengths, 64 sequences a pass
+//    (a separate kernel instance, so the index orders keep their prologue).
+struct Item {
+  int b, split, len;
+};
+
+struct SeqCounts {
+  int len, full, rem, band, empty;   // band: 0 = largest remainder .. 7; -1 none
+};
+
+__device__ __forceinline__ SeqCounts seq_counts(const DecodeParams& p, int b) {
+  SeqCounts c{0, 0, 0, -1, 0};
+  if (b < p.batch) {
+    c.len = p.seq_lens[b];
+    const int L = p.chunk > 0 ? max(0, min(c.len, p.max_seq_len)) : 0;
+    if (L > 0) {
+      c.full = min(L / p.chunk, p.num_splits);
+      c.rem = L - c.full * p.chunk;   // 0 once every split is full
+      if (c.rem > 0) c.band = (p.chunk - c.rem) / (p.chunk >> 3);   // chunks are multiples of 32
+    }
+    c.empty = p.num_splits - c.full - (c.rem > 0 ? 1 : 0);
+  }
+  return c;
+}
+
+__device__ __forceinline__ int wave_inclusive_sum(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ Item longest_first_item(const DecodeParams& p, int k) {
+  const int lane = threadIdx.x & 63;
+  // class sizes: full chunks, the eight remainder bands
+  const SeqCounts first = seq_counts(p, lane);   // reused by both sweeps
+  int full_total = 0;
+  int band_total[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    const SeqCounts c = b0 == 0 ? first : seq_counts(p, b0 + lane);
+    full_total += __builtin_amdgcn_readlane(wave_inclusive_sum(c.full, lane), 63);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) band_total[q] += __popcll(__ballot(c.band == q));
+  }
+  // the class that holds position k, and k's rank within it
+  int cls = 0;   // 0 full, 1 + q band q, 9 empty
+  if (k >= full_total) {
+    k -= full_total;
+    cls = 9;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (cls == 9) {
+        if (k < band_total[q]) cls = 1 + q;
+        else k -= band_total[q];
+      }
+    }
+  }
+  Item it{0, 0, 0};
+  int base = 0;
+  for (int b0 = 0; b0 < p.batch; b0 += 64) {
+    const SeqCounts c = b0 == 0 ? first : seq_counts(p, b0 + lane);
+    const int n = cls == 0 ? c.full : cls == 9 ? c.empty : (c.band == cls - 1 ? 1 : 0);
+    const int incl = wave_inclusive_sum(n, lane);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (k < base + total) {
+      const uint64_t hit = __ballot(n > 0 && base + incl > k);
+      const int ln = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+      const int off = k - base - (__builtin_amdgcn_readlane(incl, ln) - __builtin_amdgcn_readlane(n, ln));
+      const int full = __builtin_amdgcn_readlane(c.full, ln);
+      const int rem = __builtin_amdgcn_readlane(c.rem, ln);
+      it.b = b0 + ln;
+      it.split = cls == 0 ? off : cls == 9 ? full + (rem > 0 ? 1 : 0) + off : full;
+      it.len = __builtin_amdgcn_readlane(c.len, ln);
+      break;
+    }
+    base += total;
+  }
+  return it;
+}
+
 template <class C>
 __device__ __forceinline__ int64_t out_row(const DecodeParams& p, int b, int split, int head) {
   return p.num_splits > 1 ? (((int64_t)b * p.num_splits + split) * C::H + head)
                           : ((int64_t)b * C::H + head);
 }
 
-template <class C, bool PAGED, bool PSTREAM, bool E4M3 = false>
+template <class C, bool PAGED, bool PSTREAM, bool E4M3, bool LONGEST_FIRST>
 __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   static_assert(!E4M3 || (!PAGED && !C::F32 && !C::FP8), "e4m3 tiles stream through the contiguous 16-bit loop");
   using R8 = typename std::conditional<E4M3, E4m3Ring<C>, NoE4m3Ring>::type;
 
-  int w = blockIdx.x;
-  if (p.xcd_remap) w = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  const int b = w / p.num_splits, split = w % p.num_splits;
-  const int len_b = p.seq_lens[b];   // a scalar load, requested before the loads into LDS
+  int b, split, len_b;
+  if constexpr (LONGEST_FIRST) {
+    const Item it = longest_first_item(p, blockIdx.x);
+    b = it.b;
+    split = it.split;
+    len_b = it.len;
+  } else {
+    int w = blockIdx.x;
+    if (p.order == kOrderXcd) w = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    b = w / p.num_splits;
+    split = w % p.num_splits;
+    len_b = p.seq_lens[b];   // a scalar load, requested before the loads into LDS
+  }
   MLA_LDS char* lds = (MLA_LDS char*)smem;
   auto slot = [&](int x) -> MLA_LDS char* {   // x >= 0
     if constexpr (E4M3) {
@@ -1359,28 +1460,50 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   }
 }
 
+// Compute units of the current device, queried once per device (the item
+// order only; any value gives correct results).
+int device_compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <class C, bool LF>
+hipError_t launch_order(const DecodeParams& q, int grid, hipStream_t stream) {
+  if (q.page_shift >= 0) {
+    // pages of at least one tile, a split's pages within one wave's lanes
+    const bool stream_pages = q.page_shift >= 5 && ((q.chunk + (1 << q.page_shift) - 1) >> q.page_shift) + 1 <= 64;
+    if constexpr (C::KIND == kBF16) {
+      if (stream_pages)
+        return launch_kernel((decode_kernel<C, true, true, false, LF>), dim3(grid), dim3(C::THREADS), stream, q);
+    }
+    return launch_kernel((decode_kernel<C, true, false, false, LF>), dim3(grid), dim3(C::THREADS), stream, q);
+  }
+  if constexpr (C::FP8 && C::H == 128 && C::DC == 512 && C::DR == 64) {
+    // contiguous e4m3: widened on the fly into the 16-bit streaming loop
+    using CB = Cfg<C::H, C::DC, C::DR, kBF16>;
+    return launch_kernel((decode_kernel<CB, false, false, true, LF>), dim3(grid), dim3(CB::THREADS), stream, q);
+  }
+  return launch_kernel((decode_kernel<C, false, false, false, LF>), dim3(grid), dim3(C::THREADS), stream, q);
+}
+
 template <class C>
 hipError_t launch(const DecodeParams& p, hipStream_t stream) {
   const int grid = p.batch * p.num_splits;
   if (grid == 0) return hipSuccess;
   DecodeParams q = p;
-  q.xcd_remap = (grid % 8 == 0 && p.num_splits > 1) ? 1 : 0;
-  if (p.page_shift >= 0) {
-    // pages of at least one tile, a split's pages within one wave's lanes
-    const bool stream_pages = p.page_shift >= 5 && ((p.chunk + (1 << p.page_shift) - 1) >> p.page_shift) + 1 <= 64;
-    if constexpr (C::KIND == kBF16) {
-      if (stream_pages) return launch_kernel((decode_kernel<C, true, true>), dim3(grid), dim3(C::THREADS), stream, q);
-    }
-    launch_kernel((decode_kernel<C, true, false>), dim3(grid), dim3(C::THREADS), stream, q);
-  } else {
-    if constexpr (C::FP8 && C::H == 128 && C::DC == 512 && C::DR == 64) {
-      // contiguous e4m3: widened on the fly into the 16-bit streaming loop
-      using CB = Cfg<C::H, C::DC, C::DR, kBF16>;
-      return launch_kernel((decode_kernel<CB, false, false, true>), dim3(grid), dim3(CB::THREADS), stream, q);
-    }
-    launch_kernel((decode_kernel<C, false, false>), dim3(grid), dim3(C::THREADS), stream, q);
+  if (grid > device_compute_units()) {
+    q.order = kOrderLongestFirst;
+    return launch_order<C, true>(q, grid, stream);
   }
-  return hipGetLastError();
+  q.order = (grid % 8 == 0 && p.num_splits > 1) ? kOrderXcd : kOrderPlain;
+  return launch_order<C, false>(q, grid, stream);
 }
 
 }  // namespace

@@ -9,6 +9,9 @@ namespace mla {
 
 enum CacheKind : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
+// Item order of the decode grid (set by the launcher).
+enum DecodeOrder : int { kOrderPlain = 0, kOrderXcd = 1, kOrderLongestFirst = 2 };
+
 struct DecodeParams {
   const void* q_lat;            // [B, H, DC + DR]
   const void* latent;           // cache rows (see mla_kv_cache)
@@ -29,7 +32,7 @@ struct DecodeParams {
   void* out;                    // S == 1: [B, H, DC]; S > 1: [B, S, H, DC] (bf16 | f32)
   float* lse;                   // S == 1: [B, H]; S > 1: [B, S, H]
   int32_t out_bf16;             // out is bf16 (else f32)
-  int32_t xcd_remap;            // 1: keep a sequence's splits on one XCD
+  int32_t order;                // DecodeOrder: which item each workgroup takes
 };
 
 // Decode launchers: return the hipError_t of the launch.

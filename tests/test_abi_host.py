@@ -78,6 +78,9 @@ def test_suggest_splits(L):
     assert mla.mla_suggest_splits(0, 100, 0, 256) == 1
     s = mla.mla_suggest_splits(64, 32768, 64 * 16640, 256)
     assert 1 <= s <= 1024 and mla.mla_split_chunk(32768, s) >= 256
+    # 64 sequences averaging half of 32768 tokens: 14 splits of 2368 tokens
+    # make about 480 non-empty items, two full rounds of 256
+    assert s == 14
 
 
 DSV2 = mla.Dims(128, 512, 64, 128, 128)

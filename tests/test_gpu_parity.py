@@ -277,6 +277,51 @@ def test_timed_launch_records_the_kernel_and_changes_nothing():
         mla.mla_time_next_launch(torch.cuda.Event(enable_timing=True), None)
 
 
+def _sub_batch(inp, lo, hi):
+    """Sequences lo..hi-1 of a contiguous or paged input, sharing its cache rows."""
+    import dataclasses
+    kw = dict(seq_lens=inp.seq_lens[lo:hi], q_nope=inp.q_nope[lo:hi], q_rope=inp.q_rope[lo:hi])
+    if inp.layout == "paged":
+        kw["block_table"] = inp.block_table[lo:hi]
+    else:
+        for f in ("rows", "codes", "scale", "rope"):
+            t = getattr(inp, f)
+            if t is not None:
+                kw[f] = t[lo * inp.seq_stride: hi * inp.seq_stride]
+    return dataclasses.replace(inp, **kw)
+
+
+@pytest.mark.parametrize("kind", ["contiguous", "paged", "fp8"])
+def test_dsv2_several_rounds_equal_one_round_launches(kind):
+    # 48 sequences x 8 splits = 384 items, more than the GPU runs at once: the
+    # decode hands them out longest first. An item's result does not depend on
+    # the order, so the partials equal, bit for bit, those of two launches of
+    # 24 sequences (192 items, one round, in index order). Lengths cover the
+    # empty, one-token, chunk-boundary (512) and full (4096) cases.
+    rng = np.random.default_rng(11)
+    edge = [4096, 0, 1, 511, 512, 513, 1024, 4095, 31, 32, 33, 1536]
+    lens = edge + rng.integers(1, 4097, size=12).tolist() + edge[::-1] + rng.integers(1, 4097, size=12).tolist()
+    common = dict(seq_lens=lens, pad_fill=float("nan"))
+    if kind == "paged":
+        inp = make_inputs("dsv2_b32_l4096", layout="paged", page_size=64, **common)
+    elif kind == "fp8":
+        inp = make_inputs("fp8_b128_l8192", **common)
+    else:
+        inp = make_inputs("dsv2_b32_l4096", **common)
+    full, _, _ = _run(inp, num_splits=8)
+    halves = [_run(_sub_batch(inp, lo, lo + 24), num_splits=8)[0] for lo in (0, 24)]
+    for i, h in enumerate(halves):
+        sl = slice(24 * i, 24 * i + 24)
+        assert torch.equal(full.q_lat[sl], h.q_lat)
+        assert torch.equal(full.lse_part[sl], h.lse_part)
+        assert torch.equal(full.o_part[sl].view(torch.int16), h.o_part.view(torch.int16))
+    out = full.out.double().cpu().numpy()
+    lse = full.lse.double().cpu().numpy()
+    assert np.all(np.isfinite(out)) and np.all(out[[1, 34]] == 0) and np.all(lse[[1, 34]] == -np.inf)
+    _sampled(inp, out, lse, [(0, 5), (3, 77), (5, 127), (7, 0), (20, 64), (40, 3), (47, 100)],
+             BF16_REL, BF16_ABS)
+
+
 # --- full workload sizes, in the launch configuration the benchmark times ---------
 
 def _sampled(inp, out, lse, pairs, rel, absb=None, fp8_reference="dequantised"):
