@@ -234,7 +234,9 @@ def main():
     q_step = B / (ms_step * 1e-3)
     gbps_step = cache_bytes / (ms_step * 1e-3) / 1e9
     gbps_dec = cache_bytes / (ms_dec * 1e-3) / 1e9
-    flops_dec = B * L * 2 * inp.dims.num_heads * (inp.dims.width + inp.dims.d_latent)
+    # scores over d_c + d_rope and the latent sum over d_c, per cached token and head
+    tokens = int(inp.seq_lens.astype(np.int64).sum())
+    flops_dec = tokens * 2 * inp.dims.num_heads * (inp.dims.width + inp.dims.d_latent)
 
     result = {
         "metric": METRIC,
