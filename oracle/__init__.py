@@ -25,3 +25,4 @@ from .mla import (  # noqa: F401
     kv_reduction_vs_gqa_model,
 )
 from .e4m3 import decode_e4m3, encode_e4m3, e4m3_table  # noqa: F401
+from .append import append_entry, quantise_entry, rms_norm, rope  # noqa: F401

@@ -320,3 +320,74 @@ def test_workload_softmax_scales():
         pytest.approx(1 / math.sqrt(192), rel=1e-15)
     long = make_inputs("long_b4_l131072", batch=1, seq_lens=[2]).sm_scale
     assert long == pytest.approx(0.0987910, abs=5e-8)
+
+
+# --- the cache entry of a new token (latent, rotary key, e4m3 form) --------------
+
+def test_rms_norm_closed_forms_and_library():
+    # a constant row normalises to +-1 (eps 0); [3, 4] has mean square 12.5
+    assert np.allclose(oracle.rms_norm(np.full(7, -2.5), 0.0), -1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(oracle.rms_norm(np.array([3.0, 4.0]), 0.0),
+                               np.array([3.0, 4.0]) / math.sqrt(12.5), rtol=1e-15)
+    rng = np.random.default_rng(3)
+    x, g = rng.standard_normal((5, 96)), rng.standard_normal(96)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(g), 1e-6).numpy()
+    np.testing.assert_allclose(oracle.rms_norm(x, 1e-6, g), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_rope_closed_forms_and_relative_position():
+    # one pair at frequency 1: position 1 turns (1, 0) by one radian
+    np.testing.assert_allclose(oracle.rope(np.array([1.0, 0.0]), 1, 10000.0),
+                               [math.cos(1.0), math.sin(1.0)], rtol=0, atol=1e-15)
+    # d = 4, base 10000: the second pair turns at 10000^(-1/2) = 0.01 rad per position
+    np.testing.assert_allclose(oracle.rope(np.array([0.0, 0.0, 0.0, 1.0]), 100, 10000.0),
+                               [0.0, 0.0, -math.sin(1.0), math.cos(1.0)], rtol=0, atol=1e-14)
+    rng = np.random.default_rng(4)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    assert np.array_equal(oracle.rope(q, 0, 10000.0), q)                      # position 0: identity
+    for m in (0, 7, 4095):
+        assert np.linalg.norm(oracle.rope(q, m, 10000.0)) == pytest.approx(np.linalg.norm(q), rel=1e-14)
+    # the defining property: the score of rotated q and k depends on m - n only
+    s1 = oracle.rope(q, 1000, 10000.0) @ oracle.rope(k, 990, 10000.0)
+    s2 = oracle.rope(q, 20, 10000.0) @ oracle.rope(k, 10, 10000.0)
+    assert s1 == pytest.approx(s2, rel=1e-11)
+    s3 = oracle.rope(q, 21, 10000.0) @ oracle.rope(k, 10, 10000.0)
+    assert abs(s3 - s2) > 1e-3                                                  # and does depend on it
+
+
+def test_append_entry_brute_force_and_one_hot():
+    rng = np.random.default_rng(5)
+    B, d, d_c, d_r = 3, 12, 8, 4
+    h = rng.standard_normal((B, d))
+    w_dkv, w_kr = rng.standard_normal((d_c, d)), rng.standard_normal((d_r, d))
+    gain, pos, eps, base = rng.standard_normal(d_c), np.array([0, 5, 130]), 1e-6, 500.0
+    c, k = oracle.append_entry(h, w_dkv, w_kr, pos, eps, base, gain)
+    for b in range(B):                      # the definition in plain loops
+        x = [sum(w_dkv[i, j] * h[b, j] for j in range(d)) for i in range(d_c)]
+        ms = sum(v * v for v in x) / d_c
+        for i in range(d_c):
+            assert c[b, i] == pytest.approx(x[i] / math.sqrt(ms + eps) * gain[i], rel=1e-12)
+        y = [sum(w_kr[i, j] * h[b, j] for j in range(d)) for i in range(d_r)]
+        for i in range(d_r // 2):
+            a = pos[b] * base ** (-2.0 * i / d_r)
+            assert k[b, 2 * i] == pytest.approx(y[2 * i] * math.cos(a) - y[2 * i + 1] * math.sin(a), rel=1e-11, abs=1e-12)
+            assert k[b, 2 * i + 1] == pytest.approx(y[2 * i] * math.sin(a) + y[2 * i + 1] * math.cos(a), rel=1e-11, abs=1e-12)
+    # a one-hot hidden state selects a column of each projection
+    e = np.zeros((1, d))
+    e[0, 4] = 2.0
+    c1, k1 = oracle.append_entry(e, w_dkv, w_kr, [0], 0.0, base)
+    col = 2.0 * w_dkv[:, 4]
+    np.testing.assert_allclose(c1[0], col / np.sqrt(np.mean(col ** 2)), rtol=1e-14)
+    np.testing.assert_allclose(k1[0], 2.0 * w_kr[:, 4], rtol=1e-14)
+
+
+def test_quantise_entry_against_library_cast():
+    rng = np.random.default_rng(6)
+    c = rng.standard_normal((4, 512)) * np.array([1.0, 1e-3, 30.0, 0.0])[:, None]
+    codes, scale = oracle.quantise_entry(c)
+    assert scale[3] == 1.0 and np.all(codes[3] & 0x7F == 0)                  # all-zero row (signed zeros)
+    np.testing.assert_allclose(scale[:3], np.abs(c[:3]).max(axis=1) / 448.0, rtol=1e-15)
+    y = np.clip(c[:3] / scale[:3, None], -448.0, 448.0)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes[:3], ref)
+    assert np.all((codes[:3] & 0x7F).max(axis=1) == 0x7E)                     # the absmax element is 448
