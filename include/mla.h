@@ -189,6 +189,39 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
                                 const void* w_uv, int32_t w_dtype, void* out, int32_t out_dtype,
                                 float* lse, mla_stream stream);
 
+/*
+ * The cache entry of one new token per sequence (DeepSeek-V2 paper, section
+ * 2.1.2: the latent is the down-projection W_DKV h of the token's hidden
+ * state; section 2.1.3: the shared rotary key is RoPE(W_KR h) at the token's
+ * position; section 3.1.2, model hyper-parameters: an RMS norm follows the
+ * compressed latent):
+ *   c_KV[b] = RMSNorm(W_DKV h[b]) = x / sqrt(mean(x^2) + rms_eps) * gain,
+ *   k_R[b]  = RoPE(W_KR h[b], positions[b]): features (2i, 2i + 1) turned by
+ *             positions[b] * rope_base^(-2i / d_rope),
+ * written into row positions[b] of sequence b of `cache` (the same layouts
+ * mla_decode reads; this call writes through its pointers).
+ *   h           [B, hidden], w_dkv [d_latent, hidden], w_kr [d_rope, hidden],
+ *   norm_gain   [d_latent] or NULL (gain 1), all in `dtype`:
+ *               MLA_BF16 for the DeepSeek-V2 shape (cache MLA_BF16, or
+ *               MLA_FP8_E4M3: codes of c_KV / s with s = absmax(c_KV) / 448,
+ *               1 for an all-zero row, rounded to nearest even, the rotary key
+ *               in bf16), MLA_F32 for the tiny shape (cache MLA_F32).
+ *   positions   [B] int32 device array; a position outside the cache (below
+ *               0, at or beyond seq_stride, or beyond the block table's pages)
+ *               writes nothing for that sequence.
+ *   workspace   device memory of at least mla_cache_append_workspace() bytes,
+ *               16-byte aligned, owned by the caller (fp32 partial sums).
+ * Products accumulate in fp32, the norm and rotation run in fp32 (angles in
+ * fp64). hidden a multiple of 16 (bf16) or 4 (f32). batch == 0 is a no-op.
+ * Errors as for mla_decode; MLA_ERR_SHAPE also for a short workspace.
+ */
+int64_t mla_cache_append_workspace(const mla_dims* dims, int32_t batch, int32_t hidden);
+mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
+                            const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
+                            float rms_eps, float rope_base, const int32_t* positions,
+                            const mla_kv_cache* cache, void* workspace, int64_t workspace_bytes,
+                            mla_stream stream);
+
 /* Tokens per split chunk that mla_decode uses for (max_seq_len, num_splits):
  * ceil(max_seq_len / num_splits) rounded up to a multiple of 32. */
 int32_t mla_split_chunk(int32_t max_seq_len, int32_t num_splits);

@@ -22,7 +22,8 @@ _STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DT
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
            "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error",
-           "mla_time_next_launch")
+           "mla_time_next_launch",
+           "mla_cache_append", "mla_cache_append_workspace")
 
 
 class MLAError(RuntimeError):
@@ -70,6 +71,11 @@ def lib():
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_last_hip_error.argtypes = []
         L.mla_time_next_launch.argtypes = [vp, vp]
+        L.mla_cache_append_workspace.argtypes = [pd, i32, i32]
+        L.mla_cache_append_workspace.restype = i64
+        L.mla_cache_append.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, f32, f32, vp,
+                                       ctypes.POINTER(KVCache), vp, i64, vp]
+        L.mla_cache_append.restype = i32
         for name in ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_split_chunk",
                      "mla_suggest_splits", "mla_last_hip_error", "mla_combine_out_proj",
                      "mla_time_next_launch"):
@@ -195,6 +201,32 @@ def mla_combine_out_proj(dims, batch, num_splits, o_part, part_dtype, lse_part, 
         _dev(lse, "lse", torch.float32, batch * H),
         _stream(stream))
     _check(st, "mla_combine_out_proj")
+
+
+def mla_cache_append_workspace(dims, batch, hidden):
+    """Bytes of fp32 workspace mla_cache_append needs."""
+    d = dims_of(dims)
+    return int(lib().mla_cache_append_workspace(ctypes.byref(d), batch, hidden))
+
+
+def mla_cache_append(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps, rope_base,
+                     positions, cache, workspace, stream=None):
+    """Write the cache entry (RMS-normed latent, rotated key) of one new token
+    per sequence at row positions[b] of `cache`."""
+    d = dims_of(dims)
+    t = _TORCH_DTYPE.get(dtype)
+    st = lib().mla_cache_append(
+        ctypes.byref(d), batch, hidden,
+        _dev(h, "h", t, batch * hidden),
+        _dev(w_dkv, "w_dkv", t, d.d_latent * hidden),
+        _dev(w_kr, "w_kr", t, d.d_rope * hidden),
+        _dev(norm_gain, "norm_gain", t, d.d_latent),
+        dtype, float(rms_eps), float(rope_base),
+        _dev(positions, "positions", torch.int32, batch),
+        ctypes.byref(cache),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream))
+    _check(st, "mla_cache_append")
 
 
 def mla_split_chunk(max_seq_len, num_splits):

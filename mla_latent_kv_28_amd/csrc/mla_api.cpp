@@ -285,6 +285,79 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
   return hip_status(mla::launch_combine_outproj_dsv2_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
+int64_t mla_cache_append_workspace(const mla_dims* dims, int32_t batch, int32_t hidden) {
+  if (dims == nullptr || batch <= 0 || hidden <= 0) return 0;
+  return static_cast<int64_t>(mla::append_slices(hidden)) * batch * (dims->d_latent + dims->d_rope) *
+         static_cast<int64_t>(sizeof(float));
+}
+
+mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
+                            const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
+                            float rms_eps, float rope_base, const int32_t* positions,
+                            const mla_kv_cache* cache, void* workspace, int64_t workspace_bytes,
+                            mla_stream stream) {
+  if (dims == nullptr || cache == nullptr) return MLA_ERR_NULL;
+  if (batch < 0 || hidden <= 0) return MLA_ERR_SHAPE;
+  if (!std::isfinite(rms_eps) || rms_eps < 0.0f || !std::isfinite(rope_base) || rope_base <= 0.0f)
+    return MLA_ERR_SHAPE;
+  if (!valid_dtype(dtype) || !valid_dtype(cache->dtype)) return MLA_ERR_DTYPE;
+  const Shape sh = shape_of(dims);
+  if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
+  if (sh == Shape::kDsv2 && (dtype != MLA_BF16 || cache->dtype == MLA_F32)) return MLA_ERR_DTYPE;
+  if (sh == Shape::kTiny && (dtype != MLA_F32 || cache->dtype != MLA_F32)) return MLA_ERR_DTYPE;
+  if (hidden % (dtype == MLA_BF16 ? 16 : 4) != 0) return MLA_ERR_SHAPE;   // whole 16-wide k steps (bf16)
+  if (batch == 0) return MLA_OK;
+  if (!h || !w_dkv || !w_kr || !positions || !cache->latent || !workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < mla_cache_append_workspace(dims, batch, hidden)) return MLA_ERR_SHAPE;
+  const bool fp8 = cache->dtype == MLA_FP8_E4M3;
+  if (fp8 && (!cache->rope || !cache->scale)) return MLA_ERR_NULL;
+  if (cache->page_size < 0) return MLA_ERR_SHAPE;
+  const bool paged = cache->page_size > 0;
+  if (paged) {
+    if (!cache->block_table) return MLA_ERR_NULL;
+    if (!is_pow2(cache->page_size) || cache->max_pages_per_seq < 1) return MLA_ERR_SHAPE;
+  } else if (cache->seq_stride < 1) {
+    return MLA_ERR_SHAPE;
+  }
+  const int64_t width = fp8 ? dims->d_latent : dims->d_latent + dims->d_rope;
+  if (cache->row_stride < width) return MLA_ERR_SHAPE;
+  const int64_t elem = cache->dtype == MLA_F32 ? 4 : (fp8 ? 1 : 2);
+  if ((cache->row_stride * elem) % 16 != 0) return MLA_ERR_ALIGN;
+  if (fp8) {
+    if (cache->rope_stride < dims->d_rope) return MLA_ERR_SHAPE;
+    if (!aligned16(cache->rope) || (reinterpret_cast<uintptr_t>(cache->scale) & 3u) != 0) return MLA_ERR_ALIGN;
+  }
+  if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(cache->latent) ||
+      !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  mla::AppendParams p{};
+  p.h = h;
+  p.w_dkv = w_dkv;
+  p.w_kr = w_kr;
+  p.gain = norm_gain;
+  p.positions = positions;
+  p.latent = const_cast<void*>(cache->latent);
+  p.rope = const_cast<void*>(cache->rope);
+  p.scale = const_cast<float*>(cache->scale);
+  p.row_stride = cache->row_stride;
+  p.rope_stride = cache->rope_stride;
+  p.seq_stride = cache->seq_stride;
+  p.block_table = cache->block_table;
+  p.max_pages = cache->max_pages_per_seq;
+  p.page_shift = paged ? log2i(cache->page_size) : -1;
+  p.work = static_cast<float*>(workspace);
+  p.batch = batch;
+  p.hidden = hidden;
+  p.ksplits = mla::append_slices(hidden);
+  p.d_latent = dims->d_latent;
+  p.d_rope = dims->d_rope;
+  p.eps = rms_eps;
+  p.rope_base = rope_base;
+  return hip_status(mla::launch_cache_append(p, sh == Shape::kDsv2, cache->dtype == MLA_FP8_E4M3 ? mla::kFP8
+                                                 : cache->dtype == MLA_BF16 ? mla::kBF16 : mla::kF32,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 namespace mla {

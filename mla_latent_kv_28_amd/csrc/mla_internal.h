@@ -51,6 +51,26 @@ struct CombineParams {
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
+// Cache entry of one new token per sequence (append.hip).
+struct AppendParams {
+  const void* h;                // [B, hidden] (bf16 | f32)
+  const void* w_dkv;            // [d_latent, hidden]
+  const void* w_kr;             // [d_rope, hidden]
+  const void* gain;             // [d_latent] norm gain or null
+  const int32_t* positions;     // [B] position (cache row) of the new token
+  void* latent;                 // cache rows (codes for e4m3)
+  void* rope;                   // e4m3 only: rotary keys, bf16
+  float* scale;                 // e4m3 only: per-token scale
+  int64_t row_stride, rope_stride, seq_stride;
+  const int32_t* block_table;   // paged only
+  int32_t max_pages, page_shift;   // page_shift -1: contiguous
+  float* work;                  // [ksplits, B, d_latent + d_rope] partial sums
+  int32_t batch, hidden, ksplits, d_latent, d_rope;
+  float eps, rope_base;
+};
+int append_slices(int hidden);
+hipError_t launch_cache_append(const AppendParams& p, bool dsv2, int cache_kind, hipStream_t s);
+
 // Per-head batched GEMM: C[b, h, n] = sum_k A[b, h, k] * Bm_h(k, n).
 struct GemmParams {
   const void* a;         // [B, H, lda] (bf16 or f32)
@@ -91,14 +111,20 @@ void take_launch_events(hipEvent_t* start, hipEvent_t* stop);
 // Every kernel of the library is launched through this: with a pending event
 // pair the launch carries it (hipExtLaunchKernel), otherwise a plain launch.
 template <typename K, typename... Args>
-inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  take_launch_events(&e0, &e1);
+inline hipError_t launch_kernel_events(K kernel, dim3 grid, dim3 block, hipStream_t stream, hipEvent_t e0,
+                                       hipEvent_t e1, Args... args) {
   if (e0 != nullptr || e1 != nullptr)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0, args...);
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
   return hipGetLastError();
+}
+
+template <typename K, typename... Args>
+inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  take_launch_events(&e0, &e1);
+  return launch_kernel_events(kernel, grid, block, stream, e0, e1, args...);
 }
 
 }  // namespace mla

@@ -15,4 +15,6 @@ from .inputs import (  # noqa: F401
     rope_rotate,
     rms_normalise,
     quantise_rows_e4m3,
+    AppendInputs,
+    make_append_inputs,
 )

@@ -320,3 +320,38 @@ def oracle_args(inp, fp8_reference="dequantised"):
     return dict(q_nope=inp.q_nope.double().numpy(), q_rope=inp.q_rope.double().numpy(),
                 w_uk=inp.w_uk.double().numpy(), w_uv=inp.w_uv.double().numpy(),
                 cache=cache, seq_lens=inp.seq_lens, sm_scale=inp.sm_scale)
+
+
+@dataclass
+class AppendInputs:
+    """Inputs of the cache entry of one new token per sequence."""
+    dims: Dims
+    dtype: str                 # "bf16" | "f32" (hidden states and weights)
+    h: torch.Tensor            # [B, hidden]
+    w_dkv: torch.Tensor        # [d_latent, hidden]
+    w_kr: torch.Tensor         # [d_rope, hidden]
+    gain: Optional[torch.Tensor]   # [d_latent] or None
+    positions: np.ndarray      # int32 [B]
+    eps: float = 1e-6
+    base: float = 10000.0
+
+
+def make_append_inputs(dims=DSV2, batch=32, seed=0, max_position=4096, with_gain=False, positions=None):
+    """Hidden states N(0, 1); projections N(0, 0.006^2) for the DeepSeek-V2
+    shape (the paper's initialisation), N(0, 1) / sqrt(hidden) for the tiny
+    shape (stored fp32); an optional gain 1 + N(0, 0.1^2); positions uniform
+    on [0, max_position). Draws in that order from default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    hid = dims.hidden
+    store = "f32" if dims == TINY else "bf16"
+    std = 1.0 / math.sqrt(hid) if dims == TINY else 0.006
+    h = rng.standard_normal((batch, hid))
+    w_dkv = rng.standard_normal((dims.d_latent, hid)) * std
+    w_kr = rng.standard_normal((dims.d_rope, hid)) * std
+    gain = 1.0 + 0.1 * rng.standard_normal(dims.d_latent) if with_gain else None
+    pos = rng.integers(0, max_position, size=batch)
+    if positions is not None:
+        pos = np.asarray(positions, dtype=np.int64)
+    return AppendInputs(dims=dims, dtype=store, h=_store(h, store), w_dkv=_store(w_dkv, store),
+                        w_kr=_store(w_kr, store), gain=None if gain is None else _store(gain, store),
+                        positions=pos.astype(np.int32))

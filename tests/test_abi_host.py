@@ -188,3 +188,32 @@ def test_binding_refuses_host_tensors(L):
     x = torch.zeros(4)
     with pytest.raises(TypeError):
         mla.mla_absorb_q(TINY, 1, x, x, x, x, mla.F32)
+
+
+@no_gpu
+def test_cache_append_argument_errors(L):
+    d = ctypes.byref(DSV2)
+    ws = mla.mla_cache_append_workspace(DSV2, 4, 5120)
+    assert ws == 20 * 4 * 576 * 4                     # 256-wide slices of the hidden size
+
+    def f(dims=d, batch=4, hidden=5120, h=P, w1=P, w2=P, gain=None, dtype=mla.BF16, eps=1e-6, base=1e4,
+          pos=P, cache=None, work=P, work_bytes=ws):
+        cache = _cache(seq_stride=64) if cache is None else cache
+        return L.mla_cache_append(dims, batch, hidden, h, w1, w2, gain, dtype, eps, base, pos,
+                                  ctypes.byref(cache), work, work_bytes, None)
+    assert f(dims=None) == -1
+    assert f(batch=-1) == -2
+    assert f(hidden=5128) == -2                       # whole 16-wide k steps
+    assert f(eps=-1.0) == -2 and f(base=0.0) == -2 and f(eps=float("nan")) == -2
+    assert f(dims=ctypes.byref(mla.Dims(64, 512, 64, 128, 128))) == -4
+    assert f(dtype=mla.F32) == -3                     # bf16 inputs for this shape
+    assert f(cache=_cache(dtype=mla.F32, seq_stride=64)) == -3
+    assert f(dims=ctypes.byref(TINY), hidden=128, dtype=mla.F32) == -3      # the tiny shape takes an f32 cache
+    assert f(h=None) == -1 and f(pos=None) == -1 and f(work=None) == -1
+    assert f(work_bytes=ws - 4) == -2
+    assert f(cache=_cache(dtype=mla.FP8_E4M3, row_stride=512, seq_stride=64)) == -1   # no rope / scale
+    assert f(cache=_cache(page_size=48, block_table=P, max_pages_per_seq=4)) == -2
+    assert f(cache=_cache(page_size=64, block_table=None, max_pages_per_seq=4)) == -1
+    assert f(cache=_cache(row_stride=575, seq_stride=64)) == -2
+    assert f(h=P + 2) == -5 and f(work=P + 4) == -5
+    assert f(batch=0, h=None, w1=None, w2=None, pos=None, work=None) == 0

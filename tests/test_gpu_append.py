@@ -1,0 +1,147 @@
+"""GPU parity of the cache entry of a new token (mla_cache_append) against the
+float64 oracle.
+
+Bounds: a bf16 entry is within one bf16 rounding (2^-8 relative) of the
+oracle plus 1e-4 absolute for the fp32 accumulation over the hidden size; an
+fp32 entry (tiny shape) within 1e-5; an e4m3 entry has its scale within 1e-5
+relative and every code no farther from the oracle's latent / scale than the
+oracle's own nearest code, up to 1e-3 relative for the fp32 arithmetic. Rows
+other than the written ones keep their fill.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_synth import DSV2, TINY, make_append_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_latent_kv_28_amd as mla
+    mla.lib()     # fails loudly when the library is missing
+
+
+def _run(inp, kind="bf16", layout="contiguous", page_size=64, capacity=None, seed=7):
+    """Append into a cache filled with sentinels; return (written rows, cache, row index per sequence)."""
+    import mla_latent_kv_28_amd as mla
+    d, B, hid = inp.dims, inp.h.shape[0], inp.dims.hidden
+    print("case: %s B=%d kind=%s layout=%s positions=%s" % ("tiny" if d == TINY else "dsv2", B, kind, layout,
+                                                             inp.positions[:6].tolist()), flush=True)
+    dev = "cuda"
+    cap = capacity or int(max(inp.positions.max(), 0)) + 1
+    rng = np.random.default_rng(seed)
+    if layout == "contiguous":
+        n_rows, bt, pages = B * cap, None, 0
+        row_of = lambda b, p: b * cap + p
+    else:
+        pages = -(-cap // page_size)
+        bt = rng.permutation(B * pages).reshape(B, pages).astype(np.int32)
+        n_rows = B * pages * page_size
+        row_of = lambda b, p: int(bt[b, p // page_size]) * page_size + p % page_size
+    geo = dict(page_size=page_size if layout == "paged" else 0, seq_stride=cap if layout == "contiguous" else 0,
+               block_table=None if bt is None else torch.from_numpy(bt).to(dev), max_pages_per_seq=pages)
+    width = d.d_latent + d.d_rope
+    if kind == "fp8":
+        codes = torch.full((n_rows, d.d_latent), 0x55, dtype=torch.uint8, device=dev)
+        scale = torch.full((n_rows,), -1.0, dtype=torch.float32, device=dev)
+        rope = torch.full((n_rows, d.d_rope), float("nan"), dtype=torch.bfloat16, device=dev)
+        cache = mla.kv_cache(mla.FP8_E4M3, codes, rope=rope, scale=scale, row_stride=d.d_latent,
+                             rope_stride=d.d_rope, **geo)
+        store = (codes, scale, rope)
+    else:
+        t = torch.float32 if kind == "f32" else torch.bfloat16
+        rows = torch.full((n_rows, width), float("nan"), dtype=t, device=dev)
+        cache = mla.kv_cache(mla.F32 if kind == "f32" else mla.BF16, rows, row_stride=width, **geo)
+        store = (rows,)
+    dt = mla.F32 if inp.dtype == "f32" else mla.BF16
+    ws = torch.empty(mla.mla_cache_append_workspace(d, B, hid) // 4, dtype=torch.float32, device=dev)
+    mla.mla_cache_append(d, B, hid, inp.h.to(dev), inp.w_dkv.to(dev), inp.w_kr.to(dev),
+                         None if inp.gain is None else inp.gain.to(dev), dt, inp.eps, inp.base,
+                         torch.from_numpy(inp.positions).to(dev), cache, ws)
+    torch.cuda.synchronize()
+    rows_idx = [row_of(b, int(p)) if 0 <= p < cap else -1 for b, p in enumerate(inp.positions)]
+    return [s.cpu() for s in store], rows_idx
+
+
+def _reference(inp):
+    f = lambda t: None if t is None else t.double().numpy()
+    return oracle.append_entry(f(inp.h), f(inp.w_dkv), f(inp.w_kr), inp.positions, inp.eps, inp.base, f(inp.gain))
+
+
+def _check_dense(store, rows_idx, inp, rtol, atol):
+    rows = store[0].double().numpy()
+    c_ref, k_ref = _reference(inp)
+    d = inp.dims
+    written = [r for r in rows_idx if r >= 0]
+    for b, r in enumerate(rows_idx):
+        if r < 0:
+            continue
+        got = rows[r]
+        for got_part, ref in ((got[:d.d_latent], c_ref[b]), (got[d.d_latent:], k_ref[b])):
+            err = np.abs(got_part - ref)
+            assert np.all(err <= rtol * np.abs(ref) + atol), (b, float(err.max()))
+    untouched = np.ones(rows.shape[0], dtype=bool)
+    untouched[written] = False
+    assert np.all(np.isnan(rows[untouched]))
+
+
+def test_dsv2_bf16_contiguous_two_row_blocks():
+    inp = make_append_inputs(DSV2, batch=40, seed=1, max_position=700)
+    store, idx = _run(inp, "bf16")
+    _check_dense(store, idx, inp, 2.0 ** -8, 1e-4)
+
+
+def test_dsv2_bf16_paged_with_gain():
+    inp = make_append_inputs(DSV2, batch=9, seed=2, max_position=300, with_gain=True)
+    store, idx = _run(inp, "bf16", layout="paged", page_size=64)
+    _check_dense(store, idx, inp, 2.0 ** -8, 1e-4)
+
+
+def test_dsv2_positions_outside_the_cache_write_nothing():
+    inp = make_append_inputs(DSV2, batch=5, seed=3, positions=[0, -1, 63, 64, 10])
+    store, idx = _run(inp, "bf16", layout="paged", page_size=32, capacity=64)
+    assert idx[1] == -1 and idx[3] == -1
+    _check_dense(store, idx, inp, 2.0 ** -8, 1e-4)
+    store, idx = _run(inp, "bf16", capacity=64)
+    _check_dense(store, idx, inp, 2.0 ** -8, 1e-4)
+
+
+def test_tiny_f32():
+    inp = make_append_inputs(TINY, batch=3, seed=4, max_position=64, with_gain=True)
+    store, idx = _run(inp, "f32")
+    _check_dense(store, idx, inp, 1e-5, 1e-6)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_dsv2_e4m3(layout):
+    inp = make_append_inputs(DSV2, batch=36, seed=5, max_position=200)
+    (codes, scale, rope), idx = _run(inp, "fp8", layout=layout, page_size=16)
+    codes, scale, rope = codes.numpy(), scale.double().numpy(), rope.double().numpy()
+    c_ref, k_ref = _reference(inp)
+    ref_codes, ref_scale = oracle.quantise_entry(c_ref)
+    for b, r in enumerate(idx):
+        assert abs(scale[r] - ref_scale[b]) <= 1e-5 * ref_scale[b]
+        y = c_ref[b] / ref_scale[b]
+        v = oracle.decode_e4m3(codes[r])
+        v_ref = oracle.decode_e4m3(ref_codes[b])
+        # no farther than the nearest code, up to the fp32 arithmetic
+        assert np.all(np.abs(v - y) <= np.abs(v_ref - y) + 1e-3 * np.abs(y) + 1e-9), b
+        assert np.mean(codes[r] == ref_codes[b]) > 0.99
+        assert np.all(np.abs(rope[r] - k_ref[b]) <= 2.0 ** -8 * np.abs(k_ref[b]) + 1e-4)
+    others = np.ones(codes.shape[0], dtype=bool)
+    others[idx] = False
+    assert np.all(codes[others] == 0x55) and np.all(scale[others] == -1.0) and np.all(np.isnan(rope[others]))
+
+
+def test_dsv2_full_batch_128_and_deterministic():
+    inp = make_append_inputs(DSV2, batch=128, seed=6, max_position=300)
+    s1, idx = _run(inp, "bf16")
+    _check_dense(s1, idx, inp, 2.0 ** -8, 1e-4)
+    s2, _ = _run(inp, "bf16")
+    assert torch.equal(s1[0].view(torch.int16), s2[0].view(torch.int16))
