@@ -64,6 +64,53 @@ def hbm_traffic(workload):
     return int(round(prof["bytes_per_launch"]))
 
 
+def cache_append_time(inp, stream, reps=20, per_graph=20):
+    """mla_cache_append (the new token's latent and rotary key, written into
+    the cache) for the workload's batch and the DeepSeek-V2 hidden size 5120,
+    bf16: HIP events on its stream around replays of a graph of back-to-back
+    calls. Not part of the decode step; reported beside it."""
+    import torch
+    import mla_latent_kv_28_amd as mla
+    from mla_synth import make_append_inputs
+    d, B = inp.dims, inp.batch
+    a = make_append_inputs(d, batch=B, seed=1, max_position=1, positions=[0] * B)
+    dev = "cuda:0"
+    h, w1, w2 = a.h.to(dev), a.w_dkv.to(dev), a.w_kr.to(dev)
+    pos = torch.from_numpy(a.positions).to(dev)
+    rows = torch.zeros((B, d.d_latent + d.d_rope), dtype=torch.bfloat16, device=dev)
+    cache = mla.kv_cache(mla.BF16, rows, seq_stride=1)
+    ws = torch.empty(mla.mla_cache_append_workspace(d, B, d.hidden) // 4, dtype=torch.float32, device=dev)
+
+    def call():
+        mla.mla_cache_append(d, B, d.hidden, h, w1, w2, None, mla.BF16, a.eps, a.base, pos, cache, ws)
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(per_graph):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+    # bytes that must move: both projections, the hidden states, the rows written
+    alg = (d.d_latent + d.d_rope) * d.hidden * 2 + B * d.hidden * 2 + B * (d.d_latent + d.d_rope) * 2
+    gbps = alg / (us * 1e-6) / 1e9
+    return {"batch": B, "hidden": d.hidden, "cache": "bf16", "us_per_call": round(us, 3),
+            "calls_timed": reps * per_graph, "algorithmic_bytes": alg, "GBps": round(gbps, 1),
+            "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+            "timing": "HIP events on the launch stream around graph replays of back-to-back calls"}
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle, as it stands, on whole sequences of the same
     workload until about `budget_s` seconds of CPU work have run."""
@@ -277,6 +324,8 @@ def main():
             "mfma_frac_of_bf16_dense_peak": round(flops_dec / (ms_dec * 1e-3) / 2.5e15, 4),
         },
     }
+    if inp.dims.hidden == 5120 and not args.eager:
+        result["cache_append"] = cache_append_time(inp, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

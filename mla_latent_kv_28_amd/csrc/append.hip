@@ -13,8 +13,9 @@
 //     and slice, MFMA 32x32x16 with operands loaded straight from memory;
 //     fp32: one thread per output column, plain fma). The weights are read
 //     once per 32 batch rows; they dominate the bytes.
-//  2. append_finish: one wave per sequence sums the slices in order, applies
-//     the norm and the rotation in fp32 (angles in fp64), and writes the row
+//  2. append_finish: one workgroup per sequence sums the slices in a fixed
+//     order, applies the norm and the rotation in fp32 (angles in fp64), and
+//     writes the row
 //     of its position: bf16 or fp32 [c_KV ; k_R], or e4m3 codes of c_KV with a
 //     per-token scale absmax / 448 and the rotary key in bf16.
 #include <hip/hip_runtime.h>
@@ -100,17 +101,20 @@ __device__ __forceinline__ int64_t entry_row(const AppendParams& p, int b, int p
   return (page << p.page_shift) + (pos & ((1 << p.page_shift) - 1));
 }
 
-// DC latent features, DR rotary ones; lanes own PER consecutive latent features.
+// DC latent features, DR rotary ones; lanes own PER consecutive latent
+// features. Four waves sum every fourth slice each (their loads go out
+// together); wave 0 adds the four sums in wave order and finishes the row.
+constexpr int kFinishWaves = 4;
+
 template <int DC, int DR, int KIND>
-__global__ __launch_bounds__(64) void append_finish(AppendParams p) {
+__global__ __launch_bounds__(64 * kFinishWaves) void append_finish(AppendParams p) {
   static_assert(DR <= 64 && DR % 2 == 0, "one rotary feature per lane");
   constexpr int PER = DC >= 64 ? DC / 64 : 1;
   static_assert(DC >= 64 ? DC % 64 == 0 : true, "latent width");
-  const int lane = threadIdx.x, b = blockIdx.x;
+  __shared__ float red[kFinishWaves - 1][PER + 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, b = blockIdx.x;
   const int N = DC + DR;
   const int pos = p.positions[b];
-  const int64_t row = entry_row(p, b, pos);
-  if (row < 0) return;                                  // uniform: outside the cache, nothing written
   const bool lat_ok = DC >= 64 || lane < DC;
   const int c0 = DC >= 64 ? lane * PER : lane;
   const float* part = p.work + (int64_t)b * N;
@@ -120,14 +124,50 @@ __global__ __launch_bounds__(64) void append_finish(AppendParams p) {
 #pragma unroll
   for (int j = 0; j < PER; ++j) x[j] = 0.0f;
   float kr = 0.0f;
-  for (int s = 0; s < p.ksplits; ++s) {                 // slices in order: deterministic
-    const float* ps = part + s * slice_stride;
-    if (lat_ok) {
+  // this wave's slices in order; the loads of U of them go out together
+  constexpr int U = 8;
+  for (int t0 = 0; wave + kFinishWaves * t0 < p.ksplits; t0 += U) {
+    float v[U][PER], vk[U];
 #pragma unroll
-      for (int j = 0; j < PER; ++j) x[j] += ps[c0 + j];
+    for (int u = 0; u < U; ++u) {
+      const int sl = min(wave + kFinishWaves * (t0 + u), p.ksplits - 1);
+      const float* ps = part + (int64_t)sl * slice_stride;
+      if constexpr (PER % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < PER; j += 4) {
+          const f32x4 t = *(const f32x4*)(ps + c0 + j);
+          v[u][j] = t[0], v[u][j + 1] = t[1], v[u][j + 2] = t[2], v[u][j + 3] = t[3];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[u][j] = lat_ok ? ps[c0 + j] : 0.0f;
+      }
+      vk[u] = lane < DR ? ps[DC + lane] : 0.0f;
     }
-    if (lane < DR) kr += ps[DC + lane];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (wave + kFinishWaves * (t0 + u) < p.ksplits) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) x[j] += v[u][j];
+        kr += vk[u];
+      }
+    }
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) red[wave - 1][j][lane] = x[j];
+    red[wave - 1][PER][lane] = kr;
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < kFinishWaves - 1; ++w) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) x[j] += red[w][j][lane];
+    kr += red[w][PER][lane];
+  }
+  const int64_t row = entry_row(p, b, pos);
+  if (row < 0) return;                                  // outside the cache: nothing written
   // RMS norm of the latent
   float ss = 0.0f;
 #pragma unroll
@@ -208,13 +248,16 @@ hipError_t launch_cache_append(const AppendParams& p, bool dsv2, int cache_kind,
                              stream, e0, nullptr, p);
     if (e != hipSuccess) return e;
     if (cache_kind == kFP8)
-      return launch_kernel_events((append_finish<512, 64, kFP8>), dim3(p.batch), dim3(64), stream, nullptr, e1, p);
-    return launch_kernel_events((append_finish<512, 64, kBF16>), dim3(p.batch), dim3(64), stream, nullptr, e1, p);
+      return launch_kernel_events((append_finish<512, 64, kFP8>), dim3(p.batch), dim3(64 * kFinishWaves), stream,
+                                  nullptr, e1, p);
+    return launch_kernel_events((append_finish<512, 64, kBF16>), dim3(p.batch), dim3(64 * kFinishWaves), stream,
+                                nullptr, e1, p);
   }
   e = launch_kernel_events(append_project_f32, dim3((N + 63) / 64, p.ksplits, p.batch), dim3(64), stream, e0,
                            nullptr, p);
   if (e != hipSuccess) return e;
-  return launch_kernel_events((append_finish<32, 16, kF32>), dim3(p.batch), dim3(64), stream, nullptr, e1, p);
+  return launch_kernel_events((append_finish<32, 16, kF32>), dim3(p.batch), dim3(64 * kFinishWaves), stream, nullptr,
+                              e1, p);
 }
 
 }  // namespace mla
