@@ -111,6 +111,54 @@ def cache_append_time(inp, stream, reps=20, per_graph=20):
             "timing": "HIP events on the launch stream around graph replays of back-to-back calls"}
 
 
+def o_proj_time(inp, stream, reps=10, copies=3):
+    """mla_o_proj (u = W_O [o_1; ...; o_H]) for the workload's batch, bf16,
+    hidden 5120: HIP events on its stream around replays of a graph of calls
+    that rotate over `copies` copies of W_O (168 MB each, together beyond the
+    256 MB Infinity Cache). Not part of the decode step; reported beside it."""
+    import torch
+    import mla_latent_kv_28_amd as mla
+    from mla_synth import make_oproj_inputs
+    d, B = inp.dims, inp.batch
+    o, w_o = make_oproj_inputs(d, B, seed=2)
+    o = o.to("cuda:0")
+    ws = [w_o.to("cuda:0")] + [None] * (copies - 1)
+    for i in range(1, copies):
+        ws[i] = ws[0].clone()
+    out = torch.empty((B, d.hidden), dtype=torch.bfloat16, device="cuda:0")
+    per_graph = 4 * copies
+
+    def call(i):
+        mla.mla_o_proj(d, B, d.hidden, o, ws[i % copies], mla.BF16, out, mla.BF16)
+
+    with torch.cuda.stream(stream):
+        for i in range(copies):
+            call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(per_graph):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+    k = d.num_heads * d.d_v
+    alg = d.hidden * k * 2 + B * k * 2 + B * d.hidden * 2
+    gbps = alg / (us * 1e-6) / 1e9
+    del ws
+    return {"batch": B, "hidden": d.hidden, "k": k, "us_per_call": round(us, 3), "calls_timed": reps * per_graph,
+            "weight_copies_rotated": copies, "algorithmic_bytes": alg, "GBps": round(gbps, 1),
+            "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+            "timing": "HIP events on the launch stream around graph replays of back-to-back calls"}
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle, as it stands, on whole sequences of the same
     workload until about `budget_s` seconds of CPU work have run."""
@@ -326,6 +374,7 @@ def main():
     }
     if inp.dims.hidden == 5120 and not args.eager:
         result["cache_append"] = cache_append_time(inp, stream)
+        result["o_proj"] = o_proj_time(inp, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

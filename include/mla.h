@@ -190,6 +190,22 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
                                 float* lse, mla_stream stream);
 
 /*
+ * Attention output projection (DeepSeek-V2 paper, section 2.1.1: the output
+ * is W_O times the concatenated heads; section 2.1.2: W_UV may be absorbed
+ * into W_O, which this library does not do, as the folded weight would be
+ * d_latent / d_v times larger):
+ *   u[b, :] = W_O [o[b, 0, :]; ...; o[b, H-1, :]]
+ *   o     [B, H, d_v] (the heads' outputs, e.g. from mla_out_proj),
+ *   w_o   [hidden, H * d_v], row-major (head-major columns),
+ *   out   [B, hidden] in out_dtype.
+ * dtype: MLA_BF16 for the DeepSeek-V2 shape (out MLA_BF16 or MLA_F32; hidden a
+ * multiple of 32), MLA_F32 for the tiny shape (out MLA_F32). fp32
+ * accumulation. batch == 0 is a no-op.
+ */
+mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const void* o, const void* w_o,
+                      int32_t dtype, void* out, int32_t out_dtype, mla_stream stream);
+
+/*
  * The cache entry of one new token per sequence (DeepSeek-V2 paper, section
  * 2.1.2: the latent is the down-projection W_DKV h of the token's hidden
  * state; section 2.1.3: the shared rotary key is RoPE(W_KR h) at the token's

@@ -9,7 +9,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["mla_api.cpp", "decode.hip", "gemm.hip", "combine.hip", "append.hip"]
+SOURCES = ["mla_api.cpp", "decode.hip", "gemm.hip", "combine.hip", "append.hip", "oproj.hip"]
 LIB = os.path.join(HERE, "libmla.so")
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 

@@ -285,6 +285,24 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
   return hip_status(mla::launch_combine_outproj_dsv2_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
+mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const void* o, const void* w_o,
+                      int32_t dtype, void* out, int32_t out_dtype, mla_stream stream) {
+  if (dims == nullptr) return MLA_ERR_NULL;
+  if (batch < 0 || hidden <= 0) return MLA_ERR_SHAPE;
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MLA_ERR_DTYPE;
+  const Shape sh = shape_of(dims);
+  if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
+  if (sh == Shape::kDsv2 && (dtype != MLA_BF16 || out_dtype == MLA_FP8_E4M3)) return MLA_ERR_DTYPE;
+  if (sh == Shape::kTiny && (dtype != MLA_F32 || out_dtype != MLA_F32)) return MLA_ERR_DTYPE;
+  const int32_t k = dims->num_heads * dims->d_v;
+  if (sh == Shape::kDsv2 && !mla::oproj_bf16_shape_ok(hidden, k)) return MLA_ERR_SHAPE;
+  if (batch == 0) return MLA_OK;
+  if (!o || !w_o || !out) return MLA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(w_o) || !aligned16(out)) return MLA_ERR_ALIGN;
+  mla::OProjParams p{o, w_o, out, batch, hidden, k};
+  return hip_status(mla::launch_oproj(p, sh == Shape::kDsv2, out_dtype == MLA_F32, static_cast<hipStream_t>(stream)));
+}
+
 int64_t mla_cache_append_workspace(const mla_dims* dims, int32_t batch, int32_t hidden) {
   if (dims == nullptr || batch <= 0 || hidden <= 0) return 0;
   return static_cast<int64_t>(mla::append_slices(hidden)) * batch * (dims->d_latent + dims->d_rope) *

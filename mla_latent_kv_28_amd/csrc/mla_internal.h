@@ -71,6 +71,16 @@ struct AppendParams {
 int append_slices(int hidden);
 hipError_t launch_cache_append(const AppendParams& p, bool dsv2, int cache_kind, hipStream_t s);
 
+// Attention output projection u[b] = W_O o[b] (oproj.hip).
+struct OProjParams {
+  const void* o;      // [B, k] (the heads' outputs, concatenated)
+  const void* w;      // [n, k]
+  void* out;          // [B, n]
+  int32_t batch, n, k;
+};
+bool oproj_bf16_shape_ok(int n, int k);
+hipError_t launch_oproj(const OProjParams& p, bool bf16, bool out_f32, hipStream_t s);
+
 // Per-head batched GEMM: C[b, h, n] = sum_k A[b, h, k] * Bm_h(k, n).
 struct GemmParams {
   const void* a;         // [B, H, lda] (bf16 or f32)

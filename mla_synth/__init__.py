@@ -17,4 +17,5 @@ from .inputs import (  # noqa: F401
     quantise_rows_e4m3,
     AppendInputs,
     make_append_inputs,
+    make_oproj_inputs,
 )

@@ -355,3 +355,15 @@ def make_append_inputs(dims=DSV2, batch=32, seed=0, max_position=4096, with_gain
     return AppendInputs(dims=dims, dtype=store, h=_store(h, store), w_dkv=_store(w_dkv, store),
                         w_kr=_store(w_kr, store), gain=None if gain is None else _store(gain, store),
                         positions=pos.astype(np.int32))
+
+
+def make_oproj_inputs(dims=DSV2, batch=32, seed=0):
+    """Heads' outputs o [B, H, d_v] ~ N(0, 1) and W_O [hidden, H d_v] ~ N(0, 0.006^2)
+    (DeepSeek-V2 shape, bf16) or N(0, 1) / sqrt(H d_v) (tiny, fp32), drawn in
+    that order from default_rng(seed). Returns (o, w_o) host tensors."""
+    rng = np.random.default_rng(seed)
+    k = dims.num_heads * dims.d_v
+    store = "f32" if dims == TINY else "bf16"
+    o = rng.standard_normal((batch, dims.num_heads, dims.d_v))
+    w_o = rng.standard_normal((dims.hidden, k)) * (1.0 / math.sqrt(k) if dims == TINY else 0.006)
+    return _store(o, store), _store(w_o, store)

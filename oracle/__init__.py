@@ -26,3 +26,4 @@ from .mla import (  # noqa: F401
 )
 from .e4m3 import decode_e4m3, encode_e4m3, e4m3_table  # noqa: F401
 from .append import append_entry, quantise_entry, rms_norm, rope  # noqa: F401
+from .output import output_projection  # noqa: F401

@@ -217,3 +217,19 @@ def test_cache_append_argument_errors(L):
     assert f(cache=_cache(row_stride=575, seq_stride=64)) == -2
     assert f(h=P + 2) == -5 and f(work=P + 4) == -5
     assert f(batch=0, h=None, w1=None, w2=None, pos=None, work=None) == 0
+
+
+@no_gpu
+def test_o_proj_argument_errors(L):
+    d = ctypes.byref(DSV2)
+    f = L.mla_o_proj
+    assert f(None, 1, 5120, P, P, mla.BF16, P, mla.BF16, None) == -1
+    assert f(d, -1, 5120, P, P, mla.BF16, P, mla.BF16, None) == -2
+    assert f(d, 1, 5100, P, P, mla.BF16, P, mla.BF16, None) == -2          # 32-feature blocks
+    assert f(d, 1, 5120, P, P, mla.F32, P, mla.BF16, None) == -3
+    assert f(d, 1, 5120, P, P, mla.BF16, P, mla.FP8_E4M3, None) == -3
+    assert f(ctypes.byref(TINY), 1, 128, P, P, mla.BF16, P, mla.F32, None) == -3
+    assert f(ctypes.byref(mla.Dims(8, 512, 64, 128, 128)), 1, 5120, P, P, mla.BF16, P, mla.BF16, None) == -4
+    assert f(d, 1, 5120, None, P, mla.BF16, P, mla.BF16, None) == -1
+    assert f(d, 1, 5120, P, P + 2, mla.BF16, P, mla.BF16, None) == -5
+    assert f(d, 0, 5120, None, None, mla.BF16, None, mla.BF16, None) == 0

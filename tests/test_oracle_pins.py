@@ -391,3 +391,25 @@ def test_quantise_entry_against_library_cast():
     ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     np.testing.assert_array_equal(codes[:3], ref)
     assert np.all((codes[:3] & 0x7F).max(axis=1) == 0x7E)                     # the absmax element is 448
+
+
+# --- the attention output projection -----------------------------------------------
+
+def test_output_projection_brute_force_one_hot_and_absorption():
+    rng = np.random.default_rng(8)
+    B, H, d_v, d_c, hid = 2, 3, 4, 5, 6
+    o, w_o = rng.standard_normal((B, H, d_v)), rng.standard_normal((hid, H * d_v))
+    u = oracle.output_projection(o, w_o)
+    for b in range(B):                              # the definition in plain loops
+        for i in range(hid):
+            ref = sum(w_o[i, h * d_v + j] * o[b, h, j] for h in range(H) for j in range(d_v))
+            assert u[b, i] == pytest.approx(ref, rel=1e-13, abs=1e-13)
+    e = np.zeros((1, H, d_v))                       # one head's feature selects one column
+    e[0, 2, 1] = 1.0
+    np.testing.assert_array_equal(oracle.output_projection(e, w_o)[0], w_o[:, 2 * d_v + 1])
+    # W_UV folded into W_O (V2 2.1.2) gives the same output from the latent outputs
+    w_uv, o_lat = rng.standard_normal((H, d_v, d_c)), rng.standard_normal((B, H, d_c))
+    o2 = np.einsum("hvc,bhc->bhv", w_uv, o_lat)
+    folded = np.concatenate([w_o[:, h * d_v:(h + 1) * d_v] @ w_uv[h] for h in range(H)], axis=1)
+    np.testing.assert_allclose(oracle.output_projection(o2, w_o), o_lat.reshape(B, -1) @ folded.T,
+                               rtol=1e-12, atol=1e-12)
