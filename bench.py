@@ -126,10 +126,11 @@ def o_proj_time(inp, stream, reps=10, copies=3):
     for i in range(1, copies):
         ws[i] = ws[0].clone()
     out = torch.empty((B, d.hidden), dtype=torch.bfloat16, device="cuda:0")
+    work = torch.empty(mla.mla_o_proj_workspace(d, B, d.hidden) // 4, dtype=torch.float32, device="cuda:0")
     per_graph = 4 * copies
 
     def call(i):
-        mla.mla_o_proj(d, B, d.hidden, o, ws[i % copies], mla.BF16, out, mla.BF16)
+        mla.mla_o_proj(d, B, d.hidden, o, ws[i % copies], mla.BF16, out, mla.BF16, work)
 
     with torch.cuda.stream(stream):
         for i in range(copies):

@@ -199,11 +199,16 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
  *   w_o   [hidden, H * d_v], row-major (head-major columns),
  *   out   [B, hidden] in out_dtype.
  * dtype: MLA_BF16 for the DeepSeek-V2 shape (out MLA_BF16 or MLA_F32; hidden a
- * multiple of 32), MLA_F32 for the tiny shape (out MLA_F32). fp32
- * accumulation. batch == 0 is a no-op.
+ * multiple of 256), MLA_F32 for the tiny shape (out MLA_F32). fp32
+ * accumulation, partial sums over 1024-wide K slices added in slice order.
+ * workspace: device memory of at least mla_o_proj_workspace() bytes, 16-byte
+ * aligned, owned by the caller (the DeepSeek-V2 shape; NULL allowed for the
+ * tiny one). batch == 0 is a no-op.
  */
+int64_t mla_o_proj_workspace(const mla_dims* dims, int32_t batch, int32_t hidden);
 mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const void* o, const void* w_o,
-                      int32_t dtype, void* out, int32_t out_dtype, mla_stream stream);
+                      int32_t dtype, void* out, int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                      mla_stream stream);
 
 /*
  * The cache entry of one new token per sequence (DeepSeek-V2 paper, section

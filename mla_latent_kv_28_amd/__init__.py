@@ -23,7 +23,7 @@ _STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DT
 EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
            "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error",
            "mla_time_next_launch",
-           "mla_cache_append", "mla_cache_append_workspace", "mla_o_proj")
+           "mla_cache_append", "mla_cache_append_workspace", "mla_o_proj", "mla_o_proj_workspace")
 
 
 class MLAError(RuntimeError):
@@ -71,8 +71,10 @@ def lib():
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_last_hip_error.argtypes = []
         L.mla_time_next_launch.argtypes = [vp, vp]
-        L.mla_o_proj.argtypes = [pd, i32, i32, vp, vp, i32, vp, i32, vp]
+        L.mla_o_proj.argtypes = [pd, i32, i32, vp, vp, i32, vp, i32, vp, i64, vp]
         L.mla_o_proj.restype = i32
+        L.mla_o_proj_workspace.argtypes = [pd, i32, i32]
+        L.mla_o_proj_workspace.restype = i64
         L.mla_cache_append_workspace.argtypes = [pd, i32, i32]
         L.mla_cache_append_workspace.restype = i64
         L.mla_cache_append.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, f32, f32, vp,
@@ -205,7 +207,13 @@ def mla_combine_out_proj(dims, batch, num_splits, o_part, part_dtype, lse_part, 
     _check(st, "mla_combine_out_proj")
 
 
-def mla_o_proj(dims, batch, hidden, o, w_o, dtype, out, out_dtype, stream=None):
+def mla_o_proj_workspace(dims, batch, hidden):
+    """Bytes of fp32 workspace mla_o_proj needs (0 for the tiny shape)."""
+    d = dims_of(dims)
+    return int(lib().mla_o_proj_workspace(ctypes.byref(d), batch, hidden))
+
+
+def mla_o_proj(dims, batch, hidden, o, w_o, dtype, out, out_dtype, workspace=None, stream=None):
     """u[b] = W_O [o[b, 0]; ...; o[b, H-1]] into out [B, hidden]."""
     d = dims_of(dims)
     k = d.num_heads * d.d_v
@@ -213,6 +221,8 @@ def mla_o_proj(dims, batch, hidden, o, w_o, dtype, out, out_dtype, stream=None):
     st = lib().mla_o_proj(ctypes.byref(d), batch, hidden, _dev(o, "o", t, batch * k),
                           _dev(w_o, "w_o", t, hidden * k), dtype,
                           _dev(out, "out", _TORCH_DTYPE.get(out_dtype), batch * hidden), out_dtype,
+                          _dev(workspace, "workspace"),
+                          workspace.numel() * workspace.element_size() if workspace is not None else 0,
                           _stream(stream))
     _check(st, "mla_o_proj")
 

@@ -285,8 +285,14 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
   return hip_status(mla::launch_combine_outproj_dsv2_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
+int64_t mla_o_proj_workspace(const mla_dims* dims, int32_t batch, int32_t hidden) {
+  if (dims == nullptr || batch <= 0 || hidden <= 0 || shape_of(dims) != Shape::kDsv2) return 0;
+  return mla::oproj_workspace_bytes(batch, hidden, dims->num_heads * dims->d_v);
+}
+
 mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const void* o, const void* w_o,
-                      int32_t dtype, void* out, int32_t out_dtype, mla_stream stream) {
+                      int32_t dtype, void* out, int32_t out_dtype, void* workspace, int64_t workspace_bytes,
+                      mla_stream stream) {
   if (dims == nullptr) return MLA_ERR_NULL;
   if (batch < 0 || hidden <= 0) return MLA_ERR_SHAPE;
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MLA_ERR_DTYPE;
@@ -298,8 +304,12 @@ mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const
   if (sh == Shape::kDsv2 && !mla::oproj_bf16_shape_ok(hidden, k)) return MLA_ERR_SHAPE;
   if (batch == 0) return MLA_OK;
   if (!o || !w_o || !out) return MLA_ERR_NULL;
-  if (!aligned16(o) || !aligned16(w_o) || !aligned16(out)) return MLA_ERR_ALIGN;
-  mla::OProjParams p{o, w_o, out, batch, hidden, k};
+  if (sh == Shape::kDsv2) {
+    if (!workspace) return MLA_ERR_NULL;
+    if (workspace_bytes < mla_o_proj_workspace(dims, batch, hidden)) return MLA_ERR_SHAPE;
+  }
+  if (!aligned16(o) || !aligned16(w_o) || !aligned16(out) || !aligned16(workspace)) return MLA_ERR_ALIGN;
+  mla::OProjParams p{o, w_o, out, static_cast<float*>(workspace), batch, hidden, k};
   return hip_status(mla::launch_oproj(p, sh == Shape::kDsv2, out_dtype == MLA_F32, static_cast<hipStream_t>(stream)));
 }
 

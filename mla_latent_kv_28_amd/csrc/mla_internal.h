@@ -76,9 +76,11 @@ struct OProjParams {
   const void* o;      // [B, k] (the heads' outputs, concatenated)
   const void* w;      // [n, k]
   void* out;          // [B, n]
+  float* work;        // bf16: [k / 1024, B, n] fp32 partial sums
   int32_t batch, n, k;
 };
 bool oproj_bf16_shape_ok(int n, int k);
+int64_t oproj_workspace_bytes(int batch, int n, int k);
 hipError_t launch_oproj(const OProjParams& p, bool bf16, bool out_f32, hipStream_t s);
 
 // Per-head batched GEMM: C[b, h, n] = sum_k A[b, h, k] * Bm_h(k, n).

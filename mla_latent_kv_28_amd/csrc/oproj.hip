@@ -7,14 +7,16 @@
 // library keeps the two products (mla_out_proj / mla_combine_out_proj, then
 // this one).
 //
-// bf16: one workgroup of 16 waves per (32 output features, 32 batch rows),
-// 160 workgroups at d = 5120. K = H d_v goes in batches of 64; wave w takes
-// every sixteenth batch, so the waves read neighbouring pieces of the same
-// weight rows together, and contracts them with MFMA 32x32x16 on operands
-// loaded straight from memory, the next batch requested before the current
-// one is multiplied. The 16 partial tiles are added in wave order through
-// LDS. W_O dominates the bytes (168 MB at d = 5120, H d_v = 16384) and is
-// read once per 32 batch rows.
+// bf16, two kernels:
+//  1. oproj_partial: one 8-wave workgroup per (256 output features, 1024-wide
+//     K slice, 32 batch rows), 320 at d = 5120 and B <= 32. Wave w streams the
+//     slice of its 32 weight rows into registers, two batches of eight k-steps
+//     in flight, while the slice of o sits in LDS (rows padded against bank
+//     conflicts); MFMA 32x32x16; the fp32 tile goes to slice s of the caller's
+//     workspace. All the register space holds weights, which come from HBM.
+//  2. oproj_reduce: adds the slices in order (deterministic) and rounds.
+// W_O dominates the bytes (168 MB at d = 5120, H d_v = 16384); it is read once
+// per 32 batch rows.
 // fp32 (tiny shape): one thread per output feature, plain fma.
 #include <hip/hip_runtime.h>
 
@@ -24,67 +26,77 @@
 namespace mla {
 namespace {
 
-constexpr int kOpWaves = 16;
-constexpr int kOpSteps = 4;   // k-steps of 16 per register buffer
+constexpr int kOpWaves = 8;     // waves per workgroup, 32 output features each
+constexpr int kOpSlice = 1024;  // K per workgroup
+constexpr int kOpSteps = 8;     // k-steps of 16 per register buffer
+constexpr int kOpRow = kOpSlice + 8;   // LDS row of o (elements), padded against bank conflicts
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(64 * kOpWaves) void oproj_bf16(OProjParams p) {
-  __shared__ float tile[kOpWaves][16][64];   // each wave's 32 x 32 fp32 tile, MFMA lane order
+// Partial sums of one K slice: work[slice][b][n].
+__global__ __launch_bounds__(64 * kOpWaves) void oproj_partial(OProjParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 o_lds[32 * kOpRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 31, half = lane >> 5;
-  const int n = blockIdx.x * 32 + r;         // output feature of this lane's B operand
-  const int m = blockIdx.y * 32 + r;         // batch row of this lane's A operand
-  // rows past the batch read row 0 instead: an MFMA row only reaches its own
-  // output row, and those are not stored
-  const __bf16* a_row = (const __bf16*)p.o + (int64_t)(m < p.batch ? m : 0) * p.k + 8 * half;
-  const __bf16* b_row = (const __bf16*)p.w + (int64_t)n * p.k + 8 * half;
+  const int k0 = blockIdx.y * kOpSlice, b0 = blockIdx.z * 32;
+  const int n = blockIdx.x * (32 * kOpWaves) + wave * 32 + r;   // output feature of this lane's B operand
+  const __bf16* b_row = (const __bf16*)p.w + (int64_t)n * p.k + k0 + 8 * half;
   f32x16 acc = {};
-  // K in batches of kBatch; wave w takes batches w, w + 16, ..., so the 16
-  // waves read neighbouring pieces of the same 32 weight rows at a time. Two
-  // register buffers: the next batch is requested before the current one is
-  // multiplied (each wave has an even number of batches).
-  constexpr int kBatch = 16 * kOpSteps;
-  const int nb = p.k / (kOpWaves * kBatch);
-  auto at = [&](int t) { return (t * kOpWaves + wave) * kBatch; };
-  bf16x8 a0[kOpSteps], b0[kOpSteps], a1[kOpSteps], b1[kOpSteps];
-  auto load = [&](bf16x8 (&a)[kOpSteps], bf16x8 (&b)[kOpSteps], int k0) {
+  bf16x8 w0[kOpSteps], w1[kOpSteps];
+  auto load = [&](bf16x8 (&w)[kOpSteps], int s0) {
+#pragma unroll
+    for (int s = 0; s < kOpSteps; ++s) w[s] = *(const bf16x8*)(b_row + 16 * (s0 + s));
+  };
+  load(w0, 0);                       // the weights first: they come from HBM
+  // the slice of o (32 batch rows x kOpSlice) into LDS; rows past the batch are zero
+  for (int e = threadIdx.x; e < 32 * kOpSlice / 8; e += 64 * kOpWaves) {
+    const int row = e / (kOpSlice / 8), c = (e % (kOpSlice / 8)) * 8;
+    const bf16x8 v = b0 + row < p.batch ? *(const bf16x8*)((const __bf16*)p.o + (int64_t)(b0 + row) * p.k + k0 + c)
+                                        : bf16x8{};
+    *(bf16x8*)(o_lds + row * kOpRow + c) = v;
+  }
+  __syncthreads();
+  auto mul = [&](const bf16x8 (&w)[kOpSteps], int s0) {
 #pragma unroll
     for (int s = 0; s < kOpSteps; ++s) {
-      a[s] = *(const bf16x8*)(a_row + k0 + 16 * s);
-      b[s] = *(const bf16x8*)(b_row + k0 + 16 * s);
+      const bf16x8 a = *(const bf16x8*)(o_lds + r * kOpRow + 16 * (s0 + s) + 8 * half);
+      acc = mfma32x32x16(a, w[s], acc);
     }
   };
-  auto mul = [&](const bf16x8 (&a)[kOpSteps], const bf16x8 (&b)[kOpSteps]) {
-#pragma unroll
-    for (int s = 0; s < kOpSteps; ++s) acc = mfma32x32x16(a[s], b[s], acc);
-  };
-  load(a0, b0, at(0));
-  for (int t = 0; t < nb; t += 2) {
-    load(a1, b1, at(t + 1));
+  constexpr int kBatches = kOpSlice / 16 / kOpSteps;   // even
+  for (int t = 0; t < kBatches; t += 2) {
+    load(w1, (t + 1) * kOpSteps);
     __builtin_amdgcn_sched_barrier(0);
-    mul(a0, b0);
+    mul(w0, t * kOpSteps);
     __builtin_amdgcn_sched_barrier(0);
-    load(a0, b0, at(min(t + 2, nb - 1)));   // unconditional: the last pass reloads a batch
+    load(w0, min(t + 2, kBatches - 1) * kOpSteps);   // unconditional: the last pass reloads a batch
     __builtin_amdgcn_sched_barrier(0);
-    mul(a1, b1);
+    mul(w1, (t + 1) * kOpSteps);
     __builtin_amdgcn_sched_barrier(0);
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) tile[wave][i][lane] = acc[i];
-  __syncthreads();
-  if (wave > 0) return;
+  float* out = p.work + (int64_t)blockIdx.y * p.batch * p.n;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kOpWaves; ++w) v += tile[w][i][lane];   // wave order: deterministic
-    const int row = blockIdx.y * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (row < p.batch) {
-      if constexpr (OUT_F32)
-        ((float*)p.out)[(int64_t)row * p.n + n] = v;
-      else
-        ((__bf16*)p.out)[(int64_t)row * p.n + n] = (__bf16)v;
-    }
+    const int row = b0 + 8 * (i >> 2) + 4 * half + (i & 3);   // D[row][col], col = lane % 32
+    if (row < p.batch) out[(int64_t)row * p.n + n] = acc[i];
   }
+}
+
+// out[b][n] = the slices' partial sums added in slice order.
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void oproj_reduce(OProjParams p) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)p.batch * p.n) return;
+  const int slices = p.k / kOpSlice;
+  const int64_t stride = (int64_t)p.batch * p.n;
+  float v[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) v[s] = s < slices ? p.work[s * stride + e] : 0.0f;   // loads together
+  float sum = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) sum += v[s];
+  for (int s = 16; s < slices; ++s) sum += p.work[s * stride + e];
+  if constexpr (OUT_F32)
+    ((float*)p.out)[e] = sum;
+  else
+    ((__bf16*)p.out)[e] = (__bf16)sum;
 }
 
 __global__ __launch_bounds__(128) void oproj_f32(OProjParams p) {
@@ -99,16 +111,22 @@ __global__ __launch_bounds__(128) void oproj_f32(OProjParams p) {
 
 }  // namespace
 
-// k must be a multiple of 16 waves x 2 batches x 16 x kOpSteps for bf16 (each
-// wave an even number of whole batches of k-steps) and n a multiple of 32.
-bool oproj_bf16_shape_ok(int n, int k) { return n % 32 == 0 && k % (kOpWaves * 2 * 16 * kOpSteps) == 0; }
+// bf16: n a multiple of 32 * kOpWaves, k a multiple of kOpSlice.
+bool oproj_bf16_shape_ok(int n, int k) { return n % (32 * kOpWaves) == 0 && k % kOpSlice == 0; }
+
+int64_t oproj_workspace_bytes(int batch, int n, int k) { return (int64_t)(k / kOpSlice) * batch * n * 4; }
 
 hipError_t launch_oproj(const OProjParams& p, bool bf16, bool out_f32, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
   if (!bf16) return launch_kernel(oproj_f32, dim3((p.n + 127) / 128, p.batch), dim3(128), stream, p);
-  const dim3 grid(p.n / 32, (p.batch + 31) / 32);
-  if (out_f32) return launch_kernel(oproj_bf16<true>, grid, dim3(64 * kOpWaves), stream, p);
-  return launch_kernel(oproj_bf16<false>, grid, dim3(64 * kOpWaves), stream, p);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  take_launch_events(&e0, &e1);      // a pending event pair brackets both kernels
+  const hipError_t e = launch_kernel_events(oproj_partial, dim3(p.n / (32 * kOpWaves), p.k / kOpSlice, (p.batch + 31) / 32),
+                                            dim3(64 * kOpWaves), stream, e0, nullptr, p);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(((int64_t)p.batch * p.n + 255) / 256));
+  if (out_f32) return launch_kernel_events(oproj_reduce<true>, grid, dim3(256), stream, nullptr, e1, p);
+  return launch_kernel_events(oproj_reduce<false>, grid, dim3(256), stream, nullptr, e1, p);
 }
 
 }  // namespace mla

@@ -222,14 +222,19 @@ def test_cache_append_argument_errors(L):
 @no_gpu
 def test_o_proj_argument_errors(L):
     d = ctypes.byref(DSV2)
-    f = L.mla_o_proj
-    assert f(None, 1, 5120, P, P, mla.BF16, P, mla.BF16, None) == -1
-    assert f(d, -1, 5120, P, P, mla.BF16, P, mla.BF16, None) == -2
-    assert f(d, 1, 5100, P, P, mla.BF16, P, mla.BF16, None) == -2          # 32-feature blocks
-    assert f(d, 1, 5120, P, P, mla.F32, P, mla.BF16, None) == -3
-    assert f(d, 1, 5120, P, P, mla.BF16, P, mla.FP8_E4M3, None) == -3
-    assert f(ctypes.byref(TINY), 1, 128, P, P, mla.BF16, P, mla.F32, None) == -3
-    assert f(ctypes.byref(mla.Dims(8, 512, 64, 128, 128)), 1, 5120, P, P, mla.BF16, P, mla.BF16, None) == -4
-    assert f(d, 1, 5120, None, P, mla.BF16, P, mla.BF16, None) == -1
-    assert f(d, 1, 5120, P, P + 2, mla.BF16, P, mla.BF16, None) == -5
-    assert f(d, 0, 5120, None, None, mla.BF16, None, mla.BF16, None) == 0
+    ws = mla.mla_o_proj_workspace(DSV2, 2, 5120)
+    assert ws == 16 * 2 * 5120 * 4                   # 1024-wide K slices
+    assert mla.mla_o_proj_workspace(TINY, 2, 128) == 0
+
+    def f(dims=d, batch=2, hidden=5120, o=P, w=P, dtype=mla.BF16, out=P, out_dtype=mla.BF16, work=P, nbytes=ws):
+        return L.mla_o_proj(dims, batch, hidden, o, w, dtype, out, out_dtype, work, nbytes, None)
+    assert f(dims=None) == -1
+    assert f(batch=-1) == -2
+    assert f(hidden=5120 - 32) == -2                  # 256-feature blocks
+    assert f(dtype=mla.F32) == -3 and f(out_dtype=mla.FP8_E4M3) == -3
+    assert f(dims=ctypes.byref(TINY), hidden=128, dtype=mla.BF16, out_dtype=mla.F32) == -3
+    assert f(dims=ctypes.byref(mla.Dims(8, 512, 64, 128, 128))) == -4
+    assert f(o=None) == -1 and f(work=None) == -1
+    assert f(nbytes=ws - 4) == -2
+    assert f(w=P + 2) == -5 and f(work=P + 4) == -5
+    assert f(batch=0, o=None, w=None, out=None, work=None) == 0

@@ -30,7 +30,9 @@ def _run(dims, batch, out_dtype, seed):
     dt = mla.F32 if dims == TINY else mla.BF16
     t = torch.float32 if out_dtype == mla.F32 else torch.bfloat16
     out = torch.full((batch, dims.hidden), float("nan"), dtype=t, device="cuda")
-    mla.mla_o_proj(dims, batch, dims.hidden, o.cuda(), w_o.cuda(), dt, out, out_dtype)
+    nws = mla.mla_o_proj_workspace(dims, batch, dims.hidden)
+    ws = torch.empty(max(nws // 4, 1), dtype=torch.float32, device="cuda") if nws else None
+    mla.mla_o_proj(dims, batch, dims.hidden, o.cuda(), w_o.cuda(), dt, out, out_dtype, ws)
     torch.cuda.synchronize()
     ref = oracle.output_projection(o.double().numpy(), w_o.double().numpy())
     return out.double().cpu().numpy(), ref
