@@ -10,8 +10,9 @@
 // bf16, two kernels:
 //  1. oproj_partial: one 8-wave workgroup per (256 output features, 1024-wide
 //     K slice, 32 batch rows), 320 at d = 5120 and B <= 32. Wave w streams the
-//     slice of its 32 weight rows into registers, two batches of eight k-steps
-//     in flight, while the slice of o sits in LDS (rows padded against bank
+//     slice of its 32 weight rows through three register buffers of eight
+//     k-steps (two in flight while one is multiplied), while the slice of o
+//     sits in LDS (rows padded against bank
 //     conflicts); MFMA 32x32x16; the fp32 tile goes to slice s of the caller's
 //     workspace. All the register space holds weights, which come from HBM.
 //  2. oproj_reduce: adds the slices in order (deterministic) and rounds.
@@ -39,12 +40,16 @@ __global__ __launch_bounds__(64 * kOpWaves) void oproj_partial(OProjParams p) {
   const int n = blockIdx.x * (32 * kOpWaves) + wave * 32 + r;   // output feature of this lane's B operand
   const __bf16* b_row = (const __bf16*)p.w + (int64_t)n * p.k + k0 + 8 * half;
   f32x16 acc = {};
-  bf16x8 w0[kOpSteps], w1[kOpSteps];
-  auto load = [&](bf16x8 (&w)[kOpSteps], int s0) {
+  constexpr int kBatches = kOpSlice / 16 / kOpSteps;
+  // three register buffers: two batches of weights stay in flight while one is
+  // multiplied (the loop is unrolled, so every buffer index is a constant)
+  bf16x8 w[3][kOpSteps];
+  auto load = [&](bf16x8 (&u)[kOpSteps], int s0) {
 #pragma unroll
-    for (int s = 0; s < kOpSteps; ++s) w[s] = *(const bf16x8*)(b_row + 16 * (s0 + s));
+    for (int s = 0; s < kOpSteps; ++s) u[s] = *(const bf16x8*)(b_row + 16 * (s0 + s));
   };
-  load(w0, 0);                       // the weights first: they come from HBM
+  load(w[0], 0);                     // the weights first: they come from HBM
+  load(w[1], kOpSteps);
   // the slice of o (32 batch rows x kOpSlice) into LDS; rows past the batch are zero
   for (int e = threadIdx.x; e < 32 * kOpSlice / 8; e += 64 * kOpWaves) {
     const int row = e / (kOpSlice / 8), c = (e % (kOpSlice / 8)) * 8;
@@ -53,22 +58,15 @@ __global__ __launch_bounds__(64 * kOpWaves) void oproj_partial(OProjParams p) {
     *(bf16x8*)(o_lds + row * kOpRow + c) = v;
   }
   __syncthreads();
-  auto mul = [&](const bf16x8 (&w)[kOpSteps], int s0) {
+#pragma unroll
+  for (int t = 0; t < kBatches; ++t) {
+    if (t + 2 < kBatches) load(w[(t + 2) % 3], (t + 2) * kOpSteps);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < kOpSteps; ++s) {
-      const bf16x8 a = *(const bf16x8*)(o_lds + r * kOpRow + 16 * (s0 + s) + 8 * half);
-      acc = mfma32x32x16(a, w[s], acc);
+      const bf16x8 a = *(const bf16x8*)(o_lds + r * kOpRow + 16 * (t * kOpSteps + s) + 8 * half);
+      acc = mfma32x32x16(a, w[t % 3][s], acc);
     }
-  };
-  constexpr int kBatches = kOpSlice / 16 / kOpSteps;   // even
-  for (int t = 0; t < kBatches; t += 2) {
-    load(w1, (t + 1) * kOpSteps);
-    __builtin_amdgcn_sched_barrier(0);
-    mul(w0, t * kOpSteps);
-    __builtin_amdgcn_sched_barrier(0);
-    load(w0, min(t + 2, kBatches - 1) * kOpSteps);   // unconditional: the last pass reloads a batch
-    __builtin_amdgcn_sched_barrier(0);
-    mul(w1, (t + 1) * kOpSteps);
     __builtin_amdgcn_sched_barrier(0);
   }
   float* out = p.work + (int64_t)blockIdx.y * p.batch * p.n;
