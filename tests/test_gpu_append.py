@@ -145,3 +145,31 @@ def test_dsv2_full_batch_128_and_deterministic():
     _check_dense(s1, idx, inp, 2.0 ** -8, 1e-4)
     s2, _ = _run(inp, "bf16")
     assert torch.equal(s1[0].view(torch.int16), s2[0].view(torch.int16))
+
+
+def test_append_then_decode_reads_the_new_token():
+    # a token appended on the GPU is read by the decode that follows: the
+    # oracle's cache gets the oracle's own entry (rounded to the stored bf16)
+    import dataclasses
+    import mla_latent_kv_28_amd as mla
+    from mla_latent_kv_28_amd.pipeline import DecodePipeline
+    from mla_synth import make_inputs, oracle_args
+    lens = np.array([300, 77], dtype=np.int32)
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=lens.tolist(), seq_stride=320, pad_fill=float("nan"))
+    a = make_append_inputs(DSV2, batch=2, seed=9, positions=lens.tolist())
+    grown = dataclasses.replace(inp, seq_lens=lens + 1)
+    pipe = DecodePipeline(grown, num_splits=2, device="cuda:0")
+    ws = torch.empty(mla.mla_cache_append_workspace(DSV2, 2, DSV2.hidden) // 4, dtype=torch.float32, device="cuda")
+    mla.mla_cache_append(DSV2, 2, DSV2.hidden, a.h.cuda(), a.w_dkv.cuda(), a.w_kr.cuda(), None, mla.BF16, a.eps,
+                         a.base, torch.from_numpy(a.positions).cuda(), pipe.cache, ws)
+    out, _ = pipe.run()
+    torch.cuda.synchronize()
+    c_ref, k_ref = _reference(a)
+    rows = inp.rows.clone()
+    for b in range(2):
+        rows[b * 320 + int(lens[b])] = torch.from_numpy(np.concatenate([c_ref[b], k_ref[b]])).to(torch.bfloat16)
+    ref, _ = oracle.decode(**oracle_args(dataclasses.replace(grown, rows=rows)))
+    got = out.double().cpu().numpy()
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    print("append then decode: rel_l2 %.3e" % rel, flush=True)
+    assert np.all(np.isfinite(got)) and rel <= 1e-2
