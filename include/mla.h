@@ -199,7 +199,7 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
  *   w_o   [hidden, H * d_v], row-major (head-major columns),
  *   out   [B, hidden] in out_dtype.
  * dtype: MLA_BF16 for the DeepSeek-V2 shape (out MLA_BF16 or MLA_F32; hidden a
- * multiple of 256), MLA_F32 for the tiny shape (out MLA_F32). fp32
+ * multiple of 32), MLA_F32 for the tiny shape (out MLA_F32). fp32
  * accumulation, partial sums over 1024-wide K slices added in slice order.
  * workspace: device memory of at least mla_o_proj_workspace() bytes, 16-byte
  * aligned, owned by the caller (the DeepSeek-V2 shape; NULL allowed for the

@@ -8,8 +8,9 @@
 // this one).
 //
 // bf16, two kernels:
-//  1. oproj_partial: one 8-wave workgroup per (256 output features, 1024-wide
-//     K slice, 32 batch rows), 320 at d = 5120 and B <= 32. Wave w streams the
+//  1. oproj_partial: one workgroup of 5 waves per (160 output features,
+//     1024-wide K slice, 32 batch rows), 512 at d = 5120 and B <= 32 (8, 4 or
+//     1 waves where 160 does not divide the features). Wave w streams the
 //     slice of its 32 weight rows through three register buffers of eight
 //     k-steps (two in flight while one is multiplied), while the slice of o
 //     sits in LDS (rows padded against bank
@@ -27,17 +28,18 @@
 namespace mla {
 namespace {
 
-constexpr int kOpWaves = 8;     // waves per workgroup, 32 output features each
 constexpr int kOpSlice = 1024;  // K per workgroup
 constexpr int kOpSteps = 8;     // k-steps of 16 per register buffer
 constexpr int kOpRow = kOpSlice + 8;   // LDS row of o (elements), padded against bank conflicts
 
 // Partial sums of one K slice: work[slice][b][n].
-__global__ __launch_bounds__(64 * kOpWaves) void oproj_partial(OProjParams p) {
+// WAVES waves per workgroup, 32 output features each.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void oproj_partial(OProjParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 o_lds[32 * kOpRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 31, half = lane >> 5;
   const int k0 = blockIdx.y * kOpSlice, b0 = blockIdx.z * 32;
-  const int n = blockIdx.x * (32 * kOpWaves) + wave * 32 + r;   // output feature of this lane's B operand
+  const int n = blockIdx.x * (32 * WAVES) + wave * 32 + r;   // output feature of this lane's B operand
   const __bf16* b_row = (const __bf16*)p.w + (int64_t)n * p.k + k0 + 8 * half;
   f32x16 acc = {};
   constexpr int kBatches = kOpSlice / 16 / kOpSteps;
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(64 * kOpWaves) void oproj_partial(OProjParams p) {
   load(w[0], 0);                     // the weights first: they come from HBM
   load(w[1], kOpSteps);
   // the slice of o (32 batch rows x kOpSlice) into LDS; rows past the batch are zero
-  for (int e = threadIdx.x; e < 32 * kOpSlice / 8; e += 64 * kOpWaves) {
+  for (int e = threadIdx.x; e < 32 * kOpSlice / 8; e += 64 * WAVES) {
     const int row = e / (kOpSlice / 8), c = (e % (kOpSlice / 8)) * 8;
     const bf16x8 v = b0 + row < p.batch ? *(const bf16x8*)((const __bf16*)p.o + (int64_t)(b0 + row) * p.k + k0 + c)
                                         : bf16x8{};
@@ -109,8 +111,8 @@ __global__ __launch_bounds__(128) void oproj_f32(OProjParams p) {
 
 }  // namespace
 
-// bf16: n a multiple of 32 * kOpWaves, k a multiple of kOpSlice.
-bool oproj_bf16_shape_ok(int n, int k) { return n % (32 * kOpWaves) == 0 && k % kOpSlice == 0; }
+// bf16: n a multiple of 32, k a multiple of kOpSlice.
+bool oproj_bf16_shape_ok(int n, int k) { return n % 32 == 0 && k % kOpSlice == 0; }
 
 int64_t oproj_workspace_bytes(int batch, int n, int k) { return (int64_t)(k / kOpSlice) * batch * n * 4; }
 
@@ -119,8 +121,19 @@ hipError_t launch_oproj(const OProjParams& p, bool bf16, bool out_f32, hipStream
   if (!bf16) return launch_kernel(oproj_f32, dim3((p.n + 127) / 128, p.batch), dim3(128), stream, p);
   hipEvent_t e0 = nullptr, e1 = nullptr;
   take_launch_events(&e0, &e1);      // a pending event pair brackets both kernels
-  const hipError_t e = launch_kernel_events(oproj_partial, dim3(p.n / (32 * kOpWaves), p.k / kOpSlice, (p.batch + 31) / 32),
-                                            dim3(64 * kOpWaves), stream, e0, nullptr, p);
+  // Workgroups of 5 waves (160 features) where they divide the features:
+  // at d = 5120 that makes 32 x 16 = 512 workgroups, two per compute unit in
+  // one round (8-wave workgroups left 64 units with two of 320); else 8, 4 or 1.
+  const dim3 g0(0, p.k / kOpSlice, (p.batch + 31) / 32);
+  hipError_t e;
+  if (p.n % 160 == 0)
+    e = launch_kernel_events(oproj_partial<5>, dim3(p.n / 160, g0.y, g0.z), dim3(320), stream, e0, nullptr, p);
+  else if (p.n % 256 == 0)
+    e = launch_kernel_events(oproj_partial<8>, dim3(p.n / 256, g0.y, g0.z), dim3(512), stream, e0, nullptr, p);
+  else if (p.n % 128 == 0)
+    e = launch_kernel_events(oproj_partial<4>, dim3(p.n / 128, g0.y, g0.z), dim3(256), stream, e0, nullptr, p);
+  else
+    e = launch_kernel_events(oproj_partial<1>, dim3(p.n / 32, g0.y, g0.z), dim3(64), stream, e0, nullptr, p);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(((int64_t)p.batch * p.n + 255) / 256));
   if (out_f32) return launch_kernel_events(oproj_reduce<true>, grid, dim3(256), stream, nullptr, e1, p);

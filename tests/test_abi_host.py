@@ -230,7 +230,7 @@ def test_o_proj_argument_errors(L):
         return L.mla_o_proj(dims, batch, hidden, o, w, dtype, out, out_dtype, work, nbytes, None)
     assert f(dims=None) == -1
     assert f(batch=-1) == -2
-    assert f(hidden=5120 - 32) == -2                  # 256-feature blocks
+    assert f(hidden=5120 - 16) == -2                  # 32-feature blocks
     assert f(dtype=mla.F32) == -3 and f(out_dtype=mla.FP8_E4M3) == -3
     assert f(dims=ctypes.byref(TINY), hidden=128, dtype=mla.BF16, out_dtype=mla.F32) == -3
     assert f(dims=ctypes.byref(mla.Dims(8, 512, 64, 128, 128))) == -4

@@ -56,6 +56,16 @@ def test_dsv2_bf16_out():
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4)
 
 
+@pytest.mark.parametrize("hidden", [4096, 2048 + 128, 1024 + 32])
+def test_dsv2_other_widths(hidden):
+    # the 8-, 4- and 1-wave workgroups (160 does not divide these widths)
+    import dataclasses
+    import mla_latent_kv_28_amd as mla
+    d = dataclasses.replace(DSV2, hidden=hidden)
+    got, ref = _run(d, 7, mla.F32, seed=hidden)
+    assert _rel(got, ref) <= 1e-5
+
+
 def test_tiny_f32():
     import mla_latent_kv_28_amd as mla
     got, ref = _run(TINY, 3, mla.F32, seed=4)
