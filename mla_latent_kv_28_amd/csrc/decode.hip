@@ -219,18 +219,17 @@ __device__ __forceinline__ void issue_tile(const DecodeParams& p, const SeqView&
     if (consecutive && tile_base + C::T <= end) {
       const int64_t rs = p.row_stride * C::ESZ;
       const char* tile = (const char*)p.latent + tr.row(0) * rs;
+      const auto res = buffer_rsrc(tile, (uint32_t)(C::T * rs));   // rows are at most 2^24 bytes apart
       const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
       static_assert(C::WAVES == 4, "row 4k + wave has swizzle key (wave << 2) | (k & 3)");
       // rotary keys: 8 lanes per row, one instruction for the whole tile
       static_assert(C::T * C::ROPE_CH == C::THREADS, "one rotary chunk per thread");
-      load16_to_lds(tile + (uint32_t)dma.rope, buf + C::LAT_BYTES + wave * 64 * 16);
-      // latent rows wave, wave + 4, ...: one scalar row pointer stepped by 4 rows
-      const char* row = tile + wave * rs;
+      buf_load16_to_lds(res, (uint32_t)dma.rope, 0u, buf + C::LAT_BYTES + wave * 64 * 16);
+      // latent rows wave, wave + 4, ...
       MLA_LDS char* dst = buf + wave * (C::DC * C::ESZ);
 #pragma unroll
       for (int k = 0; k < C::T / C::WAVES; ++k) {
-        load16_to_lds(row + (uint32_t)(dma.lat ^ (16 * (k & 3))), dst);
-        row += C::WAVES * rs;
+        buf_load16_to_lds(res, (uint32_t)(dma.lat ^ (16 * (k & 3))), (uint32_t)((k * C::WAVES + wave) * rs), dst);
         dst += C::WAVES * (C::DC * C::ESZ);
       }
       return;
@@ -375,6 +374,7 @@ __device__ __forceinline__ void stage_q_issue(const DecodeParams& p, int b, int 
   using Q = QStage<C>;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const char* rows = (const char*)p.q_lat + ((int64_t)b * C::H + 32 * wave) * (C::W * 2) + half * Q::HALF * 16;
+  const auto res = buffer_rsrc(rows, 32 * (C::W * 2));
   // LDS chunk 64 i + lane holds padded row r, chunk c; stepping i moves the
   // position by 64 = STEP_R rows + STEP_C chunks
   constexpr int STEP_R = 64 / Q::PITCH, STEP_C = 64 % Q::PITCH;
@@ -383,7 +383,7 @@ __device__ __forceinline__ void stage_q_issue(const DecodeParams& p, int b, int 
   for (int i = 0; i < Q::LOADS; ++i) {
     const uint32_t off = r * (C::W * 2) + min(c, Q::HALF - 1) * 16;   // the pad re-reads a real chunk
     if (Q::CHUNKS % 64 == 0 || i + 1 < Q::LOADS || lane < Q::CHUNKS - 64 * (Q::LOADS - 1))
-      load16_to_lds(rows + off, region + 64 * 16 * i);
+      buf_load16_to_lds(res, off, 0u, region + 64 * 16 * i);
     r += STEP_R;
     c += STEP_C;
     if (c >= Q::PITCH) { c -= Q::PITCH; r += 1; }
@@ -871,7 +871,7 @@ struct TileBase {
 // row, so every tile costs every thread the same nine loads.
 template <class C>
 struct StreamTile {
-  const char* tile;
+  __amdgpu_buffer_rsrc_t res;   // the tile's 32 rows
   int last, rs;
   template <bool PAGED>
   __device__ __forceinline__ StreamTile(const DecodeParams& p, const TileBase& tbase, int t, int ntiles, int start,
@@ -879,23 +879,25 @@ struct StreamTile {
     const int tb = start + min(t, ntiles - 1) * C::T;
     last = min(end - tb, C::T) - 1;
     rs = (int)(p.row_stride * C::ESZ);
+    const char* tile;
     if constexpr (PAGED) {
       const int64_t pg = __builtin_amdgcn_readlane(tbase.pages, (tb >> tbase.shift) - tbase.lp0);
       tile = tbase.base + ((pg << tbase.shift) + (tb & ((1 << tbase.shift) - 1))) * rs;
     } else {
       tile = tbase.base + (int64_t)tb * rs;
     }
+    res = buffer_rsrc(tile, (uint32_t)(C::T * rs));   // rows are at most 2^24 bytes apart
   }
   // latent row 4k + wave (one 1 KiB row per wave instruction)
   __device__ __forceinline__ void latent(const DmaOffs& dma, MLA_LDS char* fill, int wave, int k) const {
     const int row = min(k * C::WAVES + wave, last);
-    load16_to_lds(tile + row * rs + (uint32_t)(dma.lat ^ (16 * (k & 3))),
-                  fill + (k * C::WAVES + wave) * (C::DC * C::ESZ));
+    buf_load16_to_lds(res, (uint32_t)(dma.lat ^ (16 * (k & 3))), (uint32_t)(row * rs),
+                      fill + (k * C::WAVES + wave) * (C::DC * C::ESZ));
   }
   // rotary parts: 8 lanes per row, rows tid / 8
   __device__ __forceinline__ void rope(const DmaOffs& dma, MLA_LDS char* fill, int wave) const {
     const int row = min((int)(threadIdx.x >> 3), last);
-    load16_to_lds(tile + (uint32_t)(row * rs + dma.rope_chunk), fill + C::LAT_BYTES + wave * 64 * 16);
+    buf_load16_to_lds(res, (uint32_t)(row * rs + dma.rope_chunk), 0u, fill + C::LAT_BYTES + wave * 64 * 16);
   }
   __device__ __forceinline__ void all(const DmaOffs& dma, MLA_LDS char* fill, int wave) const {
 #pragma unroll
@@ -955,20 +957,22 @@ struct E4m3Tile {
     asm volatile("" : "+v"(lane));
     const int r0 = 8 * wave + 2 * k, rs = (int)p.row_stride;
     const int step = r0 + 1 <= last ? rs : 0;
-    const char* row = (const char*)p.latent + (row0 + min(r0, last)) * p.row_stride;
-    load16_to_lds(row + (uint32_t)((lane >> 5) * step + 16 * (lane & 31)), land + (4 * wave + k) * 1024);
+    const auto res = buffer_rsrc((const char*)p.latent + row0 * p.row_stride, (uint32_t)(C::T * rs));
+    buf_load16_to_lds(res, (uint32_t)((lane >> 5) * step + 16 * (lane & 31)), (uint32_t)(min(r0, last) * rs),
+                      land + (4 * wave + k) * 1024);
   }
   __device__ __forceinline__ void issue_scales(MLA_LDS char* land, int wave) const {
     const int row = min(8 * wave + (int)(threadIdx.x & 7), last);
-    __builtin_amdgcn_global_load_lds((const char*)(p.scale + row0) + (uint32_t)(4 * row),
-                                     land + E4m3Ring<C>::CODES + wave * 256, 4, 0, 0);
+    const auto res = buffer_rsrc(p.scale + row0, (uint32_t)(C::T * 4));
+    buf_load4_to_lds(res, (uint32_t)(4 * row), 0u, land + E4m3Ring<C>::CODES + wave * 256);
   }
   // rotary parts into the slot, as the 16-bit loader places them
   __device__ __forceinline__ void issue_rope(const DmaOffs& dma, MLA_LDS char* slot, int wave) const {
     const int row = min((int)(threadIdx.x >> 3), last);
-    const char* r = (const char*)p.rope + row0 * (p.rope_stride * 2);
-    load16_to_lds(r + (uint32_t)(row * (int)(p.rope_stride * 2) + (dma.rope_chunk - C::DC * C::ESZ)),
-                  slot + C::LAT_BYTES + wave * 64 * 16);
+    const int rs2 = (int)(p.rope_stride * 2);
+    const auto res = buffer_rsrc((const char*)p.rope + row0 * (p.rope_stride * 2), (uint32_t)(C::T * rs2));
+    buf_load16_to_lds(res, (uint32_t)(row * rs2 + (dma.rope_chunk - C::DC * C::ESZ)), 0u,
+                      slot + C::LAT_BYTES + wave * 64 * 16);
   }
 };
 

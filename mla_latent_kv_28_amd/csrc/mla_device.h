@@ -72,6 +72,26 @@ __device__ __forceinline__ void load16_to_lds(const void* gptr, MLA_LDS void* ld
   __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
 }
 
+// Raw buffer resource over [base, base + bytes) (gfx9 descriptor word 3;
+// reads past the end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Direct buffer -> LDS loads (the MUBUF form of the direct-to-LDS load): lane
+// i's SIZE bytes from base + soff + voff land at lds_base + SIZE * i. The
+// compiler counts these on the vector-memory counter only, so LDS reads issued
+// after them keep their own in-order waits; with the global (FLAT-encoded)
+// form in flight it waits for every outstanding LDS read at each use.
+__device__ __forceinline__ void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                  MLA_LDS void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf_load4_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                                 MLA_LDS void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 4, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Transposing LDS read: within each 16-lane group, lane 4*a + x receives

@@ -154,12 +154,19 @@ def decode(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale):
     return o, lse
 
 
-def decode_one(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, h):
-    """One (sequence, head) output of `decode`, for sampled checks at full size."""
+def decode_heads(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, heads):
+    """Outputs of `decode` for sequence b and the listed heads only:
+    o [len(heads), d_v], lse [len(heads)] (one gather of the sequence's rows,
+    the same attention restricted to those heads). For checks at full size."""
+    hs = np.asarray(heads, dtype=np.int64).reshape(-1)
     c_kv, k_rope = gather_rows(cache, b, int(seq_lens[b]))
-    o, lse = attend_nonabsorbed(c_kv, k_rope, _f64(q_nope)[b, h:h + 1],
-                                _f64(q_rope)[b, h:h + 1], _f64(w_uk)[h:h + 1],
-                                _f64(w_uv)[h:h + 1], sm_scale)
+    return attend_nonabsorbed(c_kv, k_rope, _f64(q_nope)[b, hs], _f64(q_rope)[b, hs],
+                              _f64(w_uk)[hs], _f64(w_uv)[hs], sm_scale)
+
+
+def decode_one(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, h):
+    """One (sequence, head) output of `decode`: (o [d_v], lse)."""
+    o, lse = decode_heads(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, [h])
     return o[0], lse[0]
 
 

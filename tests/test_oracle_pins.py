@@ -233,6 +233,108 @@ def test_paged_and_contiguous_layouts_agree():
     np.testing.assert_array_equal(l1, l2)
 
 
+def _glue_case(rng, lens, H=3, d_c=12, d_nope=8, d_r=6, d_v=10):
+    """A small batch whose every sequence has its own rows and its own query,
+    so that an indexing slip (a sequence reading another's rows, or another's
+    query) changes the result."""
+    B = len(lens)
+    return dict(
+        q_nope=rng.standard_normal((B, H, d_nope)),
+        q_rope=rng.standard_normal((B, H, d_r)),
+        w_uk=rng.standard_normal((H, d_nope, d_c)) / math.sqrt(d_c),
+        w_uv=rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c),
+        sm_scale=1.0 / math.sqrt(d_nope + d_r),
+    ), d_c, d_r
+
+
+def test_batched_decode_equals_attention_on_hand_sliced_rows():
+    # oracle.decode is glue: gather each sequence's rows, attend with that
+    # sequence's query. Rows are placed by hand here (contiguous: sequence b at
+    # rows b * stride ..; paged: pages taken from a hand-written table) and the
+    # attention of each sequence is taken on exactly those rows.
+    rng = np.random.default_rng(31)
+    lens = [5, 0, 9, 1]
+    args, d_c, d_r = _glue_case(rng, lens)
+    stride = 11
+    rows = np.full((len(lens) * stride, d_c + d_r), np.nan)
+    per_seq = []
+    for b, L in enumerate(lens):
+        r = rng.standard_normal((L, d_c + d_r))
+        rows[b * stride: b * stride + L] = r
+        per_seq.append(r)
+    page = 4
+    table = np.array([[6, 1, 9], [0, 0, 0], [3, 8, 5], [2, 0, 0]], dtype=np.int32)
+    pool = np.full((10 * page, d_c + d_r), np.nan)
+    for b, L in enumerate(lens):
+        for j in range(L):
+            pool[table[b, j // page] * page + j % page] = per_seq[b][j]
+    caches = [dict(kind="dense", d_c=d_c, rows=rows, seq_stride=stride),
+              dict(kind="dense", d_c=d_c, rows=pool, block_table=table, page_size=page)]
+    for cache in caches:
+        o, lse = oracle.decode(cache=cache, seq_lens=np.array(lens), **args)
+        for b, L in enumerate(lens):
+            r = per_seq[b]
+            ref_o, ref_l = oracle.attend_nonabsorbed(r[:, :d_c], r[:, d_c:], args["q_nope"][b],
+                                                     args["q_rope"][b], args["w_uk"], args["w_uv"],
+                                                     args["sm_scale"])
+            np.testing.assert_array_equal(o[b], ref_o)
+            np.testing.assert_array_equal(lse[b], ref_l)
+        assert np.all(o[1] == 0) and np.all(lse[1] == -np.inf)
+        # every sequence's result differs from the others' (distinct queries and rows)
+        for b in (0, 2, 3):
+            for c in (0, 2, 3):
+                if b != c:
+                    assert not np.allclose(o[b], o[c])
+
+
+def test_decode_one_and_heads_equal_batched_decode():
+    # the single-(sequence, head) and head-subset forms used for the checks at
+    # full size give the same values as the batched call, head by head
+    rng = np.random.default_rng(32)
+    lens = [7, 3, 12]
+    args, d_c, d_r = _glue_case(rng, lens, H=4)
+    stride = 12
+    rows = rng.standard_normal((len(lens) * stride, d_c + d_r))
+    cache = dict(kind="dense", d_c=d_c, rows=rows, seq_stride=stride)
+    o, lse = oracle.decode(cache=cache, seq_lens=np.array(lens), **args)
+    for b in range(len(lens)):
+        for h in range(4):
+            o1, l1 = oracle.decode_one(cache=cache, seq_lens=np.array(lens), b=b, h=h, **args)
+            np.testing.assert_allclose(o1, o[b, h], rtol=1e-13, atol=1e-15)
+            assert abs(l1 - lse[b, h]) <= 1e-13 * max(1.0, abs(lse[b, h]))
+        hs = [3, 0, 2]
+        oh, lh = oracle.decode_heads(cache=cache, seq_lens=np.array(lens), b=b, heads=hs, **args)
+        np.testing.assert_allclose(oh, o[b, hs], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(lh, lse[b, hs], rtol=1e-13, atol=0)
+
+
+def test_fp8_cache_gather_equals_dense_cache_of_library_decoded_codes():
+    # the e4m3 branch of the gather (codes decoded by the oracle's own table,
+    # times the per-token scale) against a dense cache whose latent values come
+    # from torch's float8_e4m3fn -> float32 conversion, times the scale in float64
+    rng = np.random.default_rng(33)
+    lens = [6, 9]
+    args, d_c, d_r = _glue_case(rng, lens)
+    R = 20
+    codes = rng.integers(0, 256, size=(R, d_c)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C          # no NaN codes
+    scale = (rng.random(R) * 0.02 + 1e-3).astype(np.float32)
+    rope = rng.standard_normal((R, d_r)).astype(np.float32)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    dense_rows = np.concatenate([lib * scale.astype(np.float64)[:, None], rope], axis=1)
+    fp8 = dict(kind="fp8", d_c=d_c, codes=codes, scale=scale, rope=rope, seq_stride=10)
+    dense = dict(kind="dense", d_c=d_c, rows=dense_rows, seq_stride=10)
+    for b, L in enumerate(lens):
+        c8, r8 = oracle.gather_rows(fp8, b, L)
+        cd, rd = oracle.gather_rows(dense, b, L)
+        np.testing.assert_array_equal(c8, cd)
+        np.testing.assert_array_equal(r8, rd)
+    o8, l8 = oracle.decode(cache=fp8, seq_lens=np.array(lens), **args)
+    od, ld = oracle.decode(cache=dense, seq_lens=np.array(lens), **args)
+    np.testing.assert_array_equal(o8, od)
+    np.testing.assert_array_equal(l8, ld)
+
+
 def test_token_rows_paged_mapping():
     bt = np.array([[5, 2, 7], [0, 1, 3]], dtype=np.int32)
     rows = oracle.mla.token_rows(0, 10, block_table=bt, page_size=4)
