@@ -60,9 +60,6 @@ struct Cfg {
   static constexpr int P_BYTES = HB * 32 * PROW;
   static constexpr int NKC_LAT = DC / 16, NKC_ROPE = DR / 16, NKC = NKC_LAT + NKC_ROPE;
   static constexpr int LDS_BYTES = NBUF * BUF_BYTES + 2 * P_BYTES;
-  // bf16 output rows staged in the tile ring (row stride padded by 16 bytes)
-  static constexpr int OROW = DC * 2 + 16;
-  static constexpr bool OUT_STAGE = !F32 && DC * 2 == 64 * 16 && H * OROW <= NBUF * BUF_BYTES;
   static_assert(DC % (32 * WAVES) == 0 && DR % 16 == 0, "head shape");
   static_assert(FPW % 128 == 0 || F32, "a wave's feature slice starts on a swizzle period");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -418,6 +415,10 @@ struct State {
 // split is recomputed with the true maximum as reference.
 constexpr float kHeadroom = 64.0f;
 
+// Byte offset of the per-wave overflow flags in the buffer that holds the
+// softmax denominators at the end of a pass (after 128 floats).
+constexpr int kFinFlags = 512;
+
 // Raw scores of one tile for this wave's 32 heads: lane (hh, c) holds tokens
 // 8j + 4hh + i (accumulator 4j + i) of head 32*wave + c. The e4m3 cache keeps
 // the latent part apart: it still has to be multiplied by the token's scale.
@@ -723,6 +724,15 @@ __device__ __forceinline__ float lane32_partner(float v) {
   // lanes 0..31 find the upper half's value in the second result, lanes
   // 32..63 the lower half's in the first
   return __builtin_bit_cast(float, (uint32_t)((threadIdx.x & 32) ? sw[0] : sw[1]));
+}
+
+// Exchange between the two halves of the wave: lane r + 32's `lo` becomes
+// lane r's `hi`, and lane r's `hi` becomes lane r + 32's `lo`
+// (v_permlane32_swap of `lo` in the upper half with `hi` in the lower half).
+__device__ __forceinline__ void swap_lane_halves(uint32_t& lo, uint32_t& hi) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+  lo = sw[0];
+  hi = sw[1];
 }
 
 // The 32 latent-sum MFMAs of one tile, m = 0..31 (k step u = m / 16, head
@@ -1282,6 +1292,22 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   constexpr int LPT = loads_per_tile<C>();
   if constexpr (!PAGED) tbase.base = (const char*)p.latent + sv.seq_row * (p.row_stride * C::ESZ);
   auto pslot = [&](int x) -> MLA_LDS char* { return pbase + (x & 1) * C::P_BYTES; };
+  // End of a pass over the split. The last step left the P^T buffer
+  // pslot(ntiles) free: every wave writes its heads' softmax denominators
+  // (lanes r and r + 32 hold halves of one head's) and its overflow flag
+  // there, runs the latent sum of the last tile, and one barrier publishes
+  // both for the normalisation and the recompute decision.
+  auto finish_pass = [&]() {
+    MLA_LDS char* fin = pslot(ntiles);
+    const float l_tot = s.l + __shfl_xor(s.l, 32);
+    if (hh == 0) ((MLA_LDS float*)fin)[head] = l_tot;
+    const bool wave_overflow = __ballot(s.overflow) != 0;
+    if (lane == 0) ((MLA_LDS int*)(fin + kFinFlags))[wave] = wave_overflow ? 1 : 0;
+    latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
+    if constexpr (!C::F32) vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
+    __syncthreads();
+  };
+  static_assert(kFinFlags >= 32 * C::WAVES * 4 && kFinFlags + 4 * C::WAVES <= C::P_BYTES, "denominators and flags fit");
 
   if constexpr (!STREAM) load_q();
 
@@ -1330,9 +1356,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
                                          tbase, t, ntiles, start, end, first != 0, land(t), land(t + 1),
                                          slot(t + 1), sv.seq_row);
       }
-      latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
-      vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
-      __syncthreads();
+      finish_pass();
     } else if constexpr (STREAM) {
       // prologue: tiles 0 and 1, and (first pass) the second half of the
       // query once the first is read
@@ -1361,9 +1385,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
         tile_step_stream<C, PAGED, false>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma, tbase, t,
                             ntiles, start, end, first != 0);
       }
-      latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
-      if constexpr (!C::F32) vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
-      __syncthreads();
+      finish_pass();
     } else {
     // prologue: tile 0 resident, tile 1 in flight
     issue_tile<C, PAGED>(p, sv, dma, slot(0), start, end, st);
@@ -1386,55 +1408,65 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
     for (int t = 1; t < ntiles; ++t)
       tile_step<C, PAGED, false>(p, slot(t), slot(t - 1), slot(t + 1), slot(t + 2), pslot(t), pslot(t - 1), q,
                                  s, lo, sv, dma, st, t, ntiles, start, end, false);
-    latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
-    if constexpr (!C::F32) vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
-    __syncthreads();
+    finish_pass();
     }
     if (pass == 1) break;
     // did any lane's scores outrun the headroom? (uniform decision)
-    MLA_LDS int* redo = (MLA_LDS int*)pbase;
-    const bool wave_overflow = __ballot(s.overflow) != 0;
-    if (lane == 0) redo[wave] = wave_overflow ? 1 : 0;
-    __syncthreads();
     int any = 0;
 #pragma unroll
-    for (int v = 0; v < C::WAVES; ++v) any |= redo[v];
-    __syncthreads();
+    for (int v = 0; v < C::WAVES; ++v) any |= ((const MLA_LDS int*)(pslot(ntiles) + kFinFlags))[v];
     if (!any) break;
+    __syncthreads();   // every wave has read the flags before the second pass reuses the buffers
   }
 
-  // ---- normalise and store; every head's denominator goes through LDS ----
-  MLA_LDS float* lden = (MLA_LDS float*)pbase;
-  const float l_tot = s.l + __shfl_xor(s.l, 32);   // lanes r and r + 32 hold one head
-  if (hh == 0) lden[head] = l_tot;
+  // ---- normalise and store; every head's denominator is in LDS already ----
+  const MLA_LDS float* lden = (const MLA_LDS float*)pslot(ntiles);
+  const float l_tot = s.l + __shfl_xor(s.l, 32);   // every lane takes part in the exchange
   if (hh == 0 && head < C::H) p.lse[out_row<C>(p, b, split, head)] = (s.m_ref + fast_log2(l_tot)) * kLn2;
-  __syncthreads();
-  if constexpr (C::OUT_STAGE) {
+  // staging of the bf16 rows below: one region of H padded rows per wave,
+  // all before the P^T buffers (where the denominators are)
+  constexpr int SROW = C::FPW * 2 + 16;
+  constexpr bool STAGE = !C::F32 && C::WAVES * C::H * SROW <= (E4M3 ? R8::P : C::NBUF * C::BUF_BYTES);
+  if constexpr (STAGE) {
     if (!f32_out) {
-      // bf16 rows go through LDS (the idle tile ring) so that every store
-      // writes whole 1 KiB rows: row h at h * OROW, padded by 16 bytes so the
-      // 32 heads of one fragment write to different banks
-      MLA_LDS char* ob = lds;
+      // Lanes r and r + 32 hold alternating runs of four features of head
+      // 32 hb + r. Packed to bf16 pairs, half of them are exchanged between
+      // the two lanes (v_permlane32_swap), after which lane r holds features
+      // 0..15 and lane r + 32 features 16..31 of each 32-feature fragment.
+      // Each wave stages its own feature slice of every head (128 heads x
+      // FPW features, rows padded by 16 bytes against bank conflicts) in a
+      // region of its own, then reads it back so that every 16 lanes hold
+      // one head's slice and each store writes whole 256-byte row segments.
+      static_assert(C::FPW * 2 == 16 * 16, "16 lanes a row");
+      MLA_LDS char* stage = lds + wave * (C::H * SROW);
 #pragma unroll
       for (int hb = 0; hb < C::HB; ++hb) {
         const int h = 32 * hb + r;
         const float inv = 1.0f / lden[h];
 #pragma unroll
-        for (int j = 0; j < C::NFJ; ++j)
+        for (int j = 0; j < C::NFJ; ++j) {
+          uint32_t pk[8];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int feat = wave * C::FPW + 32 * j + 8 * jj + 4 * hh;
-            u32x2 v;
-            v[0] = pack_bf16x2(s.o[j][hb][4 * jj + 0] * inv, s.o[j][hb][4 * jj + 1] * inv);
-            v[1] = pack_bf16x2(s.o[j][hb][4 * jj + 2] * inv, s.o[j][hb][4 * jj + 3] * inv);
-            *(MLA_LDS u32x2*)(ob + h * C::OROW + feat * 2) = v;
-          }
+          for (int k = 0; k < 8; ++k) pk[k] = pack_bf16x2(s.o[j][hb][2 * k] * inv, s.o[j][hb][2 * k + 1] * inv);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) swap_lane_halves(pk[k], pk[k + 4]);
+          MLA_LDS char* dst = stage + h * SROW + (32 * j + 16 * hh) * 2;
+          *(MLA_LDS u32x4*)dst = u32x4{pk[0], pk[1], pk[4], pk[5]};
+          *(MLA_LDS u32x4*)(dst + 16) = u32x4{pk[2], pk[3], pk[6], pk[7]};
+        }
       }
-      __syncthreads();
-      // wave w stores rows w, w + WAVES, ...: 64 lanes x 16 bytes per row
-      for (int h = wave; h < C::H; h += C::WAVES) {
-        const u32x4 v = *(const MLA_LDS u32x4*)(ob + h * C::OROW + lane * 16);
-        *(u32x4*)((uint16_t*)p.out + out_row<C>(p, b, split, h) * C::DC + lane * 8) = v;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's own staging
+      // 16 lanes per head, four heads per instruction; eight reads in flight
+      const int c = lane & 15;
+      const MLA_LDS char* src = stage + (lane >> 4) * SROW + 16 * c;
+      uint16_t* dst = (uint16_t*)p.out + out_row<C>(p, b, split, lane >> 4) * C::DC + wave * C::FPW + 8 * c;
+#pragma unroll
+      for (int i0 = 0; i0 < C::H / 4; i0 += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = *(const MLA_LDS u32x4*)(src + 4 * (i0 + k) * SROW);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) *(u32x4*)(dst + (int64_t)4 * (i0 + k) * C::DC) = v[k];
       }
       return;
     }
