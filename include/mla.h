@@ -48,7 +48,8 @@ typedef int32_t mla_status;
 #define MLA_ERR_SHAPE       (-2)  /* a size is negative, zero where it must not be,
                                      or inconsistent with another                 */
 #define MLA_ERR_DTYPE       (-3)  /* unknown dtype or unsupported dtype combination */
-#define MLA_ERR_UNSUPPORTED (-4)  /* head shape outside the compiled set           */
+#define MLA_ERR_UNSUPPORTED (-4)  /* head shape outside the compiled set, or a size
+                                     beyond a documented limit                    */
 #define MLA_ERR_ALIGN       (-5)  /* a pointer or stride breaks 16-byte alignment   */
 #define MLA_ERR_HIP         (-6)  /* a HIP call failed; see mla_last_hip_error()    */
 
@@ -81,8 +82,9 @@ typedef struct {
  *   elements apart); `scale` holds one fp32 per row; c_KV = code * scale.
  * Only rows of tokens j < seq_lens[b] are read; padding rows and the unused
  * tail of a sequence's last page may hold anything (NaN included).
- * page_size must be a power of two; block-table entries past a sequence's
- * last page are never read.
+ * page_size must be a power of two. The decode may load block-table entries
+ * anywhere in row b (up to max_pages_per_seq), but it follows only those of
+ * pages that hold tokens j < seq_lens[b]; the others may hold any value.
  */
 typedef struct {
   int32_t dtype;
@@ -133,7 +135,14 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch,
  *           MLA_F32), each normalised over its own chunk; lse [B, S, H] f32.
  *           Merge them with mla_combine (same dtype as its part_dtype).
  * A sequence (or chunk) with no tokens yields out = 0 and lse = -inf.
- * Limits: row_stride (and rope_stride) at most 2^24 bytes.
+ * Limits: row_stride (and rope_stride) at most 2^24 bytes; a chunk,
+ * mla_split_chunk(max_seq_len, num_splits), of at most 2^17 tokens
+ * (MLA_ERR_UNSUPPORTED above: raise num_splits). The softmax exponentials of
+ * a chunk are taken against a fixed reference (the largest score of its
+ * first 32 tokens) and the chunk is computed again against its true maximum
+ * if a later score exceeds that reference by more than 64 (base 2). So every
+ * exponential is at most 2^64 and, over at most 2^17 tokens, every sum stays
+ * finite in fp32 for cache values of magnitude below 2^40.
  */
 mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat,
                       const mla_kv_cache* cache, const int32_t* seq_lens,
@@ -266,7 +275,9 @@ int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tok
  * executing and `stop_event` when it ends (hipExtLaunchKernel's event pair),
  * so hipEventElapsedTime on the two gives that kernel's own duration, without
  * the gaps that events recorded separately on the stream add. Each entry
- * point launches one kernel. The events are hipEvent_t handles created by
+ * point launches one kernel, except mla_cache_append and mla_o_proj, which
+ * launch two: the start event goes with the first and the stop event with the
+ * second, so the pair brackets both. The events are hipEvent_t handles created by
  * the caller with timing enabled; either may be NULL. The pair is consumed
  * by that one launch; a call that fails validation launches nothing and
  * leaves it pending. Always returns MLA_OK.

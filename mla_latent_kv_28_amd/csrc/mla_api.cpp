@@ -93,7 +93,7 @@ const char* mla_status_string(mla_status status) {
     case MLA_ERR_NULL: return "a required pointer is NULL";
     case MLA_ERR_SHAPE: return "a size is negative, zero where it must not be, or inconsistent";
     case MLA_ERR_DTYPE: return "unknown dtype or unsupported dtype combination";
-    case MLA_ERR_UNSUPPORTED: return "head shape outside the compiled set";
+    case MLA_ERR_UNSUPPORTED: return "head shape outside the compiled set, or a size beyond a documented limit";
     case MLA_ERR_ALIGN: return "a pointer or stride is not 16-byte aligned";
     case MLA_ERR_HIP: return "a HIP call failed (see mla_last_hip_error)";
     default: return "unknown status";
@@ -171,6 +171,8 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, co
   if (!aligned16(q_lat) || !aligned16(cache->latent) || !aligned16(out) || !aligned16(lse))
     return MLA_ERR_ALIGN;
   if (static_cast<int64_t>(batch) * num_splits > 0x7fffffff) return MLA_ERR_SHAPE;
+  // the fixed-reference softmax keeps its sums finite for at most 2^17 tokens a chunk
+  if (mla_split_chunk(max_seq_len, num_splits) > (1 << 17)) return MLA_ERR_UNSUPPORTED;
 
   mla::DecodeParams p{};
   p.q_lat = q_lat;

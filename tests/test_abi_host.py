@@ -134,6 +134,12 @@ def test_decode_argument_errors(L):
     assert _decode(L, out=P + 8) == -5
     assert _decode(L, cache=_cache(latent=P + 4)) == -5
     assert _decode(L, batch=0) == 0                                 # empty batch: nothing to do
+    # chunks longer than 2^17 tokens: the fixed-reference softmax bound no longer holds
+    long_cache = _cache(seq_stride=1 << 18)
+    assert _decode(L, cache=long_cache, max_len=(1 << 17) + 1) == -4
+    assert _decode(L, cache=long_cache, max_len=1 << 18) == -4
+    assert _decode(L, cache=_cache(seq_stride=300000), max_len=300000, splits=2) == -4   # 150016 > 2^17
+    assert mla.mla_split_chunk((1 << 17) + 1, 2) <= (1 << 17)        # two splits would be accepted
 
 
 @no_gpu
