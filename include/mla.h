@@ -252,6 +252,26 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
                             const mla_kv_cache* cache, void* workspace, int64_t workspace_bytes,
                             mla_stream stream);
 
+/*
+ * mla_cache_append without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation): the fp32 partial sums go to a scratch array inside the
+ * library instead, one copy on each GPU it runs on, 8 MiB, held until the
+ * process ends. The call allocates nothing. Limit:
+ * mla_cache_append_workspace(dims, batch, hidden) <= 8 MiB (batch up to 182
+ * at hidden 5120 with the DeepSeek-V2 shape); beyond it the call returns
+ * MLA_ERR_UNSUPPORTED and enqueues nothing. Every call on one GPU uses that
+ * GPU's array, so calls that can run at the same time on one GPU (on
+ * different streams or threads) race; the caller orders them. The first call
+ * on each device resolves the array's address with that device current.
+ * Arguments, results and other errors as for mla_cache_append.
+ */
+mla_status mla_cache_append_noalloc(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
+                                    const void* w_dkv, const void* w_kr, const void* norm_gain,
+                                    int32_t dtype, float rms_eps, float rope_base,
+                                    const int32_t* positions, const mla_kv_cache* cache,
+                                    mla_stream stream);
+
 /* Tokens per split chunk that mla_decode uses for (max_seq_len, num_splits):
  * ceil(max_seq_len / num_splits) rounded up to a multiple of 32. */
 int32_t mla_split_chunk(int32_t max_seq_len, int32_t num_splits);

@@ -23,7 +23,8 @@ _STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DT
 EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
            "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error",
            "mla_time_next_launch",
-           "mla_cache_append", "mla_cache_append_workspace", "mla_o_proj", "mla_o_proj_workspace")
+           "mla_cache_append", "mla_cache_append_workspace", "mla_cache_append_noalloc",
+           "mla_o_proj", "mla_o_proj_workspace")
 
 
 class MLAError(RuntimeError):
@@ -80,6 +81,9 @@ def lib():
         L.mla_cache_append.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, f32, f32, vp,
                                        ctypes.POINTER(KVCache), vp, i64, vp]
         L.mla_cache_append.restype = i32
+        L.mla_cache_append_noalloc.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, f32, f32, vp,
+                                               ctypes.POINTER(KVCache), vp]
+        L.mla_cache_append_noalloc.restype = i32
         for name in ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_split_chunk",
                      "mla_suggest_splits", "mla_last_hip_error", "mla_combine_out_proj",
                      "mla_time_next_launch"):
@@ -251,6 +255,24 @@ def mla_cache_append(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size() if workspace is not None else 0,
         _stream(stream))
     _check(st, "mla_cache_append")
+
+
+def mla_cache_append_noalloc(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps, rope_base,
+                             positions, cache, stream=None):
+    """mla_cache_append with the library's own per-GPU scratch in place of a
+    workspace (the call allocates nothing; calls on one GPU must not overlap)."""
+    d = dims_of(dims)
+    t = _TORCH_DTYPE.get(dtype)
+    st = lib().mla_cache_append_noalloc(
+        ctypes.byref(d), batch, hidden,
+        _dev(h, "h", t, batch * hidden),
+        _dev(w_dkv, "w_dkv", t, d.d_latent * hidden),
+        _dev(w_kr, "w_kr", t, d.d_rope * hidden),
+        _dev(norm_gain, "norm_gain", t, d.d_latent),
+        dtype, float(rms_eps), float(rope_base),
+        _dev(positions, "positions", torch.int32, batch),
+        ctypes.byref(cache), _stream(stream))
+    _check(st, "mla_cache_append_noalloc")
 
 
 def mla_split_chunk(max_seq_len, num_splits):

@@ -20,6 +20,7 @@
 //     per-token scale absmax / 448 and the rotary key in bf16.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "mla_device.h"
@@ -234,6 +235,40 @@ __global__ __launch_bounds__(64 * kFinishWaves) void append_finish(AppendParams 
 }  // namespace
 
 int append_slices(int hidden) { return (hidden + kSlice - 1) / kSlice; }
+
+// Scratch of the allocation-free entry point: the fp32 partial sums that
+// mla_cache_append keeps in the caller's workspace, here in a device array of
+// the library's own (one copy on each GPU the library runs on, held until the
+// process ends). Every element a call reads was written by that call's
+// projection, so nothing needs clearing between calls.
+constexpr int64_t kAppendScratchBytes = int64_t{8} << 20;
+static __device__ __align__(256) float scratch[kAppendScratchBytes / sizeof(float)];
+
+int64_t append_scratch_bytes() { return kAppendScratchBytes; }
+
+// Device address of the current GPU's copy of `scratch`, resolved with
+// hipGetSymbolAddress the first time a device asks (with that device current)
+// and kept per device. Host code passes this address to kernels, never the
+// array's name (which on the host is only a stand-in).
+hipError_t append_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<float*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* ptr = addr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (q == nullptr) return hipErrorInvalidSymbol;
+    ptr = static_cast<float*>(q);
+    addr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
 
 // A pending event pair (mla_time_next_launch) brackets both kernels: the
 // start event goes with the projection, the stop event with the finish.

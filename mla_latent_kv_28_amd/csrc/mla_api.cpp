@@ -321,11 +321,16 @@ int64_t mla_cache_append_workspace(const mla_dims* dims, int32_t batch, int32_t 
          static_cast<int64_t>(sizeof(float));
 }
 
-mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
-                            const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
-                            float rms_eps, float rope_base, const int32_t* positions,
-                            const mla_kv_cache* cache, void* workspace, int64_t workspace_bytes,
-                            mla_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the two cache-append entry points: everything but the
+// workspace. Fills `p` (work left null) and returns MLA_OK, or the status.
+mla_status cache_append_params(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
+                               const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
+                               float rms_eps, float rope_base, const int32_t* positions, const mla_kv_cache* cache,
+                               mla::AppendParams& p, bool& dsv2) {
   if (dims == nullptr || cache == nullptr) return MLA_ERR_NULL;
   if (batch < 0 || hidden <= 0) return MLA_ERR_SHAPE;
   if (!std::isfinite(rms_eps) || rms_eps < 0.0f || !std::isfinite(rope_base) || rope_base <= 0.0f)
@@ -337,8 +342,7 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
   if (sh == Shape::kTiny && (dtype != MLA_F32 || cache->dtype != MLA_F32)) return MLA_ERR_DTYPE;
   if (hidden % (dtype == MLA_BF16 ? 16 : 4) != 0) return MLA_ERR_SHAPE;   // whole 16-wide k steps (bf16)
   if (batch == 0) return MLA_OK;
-  if (!h || !w_dkv || !w_kr || !positions || !cache->latent || !workspace) return MLA_ERR_NULL;
-  if (workspace_bytes < mla_cache_append_workspace(dims, batch, hidden)) return MLA_ERR_SHAPE;
+  if (!h || !w_dkv || !w_kr || !positions || !cache->latent) return MLA_ERR_NULL;
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
   if (fp8 && (!cache->rope || !cache->scale)) return MLA_ERR_NULL;
   if (cache->page_size < 0) return MLA_ERR_SHAPE;
@@ -357,10 +361,8 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
     if (cache->rope_stride < dims->d_rope) return MLA_ERR_SHAPE;
     if (!aligned16(cache->rope) || (reinterpret_cast<uintptr_t>(cache->scale) & 3u) != 0) return MLA_ERR_ALIGN;
   }
-  if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(cache->latent) ||
-      !aligned16(workspace))
-    return MLA_ERR_ALIGN;
-  mla::AppendParams p{};
+  if (!aligned16(h) || !aligned16(w_dkv) || !aligned16(w_kr) || !aligned16(cache->latent)) return MLA_ERR_ALIGN;
+  p = mla::AppendParams{};
   p.h = h;
   p.w_dkv = w_dkv;
   p.w_kr = w_kr;
@@ -375,7 +377,7 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
   p.block_table = cache->block_table;
   p.max_pages = cache->max_pages_per_seq;
   p.page_shift = paged ? log2i(cache->page_size) : -1;
-  p.work = static_cast<float*>(workspace);
+  p.work = nullptr;
   p.batch = batch;
   p.hidden = hidden;
   p.ksplits = mla::append_slices(hidden);
@@ -383,9 +385,50 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
   p.d_rope = dims->d_rope;
   p.eps = rms_eps;
   p.rope_base = rope_base;
-  return hip_status(mla::launch_cache_append(p, sh == Shape::kDsv2, cache->dtype == MLA_FP8_E4M3 ? mla::kFP8
-                                                 : cache->dtype == MLA_BF16 ? mla::kBF16 : mla::kF32,
-                                             static_cast<hipStream_t>(stream)));
+  dsv2 = sh == Shape::kDsv2;
+  return MLA_OK;
+}
+
+int cache_kind_of(int32_t dtype) {
+  return dtype == MLA_FP8_E4M3 ? mla::kFP8 : dtype == MLA_BF16 ? mla::kBF16 : mla::kF32;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
+                            const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
+                            float rms_eps, float rope_base, const int32_t* positions,
+                            const mla_kv_cache* cache, void* workspace, int64_t workspace_bytes,
+                            mla_stream stream) {
+  mla::AppendParams p{};
+  bool dsv2 = false;
+  const mla_status st = cache_append_params(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps,
+                                            rope_base, positions, cache, p, dsv2);
+  if (st != MLA_OK || batch == 0) return st;
+  if (!workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < mla_cache_append_workspace(dims, batch, hidden)) return MLA_ERR_SHAPE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  p.work = static_cast<float*>(workspace);
+  return hip_status(mla::launch_cache_append(p, dsv2, cache_kind_of(cache->dtype), static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_cache_append_noalloc(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
+                                    const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
+                                    float rms_eps, float rope_base, const int32_t* positions,
+                                    const mla_kv_cache* cache, mla_stream stream) {
+  mla::AppendParams p{};
+  bool dsv2 = false;
+  const mla_status st = cache_append_params(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps,
+                                            rope_base, positions, cache, p, dsv2);
+  if (st != MLA_OK || batch == 0) return st;
+  if (mla_cache_append_workspace(dims, batch, hidden) > mla::append_scratch_bytes()) return MLA_ERR_UNSUPPORTED;
+  float* scratch = nullptr;
+  const hipError_t e = mla::append_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e);
+  p.work = scratch;
+  return hip_status(mla::launch_cache_append(p, dsv2, cache_kind_of(cache->dtype), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -70,6 +70,9 @@ struct AppendParams {
 };
 int append_slices(int hidden);
 hipError_t launch_cache_append(const AppendParams& p, bool dsv2, int cache_kind, hipStream_t s);
+// The library's own per-GPU scratch for the allocation-free cache append.
+int64_t append_scratch_bytes();
+hipError_t append_scratch(float** ptr);   // this device's address of the array
 
 // Attention output projection u[b] = W_O o[b] (oproj.hip).
 struct OProjParams {

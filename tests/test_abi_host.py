@@ -226,6 +226,26 @@ def test_cache_append_argument_errors(L):
 
 
 @no_gpu
+def test_cache_append_noalloc_argument_errors(L):
+    # the workspace form's checks, then the scratch limit (8 MiB), all before
+    # the scratch address is looked up
+    d = ctypes.byref(DSV2)
+
+    def f(dims=d, batch=4, hidden=5120, h=P, w1=P, w2=P, dtype=mla.BF16, pos=P, cache=None):
+        cache = _cache(seq_stride=64) if cache is None else cache
+        return L.mla_cache_append_noalloc(dims, batch, hidden, h, w1, w2, None, dtype, 1e-6, 1e4, pos,
+                                          ctypes.byref(cache), None)
+    assert f(dims=None) == -1
+    assert f(batch=-1) == -2 and f(hidden=5128) == -2
+    assert f(dtype=mla.F32) == -3
+    assert f(h=None) == -1 and f(pos=None) == -1
+    assert f(h=P + 2) == -5
+    assert f(batch=183) == -4                        # 183 x 20 x 576 x 4 bytes > 8 MiB
+    assert mla.mla_cache_append_workspace(DSV2, 182, 5120) <= (8 << 20)
+    assert f(batch=0, h=None, w1=None, w2=None, pos=None) == 0
+
+
+@no_gpu
 def test_o_proj_argument_errors(L):
     d = ctypes.byref(DSV2)
     ws = mla.mla_o_proj_workspace(DSV2, 2, 5120)
