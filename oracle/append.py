@@ -46,14 +46,29 @@ def rope(x, position, base):
     return out
 
 
-def append_entry(h, w_dkv, w_kr, positions, eps, base, gain=None):
+def rope_with(x, position, freqs):
+    """Rotate the pairs (x[2i], x[2i+1]) of the last axis by position * freqs[i]."""
+    x = _f64(x)
+    ang = np.asarray(position, dtype=np.float64)[..., None] * _f64(freqs)
+    cos, sin = np.cos(ang), np.sin(ang)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * cos - x[..., 1::2] * sin
+    out[..., 1::2] = x[..., 0::2] * sin + x[..., 1::2] * cos
+    return out
+
+
+def append_entry(h, w_dkv, w_kr, positions, eps, base, gain=None, freqs=None):
     """(c_kv [B, d_c], k_rope [B, d_R]) of one new token per sequence.
 
     h [B, d] hidden states, w_dkv [d_c, d], w_kr [d_R, d], positions [B].
+    freqs [d_R / 2]: the rotary frequencies when they are not base^(-2i/d_R)
+    (a length-extended model rotates its keys with the YaRN frequencies of
+    oracle.query.rope_frequencies, as its queries).
     """
     h = _f64(h)
     c_kv = rms_norm(h @ _f64(w_dkv).T, eps, gain)
-    k_rope = rope(h @ _f64(w_kr).T, positions, base)
+    y = h @ _f64(w_kr).T
+    k_rope = rope(y, positions, base) if freqs is None else rope_with(y, positions, freqs)
     return c_kv, k_rope
 
 

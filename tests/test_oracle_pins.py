@@ -515,3 +515,105 @@ def test_output_projection_brute_force_one_hot_and_absorption():
     folded = np.concatenate([w_o[:, h * d_v:(h + 1) * d_v] @ w_uv[h] for h in range(H)], axis=1)
     np.testing.assert_allclose(oracle.output_projection(o2, w_o), o_lat.reshape(B, -1) @ folded.T,
                                rtol=1e-12, atol=1e-12)
+
+
+# --- the query path and the rotary frequencies (plain and YaRN) -----------------------
+
+def _pair_angles(freqs_rotation, d):
+    """Angle by which each pair of a unit vector turns at position 1, read off
+    the rotated vector (atan2), so frequencies are compared through rotations."""
+    out = []
+    for i in range(d // 2):
+        e = np.zeros(d)
+        e[2 * i] = 1.0
+        r = freqs_rotation(e)
+        out.append(math.atan2(r[2 * i + 1], r[2 * i]))
+    return np.array(out)
+
+
+def test_rope_frequencies_plain_equal_rope_and_yarn_limits():
+    rng = np.random.default_rng(41)
+    d, base = 64, 10000.0
+    x = rng.standard_normal((3, d))
+    pos = np.array([0, 17, 4095])
+    plain = oracle.rope_frequencies(d, base)
+    np.testing.assert_allclose(oracle.rope_with(x, pos, plain), oracle.rope(x, pos, base), rtol=0, atol=1e-12)
+    # every pair "long" against the original context: each frequency divided by
+    # s, i.e. position interpolation: turning at p with theta / s = turning at p / s
+    s = 40.0
+    interp = oracle.rope_frequencies(d, base, s, yarn_alpha=1e12, yarn_beta=2e12)
+    np.testing.assert_allclose(oracle.rope_with(x, pos, interp), oracle.rope(x, pos / s, base), rtol=0, atol=1e-12)
+    # every pair "short": no change
+    keep = oracle.rope_frequencies(d, base, s, yarn_alpha=-2.0, yarn_beta=-1.0)
+    np.testing.assert_allclose(keep, plain, rtol=0, atol=0)
+
+
+def test_yarn_frequencies_with_the_pages_parameters():
+    # s = 40, alpha = 1, beta = 32, original context 4096 (4K -> 160K), d_R = 64, base 10000
+    d, base = 64, 10000.0
+    f = oracle.rope_frequencies(d, base, 40.0, 1.0, 32.0, 4096)
+    plain = _pair_angles(lambda e: oracle.rope(e, 1, base), d)       # plain angle per position, from rotations
+    # turns of pair i over 4096 positions: pairs 0..10 turn more than 32 times
+    # (their wavelengths 2 pi / theta_i are under 128 positions), 23..31 less than once
+    turns = 4096 * plain / (2 * math.pi)
+    assert np.all(turns[:11] > 32) and np.all(turns[23:] < 1) and np.all((turns[11:23] >= 1) & (turns[11:23] <= 32))
+    np.testing.assert_allclose(f[:11], plain[:11], rtol=1e-13)          # high frequencies kept
+    np.testing.assert_allclose(f[23:], plain[23:] / 40.0, rtol=1e-12)  # low ones interpolated by s
+    assert np.all((f[11:23] < plain[11:23]) & (f[11:23] > plain[11:23] / 40.0))   # blended in between
+    assert np.all(np.diff(f) < 0)                                       # still ordered
+    # rotations with these frequencies keep the relative-position property
+    rng = np.random.default_rng(42)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    s1 = oracle.rope_with(q, 100000, f) @ oracle.rope_with(k, 99000, f)
+    s2 = oracle.rope_with(q, 1500, f) @ oracle.rope_with(k, 500, f)
+    assert s1 == pytest.approx(s2, rel=1e-9)
+
+
+def test_query_path_brute_force_one_hot_and_position_zero():
+    rng = np.random.default_rng(43)
+    B, d, dq, H, dn, dr = 2, 10, 6, 2, 3, 4
+    h = rng.standard_normal((B, d))
+    w_dq, w_uq, w_qr = rng.standard_normal((dq, d)), rng.standard_normal((H * dn, dq)), rng.standard_normal((H * dr, dq))
+    gain, pos, eps = rng.standard_normal(dq), np.array([3, 250]), 1e-6
+    f = oracle.rope_frequencies(dr, 500.0, 8.0, 1.0, 4.0, orig_ctx=64)
+    c, qn, qr = oracle.query_path(h, w_dq, w_uq, w_qr, pos, eps, f, H, gain)
+    angles = _pair_angles(lambda e: oracle.rope_with(e, 1, f), dr)
+    for b in range(B):                       # the definition in plain loops
+        x = [sum(w_dq[i, j] * h[b, j] for j in range(d)) for i in range(dq)]
+        rms = math.sqrt(sum(v * v for v in x) / dq + eps)
+        cq = [x[i] / rms * gain[i] for i in range(dq)]
+        for i in range(dq):
+            assert c[b, i] == pytest.approx(cq[i], rel=1e-12)
+        for hh in range(H):
+            for n in range(dn):
+                assert qn[b, hh, n] == pytest.approx(sum(w_uq[hh * dn + n, i] * cq[i] for i in range(dq)), rel=1e-11, abs=1e-12)
+            y = [sum(w_qr[hh * dr + n, i] * cq[i] for i in range(dq)) for n in range(dr)]
+            for i in range(dr // 2):
+                a = pos[b] * angles[i]
+                assert qr[b, hh, 2 * i] == pytest.approx(y[2 * i] * math.cos(a) - y[2 * i + 1] * math.sin(a), rel=1e-10, abs=1e-11)
+                assert qr[b, hh, 2 * i + 1] == pytest.approx(y[2 * i] * math.sin(a) + y[2 * i + 1] * math.cos(a), rel=1e-10, abs=1e-11)
+    # a one-hot hidden state at position 0: c_Q is the normed column, the
+    # queries the up-projections of it, unrotated
+    e = np.zeros((1, d))
+    e[0, 7] = -3.0
+    c1, qn1, qr1 = oracle.query_path(e, w_dq, w_uq, w_qr, [0], 0.0, f, H)
+    col = -3.0 * w_dq[:, 7]
+    np.testing.assert_allclose(c1[0], col / np.sqrt(np.mean(col ** 2)), rtol=1e-14)
+    np.testing.assert_allclose(qn1[0].ravel(), w_uq @ c1[0], rtol=1e-13)
+    np.testing.assert_allclose(qr1[0].ravel(), w_qr @ c1[0], rtol=1e-13)
+
+
+def test_append_entry_with_frequencies():
+    # the cache entry with explicit frequencies: plain ones reproduce the base
+    # form; YaRN ones rotate the key as the query path rotates its queries
+    rng = np.random.default_rng(44)
+    h, w_dkv, w_kr = rng.standard_normal((3, 16)), rng.standard_normal((8, 16)), rng.standard_normal((4, 16))
+    pos = np.array([0, 9, 300])
+    c0, k0 = oracle.append_entry(h, w_dkv, w_kr, pos, 1e-6, 10000.0)
+    c1, k1 = oracle.append_entry(h, w_dkv, w_kr, pos, 1e-6, 10000.0, freqs=oracle.rope_frequencies(4, 10000.0))
+    np.testing.assert_array_equal(c0, c1)
+    np.testing.assert_allclose(k1, k0, rtol=0, atol=1e-13)
+    f = oracle.rope_frequencies(4, 10000.0, 40.0, 1.0, 32.0, 64)
+    _, k2 = oracle.append_entry(h, w_dkv, w_kr, pos, 1e-6, 10000.0, freqs=f)
+    np.testing.assert_allclose(k2, oracle.rope_with(h @ w_kr.T, pos, f), rtol=1e-13)
+    np.testing.assert_allclose(k2[0], (h @ w_kr.T)[0], rtol=1e-15)     # position 0: unrotated
