@@ -68,6 +68,32 @@ typedef struct {
 } mla_dims;
 
 /*
+ * Rotary position frequencies (DeepSeek-V2 paper, section 2.1.3: RoPE on the
+ * decoupled query and key; section 3.1.4: YaRN applied to the decoupled key to
+ * extend the context, with s = 40, alpha = 1, beta = 32 over a 4K original
+ * context). Feature pair (2i, 2i + 1) of a rotary vector at position p turns
+ * by p * f_i:
+ *   theta_i = base^(-2i / d_rope);
+ *   yarn_scale == 1: f_i = theta_i (plain RoPE; the yarn_* fields are unused);
+ *   yarn_scale  > 1 (YaRN, by-parts interpolation of the paper the pages
+ *   cite): r_i = yarn_orig_ctx * theta_i / (2 pi) turns over the original
+ *   context, g = clamp((r_i - yarn_alpha) / (yarn_beta - yarn_alpha), 0, 1),
+ *   f_i = (1 - g) * theta_i / yarn_scale + g * theta_i.
+ * The frequencies are computed on the host in double precision; angles
+ * p * f_i are formed in double precision on the device. YaRN's length scaling
+ * of the softmax is not part of the rotation: fold it into sm_scale.
+ * Requires base > 0, yarn_scale >= 1 and, for yarn_scale > 1,
+ * yarn_alpha < yarn_beta and yarn_orig_ctx > 0 (else MLA_ERR_SHAPE).
+ */
+typedef struct {
+  float base;
+  float yarn_scale;
+  float yarn_alpha;
+  float yarn_beta;
+  int32_t yarn_orig_ctx;
+} mla_rope;
+
+/*
  * The latent cache of one layer (DeepSeek-V2 paper, section 2.1.3: one
  * (d_c + d_h^R)-element row per cached token).
  *
@@ -227,7 +253,8 @@ mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const
  * compressed latent):
  *   c_KV[b] = RMSNorm(W_DKV h[b]) = x / sqrt(mean(x^2) + rms_eps) * gain,
  *   k_R[b]  = RoPE(W_KR h[b], positions[b]): features (2i, 2i + 1) turned by
- *             positions[b] * rope_base^(-2i / d_rope),
+ *             positions[b] * f_i, f_i the frequencies `rope` describes (plain
+ *             or YaRN; a length-extended model rotates its keys as its queries),
  * written into row positions[b] of sequence b of `cache` (the same layouts
  * mla_decode reads; this call writes through its pointers).
  *   h           [B, hidden], w_dkv [d_latent, hidden], w_kr [d_rope, hidden],
@@ -248,7 +275,7 @@ mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const
 int64_t mla_cache_append_workspace(const mla_dims* dims, int32_t batch, int32_t hidden);
 mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
                             const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
-                            float rms_eps, float rope_base, const int32_t* positions,
+                            float rms_eps, const mla_rope* rope, const int32_t* positions,
                             const mla_kv_cache* cache, void* workspace, int64_t workspace_bytes,
                             mla_stream stream);
 
@@ -268,9 +295,40 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
  */
 mla_status mla_cache_append_noalloc(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
                                     const void* w_dkv, const void* w_kr, const void* norm_gain,
-                                    int32_t dtype, float rms_eps, float rope_base,
+                                    int32_t dtype, float rms_eps, const mla_rope* rope,
                                     const int32_t* positions, const mla_kv_cache* cache,
                                     mla_stream stream);
+
+/*
+ * The query of one new token per sequence (DeepSeek-V2 paper, section 2.1.2:
+ * the query is compressed too, c_Q = W_DQ h, and its content part is the
+ * up-projection q^C = W_UQ c_Q; section 2.1.3: the rotary part of every head
+ * is q^R = RoPE(W_QR c_Q) at the token's position; section 3.1.2: an RMS norm
+ * follows the compressed latent, d'_c = 1536 in DeepSeek-V2):
+ *   c_Q[b]      = RMSNorm(W_DQ h[b]) = x / sqrt(mean(x^2) + rms_eps) * gain,
+ *   q_nope[b,h] = W_UQ[h] c_Q[b],
+ *   q_rope[b,h] = RoPE(W_QR[h] c_Q[b], positions[b]) with the frequencies of `rope`,
+ * the inputs mla_absorb_q takes.
+ *   h      [B, hidden],  w_dq [d_qlatent, hidden],  q_norm_gain [d_qlatent] or NULL,
+ *   w_uq   [H * d_nope, d_qlatent] (rows grouped by head),
+ *   w_qr   [H * d_rope, d_qlatent] (rows grouped by head),
+ *   positions [B] int32 device array (any value; the angle is position * f_i),
+ *   q_nope [B, H, d_nope] and q_rope [B, H, d_rope] (outputs), all in `dtype`.
+ * MLA_BF16 with the DeepSeek-V2 head shape only (MLA_ERR_UNSUPPORTED for the
+ * tiny one); hidden a multiple of 16, d_qlatent a multiple of 256 and at most
+ * 4096. Products accumulate in fp32 over slices of 256 of the contraction,
+ * added in slice order; the norm runs in fp32 and c_Q is rounded to bf16
+ * before the up-projection; rotation angles in fp64.
+ * workspace: device memory of at least mla_query_proj_workspace() bytes,
+ * 16-byte aligned, owned by the caller. Four kernels are launched (the
+ * timing hook's pair brackets all four). batch == 0 is a no-op.
+ */
+int64_t mla_query_proj_workspace(const mla_dims* dims, int32_t batch, int32_t hidden, int32_t d_qlatent);
+mla_status mla_query_proj(const mla_dims* dims, int32_t batch, int32_t hidden, int32_t d_qlatent,
+                          const void* h, const void* w_dq, const void* q_norm_gain, const void* w_uq,
+                          const void* w_qr, int32_t dtype, float rms_eps, const mla_rope* rope,
+                          const int32_t* positions, void* q_nope, void* q_rope, void* workspace,
+                          int64_t workspace_bytes, mla_stream stream);
 
 /* Tokens per split chunk that mla_decode uses for (max_seq_len, num_splits):
  * ceil(max_seq_len / num_splits) rounded up to a multiple of 32. */
@@ -296,8 +354,8 @@ int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tok
  * so hipEventElapsedTime on the two gives that kernel's own duration, without
  * the gaps that events recorded separately on the stream add. Each entry
  * point launches one kernel, except mla_cache_append and mla_o_proj, which
- * launch two: the start event goes with the first and the stop event with the
- * second, so the pair brackets both. The events are hipEvent_t handles created by
+ * launch two, and mla_query_proj, which launches four: the start event goes
+ * with the first and the stop event with the last, so the pair brackets all. The events are hipEvent_t handles created by
  * the caller with timing enabled; either may be NULL. The pair is consumed
  * by that one launch; a call that fails validation launches nothing and
  * leaves it pending. Always returns MLA_OK.

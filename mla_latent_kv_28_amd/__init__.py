@@ -24,7 +24,7 @@ EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_com
            "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error",
            "mla_time_next_launch",
            "mla_cache_append", "mla_cache_append_workspace", "mla_cache_append_noalloc",
-           "mla_o_proj", "mla_o_proj_workspace")
+           "mla_o_proj", "mla_o_proj_workspace", "mla_query_proj", "mla_query_proj_workspace")
 
 
 class MLAError(RuntimeError):
@@ -39,6 +39,19 @@ class MLAError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32),
                 ("d_rope", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+class Rope(ctypes.Structure):
+    """mla_rope: rotary frequencies, plain RoPE (yarn_scale 1) or YaRN."""
+    _fields_ = [("base", ctypes.c_float), ("yarn_scale", ctypes.c_float), ("yarn_alpha", ctypes.c_float),
+                ("yarn_beta", ctypes.c_float), ("yarn_orig_ctx", ctypes.c_int32)]
+
+
+def rope_params(rope):
+    """A Rope from a Rope, or from a number (plain RoPE with that base)."""
+    if isinstance(rope, Rope):
+        return rope
+    return Rope(float(rope), 1.0, 1.0, 32.0, 4096)
 
 
 class KVCache(ctypes.Structure):
@@ -78,12 +91,17 @@ def lib():
         L.mla_o_proj_workspace.restype = i64
         L.mla_cache_append_workspace.argtypes = [pd, i32, i32]
         L.mla_cache_append_workspace.restype = i64
-        L.mla_cache_append.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, f32, f32, vp,
+        pr = ctypes.POINTER(Rope)
+        L.mla_cache_append.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, f32, pr, vp,
                                        ctypes.POINTER(KVCache), vp, i64, vp]
         L.mla_cache_append.restype = i32
-        L.mla_cache_append_noalloc.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, f32, f32, vp,
+        L.mla_cache_append_noalloc.argtypes = [pd, i32, i32, vp, vp, vp, vp, i32, f32, pr, vp,
                                                ctypes.POINTER(KVCache), vp]
         L.mla_cache_append_noalloc.restype = i32
+        L.mla_query_proj_workspace.argtypes = [pd, i32, i32, i32]
+        L.mla_query_proj_workspace.restype = i64
+        L.mla_query_proj.argtypes = [pd, i32, i32, i32, vp, vp, vp, vp, vp, i32, f32, pr, vp, vp, vp, vp, i64, vp]
+        L.mla_query_proj.restype = i32
         for name in ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_split_chunk",
                      "mla_suggest_splits", "mla_last_hip_error", "mla_combine_out_proj",
                      "mla_time_next_launch"):
@@ -237,10 +255,11 @@ def mla_cache_append_workspace(dims, batch, hidden):
     return int(lib().mla_cache_append_workspace(ctypes.byref(d), batch, hidden))
 
 
-def mla_cache_append(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps, rope_base,
+def mla_cache_append(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps, rope,
                      positions, cache, workspace, stream=None):
     """Write the cache entry (RMS-normed latent, rotated key) of one new token
-    per sequence at row positions[b] of `cache`."""
+    per sequence at row positions[b] of `cache`. `rope`: a Rope, or a number
+    (plain RoPE with that base)."""
     d = dims_of(dims)
     t = _TORCH_DTYPE.get(dtype)
     st = lib().mla_cache_append(
@@ -249,7 +268,7 @@ def mla_cache_append(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_
         _dev(w_dkv, "w_dkv", t, d.d_latent * hidden),
         _dev(w_kr, "w_kr", t, d.d_rope * hidden),
         _dev(norm_gain, "norm_gain", t, d.d_latent),
-        dtype, float(rms_eps), float(rope_base),
+        dtype, float(rms_eps), ctypes.byref(rope_params(rope)),
         _dev(positions, "positions", torch.int32, batch),
         ctypes.byref(cache),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size() if workspace is not None else 0,
@@ -257,7 +276,7 @@ def mla_cache_append(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_
     _check(st, "mla_cache_append")
 
 
-def mla_cache_append_noalloc(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps, rope_base,
+def mla_cache_append_noalloc(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps, rope,
                              positions, cache, stream=None):
     """mla_cache_append with the library's own per-GPU scratch in place of a
     workspace (the call allocates nothing; calls on one GPU must not overlap)."""
@@ -269,10 +288,39 @@ def mla_cache_append_noalloc(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dty
         _dev(w_dkv, "w_dkv", t, d.d_latent * hidden),
         _dev(w_kr, "w_kr", t, d.d_rope * hidden),
         _dev(norm_gain, "norm_gain", t, d.d_latent),
-        dtype, float(rms_eps), float(rope_base),
+        dtype, float(rms_eps), ctypes.byref(rope_params(rope)),
         _dev(positions, "positions", torch.int32, batch),
         ctypes.byref(cache), _stream(stream))
     _check(st, "mla_cache_append_noalloc")
+
+
+def mla_query_proj_workspace(dims, batch, hidden, d_qlatent):
+    """Bytes of workspace mla_query_proj needs."""
+    d = dims_of(dims)
+    return int(lib().mla_query_proj_workspace(ctypes.byref(d), batch, hidden, d_qlatent))
+
+
+def mla_query_proj(dims, batch, hidden, d_qlatent, h, w_dq, q_norm_gain, w_uq, w_qr, dtype, rms_eps, rope,
+                   positions, q_nope, q_rope, workspace, stream=None):
+    """q_nope [B, H, d_nope] and rotated q_rope [B, H, d_rope] of one new token
+    per sequence from its hidden state (c_Q = RMSNorm(W_DQ h))."""
+    d = dims_of(dims)
+    t = _TORCH_DTYPE.get(dtype)
+    H = d.num_heads
+    st = lib().mla_query_proj(
+        ctypes.byref(d), batch, hidden, d_qlatent,
+        _dev(h, "h", t, batch * hidden),
+        _dev(w_dq, "w_dq", t, d_qlatent * hidden),
+        _dev(q_norm_gain, "q_norm_gain", t, d_qlatent),
+        _dev(w_uq, "w_uq", t, H * d.d_nope * d_qlatent),
+        _dev(w_qr, "w_qr", t, H * d.d_rope * d_qlatent),
+        dtype, float(rms_eps), ctypes.byref(rope_params(rope)),
+        _dev(positions, "positions", torch.int32, batch),
+        _dev(q_nope, "q_nope", t, batch * H * d.d_nope),
+        _dev(q_rope, "q_rope", t, batch * H * d.d_rope),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream))
+    _check(st, "mla_query_proj")
 
 
 def mla_split_chunk(max_seq_len, num_splits):

@@ -5,7 +5,8 @@
 // 2.1.3: the shared rotary key is k_R = RoPE(W_KR h) at the token's position;
 // section 3.1.2 (model hyper-parameters): an RMS norm follows the compressed
 // latent. Norm: x / sqrt(mean(x^2) + eps), times an optional gain. Rotation:
-// pairs (2i, 2i + 1) turned by position * base^(-2i / d_R).
+// pairs (2i, 2i + 1) turned by position * f_i, the frequencies (plain RoPE or
+// YaRN, section 3.1.4) computed on the host.
 //
 // Two kernels:
 //  1. append_project: [B, d] x [d, d_c + d_R] in K slices of 256 into fp32
@@ -109,7 +110,7 @@ constexpr int kFinishWaves = 4;
 
 template <int DC, int DR, int KIND>
 __global__ __launch_bounds__(64 * kFinishWaves) void append_finish(AppendParams p) {
-  static_assert(DR <= 64 && DR % 2 == 0, "one rotary feature per lane");
+  static_assert(DR <= 64 && DR % 2 == 0 && DR / 2 <= kMaxRopePairs, "one rotary feature per lane");
   constexpr int PER = DC >= 64 ? DC / 64 : 1;
   static_assert(DC >= 64 ? DC % 64 == 0 : true, "latent width");
   __shared__ float red[kFinishWaves - 1][PER + 1][64];
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(64 * kFinishWaves) void append_finish(AppendParams 
   float k_out = 0.0f;
   if (lane < DR) {
     const int i = lane >> 1;
-    const double ang = (double)pos * pow((double)p.rope_base, -2.0 * i / DR);
+    const double ang = (double)pos * p.freq[i];
     double sn, cs;
     sincos(ang, &sn, &cs);
     const double x0 = (lane & 1) ? other : kr, x1 = (lane & 1) ? kr : other;

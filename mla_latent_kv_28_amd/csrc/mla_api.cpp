@@ -41,6 +41,31 @@ mla_status hip_status(hipError_t e) {
 
 bool valid_dtype(int32_t t) { return t == MLA_F32 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
 
+// Frequencies of the d_rope / 2 rotary pairs described by `r` (plain RoPE, or
+// YaRN's by-parts interpolation), in double precision; MLA_ERR_SHAPE for
+// parameters outside the documented ranges.
+mla_status rope_frequencies(const mla_rope* r, int d_rope, double* out) {
+  if (r == nullptr) return MLA_ERR_NULL;
+  if (d_rope / 2 > mla::kMaxRopePairs) return MLA_ERR_UNSUPPORTED;
+  const double base = r->base, s = r->yarn_scale;
+  if (!std::isfinite(base) || base <= 0.0 || !std::isfinite(s) || s < 1.0) return MLA_ERR_SHAPE;
+  const bool yarn = s > 1.0;
+  if (yarn && (!std::isfinite(r->yarn_alpha) || !std::isfinite(r->yarn_beta) || !(r->yarn_alpha < r->yarn_beta) ||
+               r->yarn_orig_ctx <= 0))
+    return MLA_ERR_SHAPE;
+  constexpr double kTwoPi = 6.283185307179586;
+  for (int i = 0; i < d_rope / 2; ++i) {
+    double f = std::pow(base, -2.0 * i / d_rope);
+    if (yarn) {
+      const double turns = r->yarn_orig_ctx * f / kTwoPi;
+      const double g = std::min(1.0, std::max(0.0, (turns - r->yarn_alpha) / (r->yarn_beta - r->yarn_alpha)));
+      f = (1.0 - g) * f / s + g * f;
+    }
+    out[i] = f;
+  }
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,18 +354,22 @@ namespace {
 // workspace. Fills `p` (work left null) and returns MLA_OK, or the status.
 mla_status cache_append_params(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
                                const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
-                               float rms_eps, float rope_base, const int32_t* positions, const mla_kv_cache* cache,
-                               mla::AppendParams& p, bool& dsv2) {
-  if (dims == nullptr || cache == nullptr) return MLA_ERR_NULL;
+                               float rms_eps, const mla_rope* rope, const int32_t* positions,
+                               const mla_kv_cache* cache, mla::AppendParams& p, bool& dsv2) {
+  if (dims == nullptr || cache == nullptr || rope == nullptr) return MLA_ERR_NULL;
   if (batch < 0 || hidden <= 0) return MLA_ERR_SHAPE;
-  if (!std::isfinite(rms_eps) || rms_eps < 0.0f || !std::isfinite(rope_base) || rope_base <= 0.0f)
-    return MLA_ERR_SHAPE;
+  if (!std::isfinite(rms_eps) || rms_eps < 0.0f) return MLA_ERR_SHAPE;
   if (!valid_dtype(dtype) || !valid_dtype(cache->dtype)) return MLA_ERR_DTYPE;
   const Shape sh = shape_of(dims);
   if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
   if (sh == Shape::kDsv2 && (dtype != MLA_BF16 || cache->dtype == MLA_F32)) return MLA_ERR_DTYPE;
   if (sh == Shape::kTiny && (dtype != MLA_F32 || cache->dtype != MLA_F32)) return MLA_ERR_DTYPE;
   if (hidden % (dtype == MLA_BF16 ? 16 : 4) != 0) return MLA_ERR_SHAPE;   // whole 16-wide k steps (bf16)
+  {
+    double f[mla::kMaxRopePairs];
+    const mla_status rs = rope_frequencies(rope, dims->d_rope, f);
+    if (rs != MLA_OK) return rs;
+  }
   if (batch == 0) return MLA_OK;
   if (!h || !w_dkv || !w_kr || !positions || !cache->latent) return MLA_ERR_NULL;
   const bool fp8 = cache->dtype == MLA_FP8_E4M3;
@@ -384,9 +413,8 @@ mla_status cache_append_params(const mla_dims* dims, int32_t batch, int32_t hidd
   p.d_latent = dims->d_latent;
   p.d_rope = dims->d_rope;
   p.eps = rms_eps;
-  p.rope_base = rope_base;
   dsv2 = sh == Shape::kDsv2;
-  return MLA_OK;
+  return rope_frequencies(rope, dims->d_rope, p.freq);
 }
 
 int cache_kind_of(int32_t dtype) {
@@ -399,13 +427,13 @@ extern "C" {
 
 mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
                             const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
-                            float rms_eps, float rope_base, const int32_t* positions,
+                            float rms_eps, const mla_rope* rope, const int32_t* positions,
                             const mla_kv_cache* cache, void* workspace, int64_t workspace_bytes,
                             mla_stream stream) {
   mla::AppendParams p{};
   bool dsv2 = false;
   const mla_status st = cache_append_params(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps,
-                                            rope_base, positions, cache, p, dsv2);
+                                            rope, positions, cache, p, dsv2);
   if (st != MLA_OK || batch == 0) return st;
   if (!workspace) return MLA_ERR_NULL;
   if (workspace_bytes < mla_cache_append_workspace(dims, batch, hidden)) return MLA_ERR_SHAPE;
@@ -414,14 +442,73 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
   return hip_status(mla::launch_cache_append(p, dsv2, cache_kind_of(cache->dtype), static_cast<hipStream_t>(stream)));
 }
 
+int64_t mla_query_proj_workspace(const mla_dims* dims, int32_t batch, int32_t hidden, int32_t d_qlatent) {
+  if (dims == nullptr || batch <= 0 || hidden <= 0 || d_qlatent <= 0 || shape_of(dims) != Shape::kDsv2) return 0;
+  int64_t cq_off = 0, part2_off = 0, total = 0;
+  mla::query_workspace_layout(batch, hidden, d_qlatent, dims->num_heads * (dims->d_nope + dims->d_rope), &cq_off,
+                              &part2_off, &total);
+  return total;
+}
+
+mla_status mla_query_proj(const mla_dims* dims, int32_t batch, int32_t hidden, int32_t d_qlatent, const void* h,
+                          const void* w_dq, const void* q_norm_gain, const void* w_uq, const void* w_qr,
+                          int32_t dtype, float rms_eps, const mla_rope* rope, const int32_t* positions,
+                          void* q_nope, void* q_rope, void* workspace, int64_t workspace_bytes, mla_stream stream) {
+  if (dims == nullptr || rope == nullptr) return MLA_ERR_NULL;
+  if (batch < 0 || hidden <= 0 || d_qlatent <= 0) return MLA_ERR_SHAPE;
+  if (!std::isfinite(rms_eps) || rms_eps < 0.0f) return MLA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  const Shape sh = shape_of(dims);
+  if (sh != Shape::kDsv2) return MLA_ERR_UNSUPPORTED;     // the DeepSeek-V2 head shape, bf16
+  if (dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (hidden % 16 != 0 || d_qlatent % 256 != 0) return MLA_ERR_SHAPE;
+  if (d_qlatent > 4096) return MLA_ERR_UNSUPPORTED;
+  mla::QueryParams p{};
+  {
+    const mla_status rs = rope_frequencies(rope, dims->d_rope, p.freq);
+    if (rs != MLA_OK) return rs;
+  }
+  if (batch == 0) return MLA_OK;
+  if (!h || !w_dq || !w_uq || !w_qr || !positions || !q_nope || !q_rope || !workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < mla_query_proj_workspace(dims, batch, hidden, d_qlatent)) return MLA_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(w_qr) || !aligned16(q_nope) ||
+      !aligned16(q_rope) || !aligned16(workspace))
+    return MLA_ERR_ALIGN;
+  int64_t cq_off = 0, part2_off = 0, total = 0;
+  const int n2 = dims->num_heads * (dims->d_nope + dims->d_rope);
+  mla::query_workspace_layout(batch, hidden, d_qlatent, n2, &cq_off, &part2_off, &total);
+  char* ws = static_cast<char*>(workspace);
+  p.h = h;
+  p.w_dq = w_dq;
+  p.gain = q_norm_gain;
+  p.w_uq = w_uq;
+  p.w_qr = w_qr;
+  p.positions = positions;
+  p.q_nope = q_nope;
+  p.q_rope = q_rope;
+  p.part1 = reinterpret_cast<float*>(ws);
+  p.cq = ws + cq_off;
+  p.part2 = reinterpret_cast<float*>(ws + part2_off);
+  p.batch = batch;
+  p.hidden = hidden;
+  p.dq = d_qlatent;
+  p.heads = dims->num_heads;
+  p.d_nope = dims->d_nope;
+  p.d_rope = dims->d_rope;
+  p.s1 = (hidden + 255) / 256;
+  p.s2 = d_qlatent / 256;
+  p.eps = rms_eps;
+  return hip_status(mla::launch_query_proj(p, static_cast<hipStream_t>(stream)));
+}
+
 mla_status mla_cache_append_noalloc(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
                                     const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
-                                    float rms_eps, float rope_base, const int32_t* positions,
+                                    float rms_eps, const mla_rope* rope, const int32_t* positions,
                                     const mla_kv_cache* cache, mla_stream stream) {
   mla::AppendParams p{};
   bool dsv2 = false;
   const mla_status st = cache_append_params(dims, batch, hidden, h, w_dkv, w_kr, norm_gain, dtype, rms_eps,
-                                            rope_base, positions, cache, p, dsv2);
+                                            rope, positions, cache, p, dsv2);
   if (st != MLA_OK || batch == 0) return st;
   if (mla_cache_append_workspace(dims, batch, hidden) > mla::append_scratch_bytes()) return MLA_ERR_UNSUPPORTED;
   float* scratch = nullptr;

@@ -51,6 +51,9 @@ struct CombineParams {
 };
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 
+// Rotary pairs a kernel parameter block carries frequencies for (d_rope <= 64).
+constexpr int kMaxRopePairs = 32;
+
 // Cache entry of one new token per sequence (append.hip).
 struct AppendParams {
   const void* h;                // [B, hidden] (bf16 | f32)
@@ -66,13 +69,37 @@ struct AppendParams {
   int32_t max_pages, page_shift;   // page_shift -1: contiguous
   float* work;                  // [ksplits, B, d_latent + d_rope] partial sums
   int32_t batch, hidden, ksplits, d_latent, d_rope;
-  float eps, rope_base;
+  float eps;
+  double freq[kMaxRopePairs];   // rotation frequency of feature pair i (plain or YaRN)
 };
 int append_slices(int hidden);
 hipError_t launch_cache_append(const AppendParams& p, bool dsv2, int cache_kind, hipStream_t s);
 // The library's own per-GPU scratch for the allocation-free cache append.
 int64_t append_scratch_bytes();
 hipError_t append_scratch(float** ptr);   // this device's address of the array
+
+// Query of one new token per sequence (query.hip): c_Q = RMSNorm(W_DQ h),
+// q_nope = W_UQ c_Q, q_rope = RoPE(W_QR c_Q).
+struct QueryParams {
+  const void* h;                // [B, hidden] bf16
+  const void* w_dq;             // [dq, hidden]
+  const void* gain;             // [dq] or null
+  const void* w_uq;             // [H * d_nope, dq]
+  const void* w_qr;             // [H * d_rope, dq]
+  const int32_t* positions;     // [B]
+  void* q_nope;                 // [B, H, d_nope] bf16
+  void* q_rope;                 // [B, H, d_rope] bf16
+  float* part1;                 // [s1, B, dq] fp32 partial sums of W_DQ h
+  void* cq;                     // [B, dq] bf16, the normed latent
+  float* part2;                 // [s2, B, H (d_nope + d_rope)] fp32 partial sums
+  int32_t batch, hidden, dq, heads, d_nope, d_rope, s1, s2;
+  float eps;
+  double freq[kMaxRopePairs];
+};
+// Workspace layout of the query path: byte offsets of cq and part2, total.
+void query_workspace_layout(int batch, int hidden, int dq, int n2, int64_t* cq_off, int64_t* part2_off,
+                            int64_t* total);
+hipError_t launch_query_proj(const QueryParams& p, hipStream_t s);
 
 // Attention output projection u[b] = W_O o[b] (oproj.hip).
 struct OProjParams {

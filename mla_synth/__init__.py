@@ -18,4 +18,6 @@ from .inputs import (  # noqa: F401
     AppendInputs,
     make_append_inputs,
     make_oproj_inputs,
+    QueryInputs,
+    make_query_inputs,
 )

@@ -367,3 +367,38 @@ def make_oproj_inputs(dims=DSV2, batch=32, seed=0):
     o = rng.standard_normal((batch, dims.num_heads, dims.d_v))
     w_o = rng.standard_normal((dims.hidden, k)) * (1.0 / math.sqrt(k) if dims == TINY else 0.006)
     return _store(o, store), _store(w_o, store)
+
+
+@dataclass
+class QueryInputs:
+    """Inputs of the query of one new token per sequence."""
+    dims: Dims
+    d_qlatent: int
+    h: torch.Tensor            # [B, hidden] bf16
+    w_dq: torch.Tensor         # [d_qlatent, hidden]
+    w_uq: torch.Tensor         # [H * d_nope, d_qlatent]
+    w_qr: torch.Tensor         # [H * d_rope, d_qlatent]
+    gain: Optional[torch.Tensor]   # [d_qlatent] or None
+    positions: np.ndarray      # int32 [B]
+    eps: float = 1e-6
+
+
+def make_query_inputs(dims=DSV2, batch=32, seed=0, d_qlatent=1536, max_position=4096, with_gain=False,
+                      positions=None):
+    """Hidden states N(0, 1); W_DQ, W_UQ, W_QR N(0, 0.006^2) (the paper's
+    initialisation; d'_c = 1536 in DeepSeek-V2); an optional norm gain
+    1 + N(0, 0.1^2); positions uniform on [0, max_position). Drawn in that
+    order from default_rng(seed), stored in bf16."""
+    rng = np.random.default_rng(seed)
+    H, dn, dr, hid = dims.num_heads, dims.d_nope, dims.d_rope, dims.hidden
+    h = rng.standard_normal((batch, hid))
+    w_dq = rng.standard_normal((d_qlatent, hid)) * 0.006
+    w_uq = rng.standard_normal((H * dn, d_qlatent)) * 0.006
+    w_qr = rng.standard_normal((H * dr, d_qlatent)) * 0.006
+    gain = 1.0 + 0.1 * rng.standard_normal(d_qlatent) if with_gain else None
+    pos = rng.integers(0, max_position, size=batch)
+    if positions is not None:
+        pos = np.asarray(positions, dtype=np.int64)
+    return QueryInputs(dims=dims, d_qlatent=d_qlatent, h=_store(h, "bf16"), w_dq=_store(w_dq, "bf16"),
+                       w_uq=_store(w_uq, "bf16"), w_qr=_store(w_qr, "bf16"),
+                       gain=None if gain is None else _store(gain, "bf16"), positions=pos.astype(np.int32))

@@ -203,9 +203,10 @@ def test_cache_append_argument_errors(L):
     assert ws == 20 * 4 * 576 * 4                     # 256-wide slices of the hidden size
 
     def f(dims=d, batch=4, hidden=5120, h=P, w1=P, w2=P, gain=None, dtype=mla.BF16, eps=1e-6, base=1e4,
-          pos=P, cache=None, work=P, work_bytes=ws):
+          pos=P, cache=None, work=P, work_bytes=ws, rope=None):
         cache = _cache(seq_stride=64) if cache is None else cache
-        return L.mla_cache_append(dims, batch, hidden, h, w1, w2, gain, dtype, eps, base, pos,
+        rope = mla.Rope(base, 1.0, 1.0, 32.0, 4096) if rope is None else rope
+        return L.mla_cache_append(dims, batch, hidden, h, w1, w2, gain, dtype, eps, ctypes.byref(rope), pos,
                                   ctypes.byref(cache), work, work_bytes, None)
     assert f(dims=None) == -1
     assert f(batch=-1) == -2
@@ -223,6 +224,13 @@ def test_cache_append_argument_errors(L):
     assert f(cache=_cache(row_stride=575, seq_stride=64)) == -2
     assert f(h=P + 2) == -5 and f(work=P + 4) == -5
     assert f(batch=0, h=None, w1=None, w2=None, pos=None, work=None) == 0
+    # rotary parameters: YaRN needs s >= 1, alpha < beta and an original context
+    assert f(rope=mla.Rope(1e4, 0.5, 1.0, 32.0, 4096)) == -2
+    assert f(rope=mla.Rope(1e4, 40.0, 32.0, 32.0, 4096)) == -2
+    assert f(rope=mla.Rope(1e4, 40.0, 1.0, 32.0, 0)) == -2
+    assert f(rope=mla.Rope(float("inf"), 1.0, 1.0, 32.0, 4096)) == -2
+    assert L.mla_cache_append(d, 4, 5120, P, P, P, None, mla.BF16, 1e-6, None, P,
+                              ctypes.byref(_cache(seq_stride=64)), P, ws, None) == -1
 
 
 @no_gpu
@@ -233,7 +241,8 @@ def test_cache_append_noalloc_argument_errors(L):
 
     def f(dims=d, batch=4, hidden=5120, h=P, w1=P, w2=P, dtype=mla.BF16, pos=P, cache=None):
         cache = _cache(seq_stride=64) if cache is None else cache
-        return L.mla_cache_append_noalloc(dims, batch, hidden, h, w1, w2, None, dtype, 1e-6, 1e4, pos,
+        return L.mla_cache_append_noalloc(dims, batch, hidden, h, w1, w2, None, dtype, 1e-6,
+                                          ctypes.byref(mla.Rope(1e4, 1.0, 1.0, 32.0, 4096)), pos,
                                           ctypes.byref(cache), None)
     assert f(dims=None) == -1
     assert f(batch=-1) == -2 and f(hidden=5128) == -2
@@ -264,3 +273,27 @@ def test_o_proj_argument_errors(L):
     assert f(nbytes=ws - 4) == -2
     assert f(w=P + 2) == -5 and f(work=P + 4) == -5
     assert f(batch=0, o=None, w=None, out=None, work=None) == 0
+
+
+@no_gpu
+def test_query_proj_argument_errors(L):
+    d = ctypes.byref(DSV2)
+    ws = mla.mla_query_proj_workspace(DSV2, 4, 5120, 1536)
+    # partial sums of W_DQ h (20 slices) and of the up-projections (6 slices), plus c_Q in bf16
+    assert ws == 20 * 4 * 1536 * 4 + 4 * 1536 * 2 + 6 * 4 * 128 * 192 * 4
+    assert mla.mla_query_proj_workspace(TINY, 4, 128, 256) == 0
+    yarn = mla.Rope(1e4, 40.0, 1.0, 32.0, 4096)
+
+    def f(dims=d, batch=4, hidden=5120, dq=1536, h=P, w_dq=P, gain=None, w_uq=P, w_qr=P, dtype=mla.BF16,
+          eps=1e-6, rope=yarn, pos=P, qn=P, qr=P, work=P, nbytes=ws):
+        return L.mla_query_proj(dims, batch, hidden, dq, h, w_dq, gain, w_uq, w_qr, dtype, eps,
+                                None if rope is None else ctypes.byref(rope), pos, qn, qr, work, nbytes, None)
+    assert f(dims=None) == -1 and f(rope=None) == -1
+    assert f(batch=-1) == -2 and f(hidden=5128) == -2 and f(dq=1000) == -2 and f(eps=-1.0) == -2
+    assert f(dims=ctypes.byref(TINY)) == -4 and f(dq=8192) == -4
+    assert f(dtype=mla.F32) == -3
+    assert f(rope=mla.Rope(1e4, 40.0, 5.0, 5.0, 4096)) == -2
+    assert f(h=None) == -1 and f(qr=None) == -1 and f(work=None) == -1 and f(pos=None) == -1
+    assert f(nbytes=ws - 4) == -2
+    assert f(w_uq=P + 2) == -5 and f(qn=P + 8) == -5
+    assert f(batch=0, h=None, w_dq=None, w_uq=None, w_qr=None, pos=None, qn=None, qr=None, work=None) == 0

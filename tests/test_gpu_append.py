@@ -27,7 +27,7 @@ def _gpu():
     mla.lib()     # fails loudly when the library is missing
 
 
-def _run(inp, kind="bf16", layout="contiguous", page_size=64, capacity=None, seed=7):
+def _run(inp, kind="bf16", layout="contiguous", page_size=64, capacity=None, seed=7, rotary=None):
     """Append into a cache filled with sentinels; return (written rows, cache, row index per sequence)."""
     import mla_latent_kv_28_amd as mla
     d, B, hid = inp.dims, inp.h.shape[0], inp.dims.hidden
@@ -62,21 +62,22 @@ def _run(inp, kind="bf16", layout="contiguous", page_size=64, capacity=None, see
     dt = mla.F32 if inp.dtype == "f32" else mla.BF16
     ws = torch.empty(mla.mla_cache_append_workspace(d, B, hid) // 4, dtype=torch.float32, device=dev)
     mla.mla_cache_append(d, B, hid, inp.h.to(dev), inp.w_dkv.to(dev), inp.w_kr.to(dev),
-                         None if inp.gain is None else inp.gain.to(dev), dt, inp.eps, inp.base,
-                         torch.from_numpy(inp.positions).to(dev), cache, ws)
+                         None if inp.gain is None else inp.gain.to(dev), dt, inp.eps,
+                         inp.base if rotary is None else rotary, torch.from_numpy(inp.positions).to(dev), cache, ws)
     torch.cuda.synchronize()
     rows_idx = [row_of(b, int(p)) if 0 <= p < cap else -1 for b, p in enumerate(inp.positions)]
     return [s.cpu() for s in store], rows_idx
 
 
-def _reference(inp):
+def _reference(inp, freqs=None):
     f = lambda t: None if t is None else t.double().numpy()
-    return oracle.append_entry(f(inp.h), f(inp.w_dkv), f(inp.w_kr), inp.positions, inp.eps, inp.base, f(inp.gain))
+    return oracle.append_entry(f(inp.h), f(inp.w_dkv), f(inp.w_kr), inp.positions, inp.eps, inp.base, f(inp.gain),
+                               freqs=freqs)
 
 
-def _check_dense(store, rows_idx, inp, rtol, atol):
+def _check_dense(store, rows_idx, inp, rtol, atol, freqs=None):
     rows = store[0].double().numpy()
-    c_ref, k_ref = _reference(inp)
+    c_ref, k_ref = _reference(inp, freqs)
     d = inp.dims
     written = [r for r in rows_idx if r >= 0]
     for b, r in enumerate(rows_idx):
@@ -110,6 +111,17 @@ def test_dsv2_positions_outside_the_cache_write_nothing():
     _check_dense(store, idx, inp, 2.0 ** -8, 1e-4)
     store, idx = _run(inp, "bf16", capacity=64)
     _check_dense(store, idx, inp, 2.0 ** -8, 1e-4)
+
+
+def test_dsv2_bf16_yarn_rotation():
+    # the rotary key with the YaRN frequencies of a length-extended model
+    # (s = 40, alpha = 1, beta = 32, 4K original context)
+    import mla_latent_kv_28_amd as mla
+    inp = make_append_inputs(DSV2, batch=8, seed=8, max_position=9000)
+    rope = mla.Rope(inp.base, 40.0, 1.0, 32.0, 4096)
+    freqs = oracle.rope_frequencies(DSV2.d_rope, inp.base, 40.0, 1.0, 32.0, 4096)
+    store, idx = _run(inp, "bf16", layout="paged", page_size=64, rotary=rope)
+    _check_dense(store, idx, inp, 2.0 ** -8, 1e-4, freqs=freqs)
 
 
 def test_tiny_f32():
