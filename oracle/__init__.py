@@ -16,6 +16,7 @@ from .mla import (  # noqa: F401
     attend_absorbed,
     decode,
     decode_one,
+    decode_multi,
     decode_heads,
     gather_rows,
     lse_merge,

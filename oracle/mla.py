@@ -164,6 +164,32 @@ def decode_heads(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, heads
                               _f64(w_uk)[hs], _f64(w_uv)[hs], sm_scale)
 
 
+def decode_multi(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, n):
+    """Decode of n new tokens per sequence in one pass: o [B n, H, d_v] and
+    lse [B n, H]; query row b n + t is token t of sequence b.
+
+    DeepSeek-V3 blog (third page), section 3 "multi-token prediction": the
+    model proposes several future tokens at once, so a decode step scores n
+    tokens of one sequence together. The pages give no formula; the reading
+    here is causal attention: the n tokens' own cache entries are appended
+    first (seq_lens[b] counts them), token t sits at position
+    seq_lens[b] - n + t and attends to cache rows 0 .. seq_lens[b] - n + t
+    (its own included, the later ones masked). A token with no row left
+    (seq_lens[b] < n - t) gives o = 0 and lse = -inf. n = 1 is `decode`.
+    """
+    q_nope, q_rope = _f64(q_nope), _f64(q_rope)
+    BN, H, _ = q_nope.shape
+    d_v = np.shape(w_uv)[1]
+    o = np.zeros((BN, H, d_v))
+    lse = np.zeros((BN, H))
+    for bv in range(BN):
+        b, t = divmod(bv, n)
+        length = max(0, int(seq_lens[b]) - (n - 1 - t))
+        c_kv, k_rope = gather_rows(cache, b, length)
+        o[bv], lse[bv] = attend_nonabsorbed(c_kv, k_rope, q_nope[bv], q_rope[bv], w_uk, w_uv, sm_scale)
+    return o, lse
+
+
 def decode_one(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, h):
     """One (sequence, head) output of `decode`: (o [d_v], lse)."""
     o, lse = decode_heads(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, [h])

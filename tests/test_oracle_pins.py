@@ -617,3 +617,81 @@ def test_append_entry_with_frequencies():
     _, k2 = oracle.append_entry(h, w_dkv, w_kr, pos, 1e-6, 10000.0, freqs=f)
     np.testing.assert_allclose(k2, oracle.rope_with(h @ w_kr.T, pos, f), rtol=1e-13)
     np.testing.assert_allclose(k2[0], (h @ w_kr.T)[0], rtol=1e-15)     # position 0: unrotated
+
+
+# --- several new tokens per sequence (causal over the appended tokens) ----------
+
+def _multi_case(rng, lens, n, H=3, d_c=12, d_nope=8, d_r=6, d_v=10, stride=13):
+    """Contiguous cache with sequence b at rows b * stride .., n queries per
+    sequence (row b n + t), distinct widths."""
+    B = len(lens)
+    rows = np.full((B * stride, d_c + d_r), np.nan)
+    for b, L in enumerate(lens):
+        rows[b * stride:b * stride + L] = rng.standard_normal((L, d_c + d_r))
+    cache = dict(kind="dense", rows=rows, d_c=d_c, seq_stride=stride)
+    args = dict(
+        q_nope=rng.standard_normal((B * n, H, d_nope)),
+        q_rope=rng.standard_normal((B * n, H, d_r)),
+        w_uk=rng.standard_normal((H, d_nope, d_c)) / math.sqrt(d_c),
+        w_uv=rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c),
+        cache=cache, seq_lens=np.array(lens, dtype=np.int32),
+        sm_scale=1.0 / math.sqrt(d_nope + d_r),
+    )
+    return args, rows, d_c
+
+
+def test_multi_token_zero_query_averages_its_causal_prefix():
+    # q = 0: every visible row weighs the same, so token t of sequence b returns
+    # W_UV times the mean latent of rows 0 .. L_b - n + t and lse = log(count);
+    # a token that sees no row returns 0 and -inf
+    n, lens = 3, [7, 1, 3, 12]
+    args, rows, d_c = _multi_case(np.random.default_rng(41), lens, n)
+    args["q_nope"][:] = 0
+    args["q_rope"][:] = 0
+    o, lse = oracle.decode_multi(n=n, **args)
+    stride = args["cache"]["seq_stride"]
+    for b, L in enumerate(lens):
+        for t in range(n):
+            count = L - n + t + 1
+            bv = b * n + t
+            if count <= 0:
+                assert np.all(o[bv] == 0) and np.all(lse[bv] == -np.inf)
+                continue
+            mean_c = rows[b * stride:b * stride + count, :d_c].mean(axis=0)
+            for h in range(o.shape[1]):
+                np.testing.assert_allclose(o[bv, h], args["w_uv"][h] @ mean_c, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(lse[bv], math.log(count), rtol=1e-14)
+
+
+def test_multi_token_mask_hides_later_tokens_only():
+    # changing the row of token t + 1 (position L - n + t + 1) leaves tokens
+    # 0 .. t of that sequence and every other sequence unchanged, and changes
+    # tokens t + 1 .. n - 1
+    n, lens = 4, [9, 6]
+    args, rows, d_c = _multi_case(np.random.default_rng(42), lens, n)
+    o0, l0 = oracle.decode_multi(n=n, **args)
+    b, t = 1, 1
+    pos = lens[b] - n + t + 1
+    rows[b * args["cache"]["seq_stride"] + pos] += 3.0
+    o1, l1 = oracle.decode_multi(n=n, **args)
+    for bv in range(len(lens) * n):
+        same = bv // n != b or bv % n <= t
+        assert np.array_equal(o0[bv], o1[bv]) == same
+        assert np.array_equal(l0[bv], l1[bv]) == same
+
+
+def test_multi_token_last_token_and_single_token_equal_decode():
+    # the last of the n tokens sees the whole sequence: it is `decode` with its
+    # own query; n = 1 is `decode` itself
+    n, lens = 3, [5, 11, 2]
+    args, _, _ = _multi_case(np.random.default_rng(43), lens, n)
+    o, lse = oracle.decode_multi(n=n, **args)
+    last = dict(args, q_nope=args["q_nope"][n - 1::n], q_rope=args["q_rope"][n - 1::n])
+    o_d, l_d = oracle.decode(**last)
+    np.testing.assert_array_equal(o[n - 1::n], o_d)
+    np.testing.assert_array_equal(lse[n - 1::n], l_d)
+    args1, _, _ = _multi_case(np.random.default_rng(44), lens, 1)
+    o1, l1 = oracle.decode_multi(n=1, **args1)
+    o_d, l_d = oracle.decode(**args1)
+    np.testing.assert_array_equal(o1, o_d)
+    np.testing.assert_array_equal(l1, l_d)
