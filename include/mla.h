@@ -176,6 +176,28 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat,
                       void* out, float* lse, int32_t out_dtype, mla_stream stream);
 
 /*
+ * Attention of n = tokens_per_seq new tokens per sequence in one pass (the
+ * DeepSeek-V3 blog, section 3 on multi-token prediction: several future tokens
+ * of one sequence are proposed together and scored together). Causal: the n
+ * tokens' own cache rows are appended before the call and counted in
+ * seq_lens[b]; token t of sequence b sits at position seq_lens[b] - n + t and
+ * attends to the rows of tokens 0 .. seq_lens[b] - n + t (clamped to
+ * [0, max_seq_len]; a token that sees no row yields out = 0, lse = -inf).
+ *   batch    sequences B; the query rows are B n, row b n + t for token t.
+ *   q_lat    [B n, H, d_latent + d_rope];
+ *   seq_lens [B] (per sequence, as in mla_decode);
+ *   out, lse as in mla_decode with B n rows: [B n, H, d_latent] and [B n, H]
+ *            for S == 1, [B n, S, H, d_latent] and [B n, S, H] partials for
+ *            S > 1 (mla_combine with batch B n merges them).
+ * Every other argument, limit and error is that of mla_decode, which this
+ * equals for tokens_per_seq == 1. tokens_per_seq < 1 is MLA_ERR_SHAPE.
+ */
+mla_status mla_decode_multi(const mla_dims* dims, int32_t batch, int32_t tokens_per_seq,
+                            const void* q_lat, const mla_kv_cache* cache, const int32_t* seq_lens,
+                            int32_t max_seq_len, float sm_scale, int32_t num_splits, void* out,
+                            float* lse, int32_t out_dtype, mla_stream stream);
+
+/*
  * Log-sum-exp merge of split partials (the split-KV pass of mla_decode):
  *   lse[b,h] = log sum_s exp(lse_part[b,s,h]),
  *   out[b,h] = sum_s exp(lse_part[b,s,h] - lse[b,h]) * o_part[b,s,h,:].

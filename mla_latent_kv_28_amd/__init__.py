@@ -20,7 +20,7 @@ _STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DT
            -4: "MLA_ERR_UNSUPPORTED", -5: "MLA_ERR_ALIGN", -6: "MLA_ERR_HIP"}
 
 # Every symbol include/mla.h declares.
-EXPORTS = ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
+EXPORTS = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
            "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error",
            "mla_time_next_launch",
            "mla_cache_append", "mla_cache_append_workspace", "mla_cache_append_noalloc",
@@ -76,6 +76,8 @@ def lib():
         pd = ctypes.POINTER(Dims)
         L.mla_absorb_q.argtypes = [pd, i32, vp, vp, vp, vp, i32, vp]
         L.mla_decode.argtypes = [pd, i32, vp, ctypes.POINTER(KVCache), vp, i32, f32, i32, vp, vp, i32, vp]
+        L.mla_decode_multi.argtypes = [pd, i32, i32, vp, ctypes.POINTER(KVCache), vp, i32, f32, i32, vp, vp, i32,
+                                       vp]
         L.mla_combine.argtypes = [pd, i32, i32, vp, i32, vp, vp, vp, i32, vp]
         L.mla_out_proj.argtypes = [pd, i32, vp, i32, vp, i32, vp, i32, vp]
         L.mla_combine_out_proj.argtypes = [pd, i32, i32, vp, i32, vp, vp, i32, vp, i32, vp, vp]
@@ -102,7 +104,7 @@ def lib():
         L.mla_query_proj_workspace.restype = i64
         L.mla_query_proj.argtypes = [pd, i32, i32, i32, vp, vp, vp, vp, vp, i32, f32, pr, vp, vp, vp, vp, i64, vp]
         L.mla_query_proj.restype = i32
-        for name in ("mla_absorb_q", "mla_decode", "mla_combine", "mla_out_proj", "mla_split_chunk",
+        for name in ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_combine", "mla_out_proj", "mla_split_chunk",
                      "mla_suggest_splits", "mla_last_hip_error", "mla_combine_out_proj",
                      "mla_time_next_launch"):
             getattr(L, name).restype = i32
@@ -184,6 +186,27 @@ def mla_decode(dims, batch, q_lat, cache, seq_lens, max_seq_len, sm_scale, num_s
         _dev(lse, "lse", torch.float32, batch * parts * H),
         out_dtype, _stream(stream))
     _check(st, "mla_decode")
+
+
+def mla_decode_multi(dims, batch, tokens_per_seq, q_lat, cache, seq_lens, max_seq_len, sm_scale, num_splits,
+                     out, lse, out_dtype, stream=None):
+    """mla_decode with tokens_per_seq causal query tokens per sequence:
+    q_lat [batch * n, H, 576], out/lse with batch * n rows, seq_lens [batch]."""
+    d = dims_of(dims)
+    H = d.num_heads
+    q_dtype = torch.float32 if cache.dtype == F32 else torch.bfloat16
+    parts = num_splits if num_splits > 1 else 1
+    rows = batch * max(tokens_per_seq, 0)
+    st = lib().mla_decode_multi(
+        ctypes.byref(d), batch, tokens_per_seq,
+        _dev(q_lat, "q_lat", q_dtype, rows * H * (d.d_latent + d.d_rope)),
+        ctypes.byref(cache),
+        _dev(seq_lens, "seq_lens", torch.int32, batch),
+        max_seq_len, float(sm_scale), num_splits,
+        _dev(out, "out", _TORCH_DTYPE.get(out_dtype), rows * parts * H * d.d_latent),
+        _dev(lse, "lse", torch.float32, rows * parts * H),
+        out_dtype, _stream(stream))
+    _check(st, "mla_decode_multi")
 
 
 def mla_combine(dims, batch, num_splits, o_part, part_dtype, lse_part, out, lse, out_dtype,

@@ -109,9 +109,22 @@ struct SeqView {
   const int32_t* bt_row;    // paged: the sequence's block-table row
 };
 
+// Query row bv = b n + t (n query tokens per sequence): the cache sequence b
+// whose rows it reads, and how many of them it attends to (token t sees rows
+// 0 .. L_b - n + t, so one query token per sequence sees all L_b).
+__device__ __forceinline__ int cache_seq(const DecodeParams& p, int bv) {
+  return p.tokens_per_seq > 1 ? bv / p.tokens_per_seq : bv;
+}
+__device__ __forceinline__ int query_len(const DecodeParams& p, int bv) {
+  if (p.tokens_per_seq <= 1) return p.seq_lens[bv];
+  const int n = p.tokens_per_seq, b = bv / n;
+  return p.seq_lens[b] - (n - 1 - (bv - b * n));
+}
+
 template <bool PAGED>
-__device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int b) {
+__device__ __forceinline__ SeqView seq_view(const DecodeParams& p, int bv) {
   SeqView v;
+  const int b = cache_seq(p, bv);
   v.seq_row = PAGED ? 0 : (int64_t)b * p.seq_stride;
   v.bt_row = PAGED ? p.block_table + (int64_t)b * p.max_pages : nullptr;
   return v;
@@ -1102,7 +1115,7 @@ struct SeqCounts {
 __device__ __forceinline__ SeqCounts seq_counts(const DecodeParams& p, int b) {
   SeqCounts c{0, 0, 0, -1, 0};
   if (b < p.batch) {
-    c.len = p.seq_lens[b];
+    c.len = query_len(p, b);
     const int L = p.chunk > 0 ? max(0, min(c.len, p.max_seq_len)) : 0;
     if (L > 0) {
       c.full = min(L / p.chunk, p.num_splits);
@@ -1194,7 +1207,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
     if (p.order == kOrderXcd) w = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     b = w / p.num_splits;
     split = w % p.num_splits;
-    len_b = p.seq_lens[b];   // a scalar load, requested before the loads into LDS
+    len_b = query_len(p, b);   // a scalar load, requested before the loads into LDS
   }
   MLA_LDS char* lds = (MLA_LDS char*)smem;
   auto slot = [&](int x) -> MLA_LDS char* {   // x >= 0
@@ -1220,7 +1233,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   if constexpr (PAGED && STREAM) {
     tbase.shift = p.page_shift;
     tbase.lp0 = (split * p.chunk) >> p.page_shift;
-    const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+    const int32_t* bt = p.block_table + (int64_t)cache_seq(p, b) * p.max_pages;
     tbase.pages = bt[min(tbase.lp0 + (int)(threadIdx.x & 63), p.max_pages - 1)];
   }
 

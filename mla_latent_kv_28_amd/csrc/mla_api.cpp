@@ -157,11 +157,16 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_nope,
                                        : mla::launch_absorb_tiny_f32(p, s));
 }
 
-mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_kv_cache* cache,
-                      const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, int32_t num_splits,
-                      void* out, float* lse, int32_t out_dtype, mla_stream stream) {
+namespace {
+
+// mla_decode over `batch` sequences with n query tokens each (query rows
+// b n + t); n = 1 is the one-token decode.
+mla_status decode_tokens(const mla_dims* dims, int32_t batch, int32_t n, const void* q_lat,
+                         const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                         int32_t num_splits, void* out, float* lse, int32_t out_dtype, mla_stream stream) {
   if (dims == nullptr || cache == nullptr) return MLA_ERR_NULL;
-  if (batch < 0 || max_seq_len < 0 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (batch < 0 || n < 1 || max_seq_len < 0 || num_splits < 1) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * n > 0x7fffffff) return MLA_ERR_SHAPE;
   if (!valid_dtype(cache->dtype) || (out_dtype != MLA_F32 && out_dtype != MLA_BF16)) return MLA_ERR_DTYPE;
   const Shape sh = shape_of(dims);
   if (sh == Shape::kNone) return MLA_ERR_UNSUPPORTED;
@@ -195,7 +200,7 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, co
   }
   if (!aligned16(q_lat) || !aligned16(cache->latent) || !aligned16(out) || !aligned16(lse))
     return MLA_ERR_ALIGN;
-  if (static_cast<int64_t>(batch) * num_splits > 0x7fffffff) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * n * num_splits > 0x7fffffff) return MLA_ERR_SHAPE;
   // the fixed-reference softmax keeps its sums finite for at most 2^17 tokens a chunk
   if (mla_split_chunk(max_seq_len, num_splits) > (1 << 17)) return MLA_ERR_UNSUPPORTED;
 
@@ -211,7 +216,8 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, co
   p.max_pages = cache->max_pages_per_seq;
   p.page_shift = paged ? log2i(cache->page_size) : -1;
   p.seq_lens = seq_lens;
-  p.batch = batch;
+  p.batch = batch * n;
+  p.tokens_per_seq = n;
   p.max_seq_len = max_seq_len;
   p.num_splits = num_splits;
   p.chunk = mla_split_chunk(max_seq_len, num_splits);
@@ -225,6 +231,23 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, co
   else if (fp8) e = mla::launch_decode_dsv2_fp8(p, s);
   else e = mla::launch_decode_dsv2_bf16(p, s);
   return hip_status(e);
+}
+
+}  // namespace
+
+mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_lat, const mla_kv_cache* cache,
+                      const int32_t* seq_lens, int32_t max_seq_len, float sm_scale, int32_t num_splits,
+                      void* out, float* lse, int32_t out_dtype, mla_stream stream) {
+  return decode_tokens(dims, batch, 1, q_lat, cache, seq_lens, max_seq_len, sm_scale, num_splits, out, lse,
+                       out_dtype, stream);
+}
+
+mla_status mla_decode_multi(const mla_dims* dims, int32_t batch, int32_t tokens_per_seq, const void* q_lat,
+                            const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                            float sm_scale, int32_t num_splits, void* out, float* lse, int32_t out_dtype,
+                            mla_stream stream) {
+  return decode_tokens(dims, batch, tokens_per_seq, q_lat, cache, seq_lens, max_seq_len, sm_scale, num_splits,
+                       out, lse, out_dtype, stream);
 }
 
 mla_status mla_combine(const mla_dims* dims, int32_t batch, int32_t num_splits, const void* o_part,

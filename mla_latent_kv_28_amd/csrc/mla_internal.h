@@ -33,6 +33,10 @@ struct DecodeParams {
   float* lse;                   // S == 1: [B, H]; S > 1: [B, S, H]
   int32_t out_bf16;             // out is bf16 (else f32)
   int32_t order;                // DecodeOrder: which item each workgroup takes
+  // Query tokens per sequence (n >= 1). `batch` counts query rows bv = b n + t
+  // (q_lat, out and lse are indexed by bv); the cache and seq_lens by b; token
+  // t of sequence b attends to rows 0 .. seq_lens[b] - n + t.
+  int32_t tokens_per_seq;
 };
 
 // Decode launchers: return the hipError_t of the launch.

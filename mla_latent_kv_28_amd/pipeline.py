@@ -7,7 +7,7 @@ the current stream. Allocation happens once, in the constructor.
 import torch
 
 from . import (BF16, F32, FP8_E4M3, kv_cache, mla_absorb_q, mla_combine, mla_combine_out_proj,
-               mla_decode, mla_out_proj, mla_suggest_splits)
+               mla_decode, mla_decode_multi, mla_out_proj, mla_suggest_splits)
 
 NUM_CUS = 256
 
@@ -24,13 +24,21 @@ class DecodePipeline:
     fuse:        with several splits of bf16 partials at the DeepSeek-V2 shape,
                  run merge and out-proj as one call (mla_combine_out_proj; o_lat
                  is then not written).
+    tokens_per_seq: n new tokens per sequence scored together, causally
+                 (mla_decode_multi); q_nope / q_rope then hold batch * n rows,
+                 row b n + t for token t, and so do the outputs.
     """
 
     def __init__(self, inp, num_splits=None, o_lat_dtype=None, out_dtype=None, device="cuda",
-                 fuse=True):
+                 fuse=True, tokens_per_seq=None):
         d = inp.dims
         self.dims = d
-        self.batch = inp.batch
+        self.seqs = inp.batch
+        self.tokens_per_seq = int(getattr(inp, "tokens_per_seq", 1) if tokens_per_seq is None else tokens_per_seq)
+        self.batch = inp.batch * self.tokens_per_seq     # query rows
+        if inp.q_nope.shape[0] != self.batch or inp.q_rope.shape[0] != self.batch:
+            raise ValueError("queries hold %d rows, expected %d sequences x %d tokens"
+                             % (inp.q_nope.shape[0], inp.batch, self.tokens_per_seq))
         self.max_seq_len = inp.max_seq_len
         self.sm_scale = inp.sm_scale
         self.compute = F32 if inp.dtype == "f32" else BF16
@@ -61,7 +69,8 @@ class DecodePipeline:
 
         if num_splits is None:
             num_splits = inp.splits or mla_suggest_splits(
-                self.batch, self.max_seq_len, int(inp.seq_lens.astype("int64").sum()), NUM_CUS)
+                self.batch, self.max_seq_len,
+                int(inp.seq_lens.astype("int64").sum()) * self.tokens_per_seq, NUM_CUS)
         self.num_splits = int(num_splits)
         B, H, S = self.batch, d.num_heads, self.num_splits
         cdt = torch.float32 if self.compute == F32 else torch.bfloat16
@@ -84,13 +93,16 @@ class DecodePipeline:
                      self.compute, stream)
 
     def decode(self, stream=None):
-        if self.num_splits > 1:
-            mla_decode(self.dims, self.batch, self.q_lat, self.cache, self.seq_lens,
-                       self.max_seq_len, self.sm_scale, self.num_splits, self.o_part,
-                       self.lse_part, self.o_lat_dtype, stream)
+        split = self.num_splits > 1
+        out = self.o_part if split else self.o_lat
+        lse = self.lse_part if split else self.lse
+        if self.tokens_per_seq > 1:
+            mla_decode_multi(self.dims, self.seqs, self.tokens_per_seq, self.q_lat, self.cache, self.seq_lens,
+                             self.max_seq_len, self.sm_scale, self.num_splits, out, lse, self.o_lat_dtype,
+                             stream)
         else:
             mla_decode(self.dims, self.batch, self.q_lat, self.cache, self.seq_lens,
-                       self.max_seq_len, self.sm_scale, 1, self.o_lat, self.lse,
+                       self.max_seq_len, self.sm_scale, self.num_splits, out, lse,
                        self.o_lat_dtype, stream)
 
     def combine(self, stream=None):

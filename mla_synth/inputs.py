@@ -142,6 +142,7 @@ class Inputs:
     scale: Optional[torch.Tensor] = None       # fp8: float32 [R]
     rope: Optional[torch.Tensor] = None        # fp8: bf16 [R, d_rope]
     splits: int = 0            # suggested split count (0 = choose)
+    tokens_per_seq: int = 1    # query rows per sequence (q_* hold batch * n rows)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -178,7 +179,7 @@ def _lengths(spec, batch, rng_len, override):
 
 def make_inputs(name, seed=0, batch=None, seq_lens=None, layout=None, page_size=None,
                 dtype=None, q_scale=1.0, pad_fill=0.0, len_seed=None, sm_scale=None,
-                seq_stride=None):
+                seq_stride=None, tokens_per_seq=1):
     """Build one workload's inputs on the host.
 
     Overrides (for smaller parity cases and stress variants): batch,
@@ -186,7 +187,9 @@ def make_inputs(name, seed=0, batch=None, seq_lens=None, layout=None, page_size=
     before rounding; 30 gives peaked attention), pad_fill (value written into
     cache rows that no sequence owns: padding of a contiguous cache and the
     tail of a sequence's last page; NaN checks that masked rows never leak),
-    sm_scale, seq_stride.
+    sm_scale, seq_stride, tokens_per_seq (n query rows per sequence, row
+    b n + t rotated at position L_b - n + t: the newest n tokens of each
+    sequence; DeepSeek-V2 shape only).
     """
     w = dict(WORKLOADS[name])
     dims = w["dims"]
@@ -208,7 +211,7 @@ def make_inputs(name, seed=0, batch=None, seq_lens=None, layout=None, page_size=
     # --- per-sequence latent and rotary rows --------------------------------
     seq_rows = []
     if dims == TINY:
-        assert batch == 1, "the tiny workload has one sequence"
+        assert batch == 1 and tokens_per_seq == 1, "the tiny workload has one sequence and one query"
         L = int(lens[0])
         h = rng.standard_normal((max(L, 1), hid))
         w_dkv = rng.standard_normal((dc, hid)) / math.sqrt(hid)
@@ -228,15 +231,18 @@ def make_inputs(name, seed=0, batch=None, seq_lens=None, layout=None, page_size=
             c = rms_normalise(rng.standard_normal((L, dc)))
             r = rope_rotate(rng.standard_normal((L, dr)), np.arange(L))
             seq_rows.append(np.concatenate([c, r], axis=1))
+        n = int(tokens_per_seq)
         w_q = rng.standard_normal((H * (dn + dr), hid)) * 0.006
-        h = rng.standard_normal((batch, hid))
-        q = (h @ w_q.T).reshape(batch, H, dn + dr)
+        h = rng.standard_normal((batch * n, hid))
+        q = (h @ w_q.T).reshape(batch * n, H, dn + dr)
         del w_q
         w_uk = rng.standard_normal((H, dn, dc)) * 0.006
         w_uv = rng.standard_normal((H, dv, dc)) * 0.006
         q_nope = q[:, :, :dn]
-        q_rope = np.stack([rope_rotate(q[b, :, dn:], np.full(H, max(int(lens[b]), 1) - 1))
-                           for b in range(batch)])
+        q_rope = np.stack([rope_rotate(q[r, :, dn:],
+                                       np.full(H, max(int(lens[r // n]) - n + r % n, 0) if n > 1
+                                               else max(int(lens[r]), 1) - 1))
+                           for r in range(batch * n)])
 
     q_nope = q_nope * q_scale
     q_rope = q_rope * q_scale
@@ -290,7 +296,7 @@ def make_inputs(name, seed=0, batch=None, seq_lens=None, layout=None, page_size=
         w_uk=_store(w_uk, store), w_uv=_store(w_uv, store),
         rows=rows, layout=layout, seq_stride=stride if layout == "contiguous" else 0,
         page_size=page_size if layout == "paged" else 0, block_table=block_table,
-        splits=w.get("splits", 0),
+        splits=w.get("splits", 0), tokens_per_seq=int(tokens_per_seq),
     )
     if dtype == "fp8":
         inp.codes, inp.scale, inp.rope = quantise_rows_e4m3(rows, dc)

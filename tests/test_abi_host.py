@@ -143,6 +143,23 @@ def test_decode_argument_errors(L):
 
 
 @no_gpu
+def test_decode_multi_argument_errors(L):
+    def multi(n, batch=1, splits=1, **kw):
+        cache = _cache(**kw)
+        return L.mla_decode_multi(ctypes.byref(DSV2), batch, n, P, ctypes.byref(cache), P, 4096, 0.07, splits,
+                                  P, P, mla.BF16, None)
+    assert L.mla_decode_multi(None, 1, 2, P, None, P, 1, 1.0, 1, P, P, 1, None) == -1
+    assert multi(0) == -2                                # at least one token per sequence
+    assert multi(-3) == -2
+    assert multi(2, batch=-1) == -2
+    assert multi(1 << 16, batch=1 << 15) == -2           # 2^31 query rows
+    assert multi(1 << 12, batch=1 << 10, splits=1 << 9) == -2   # rows x splits beyond 2^31
+    assert multi(4, batch=0) == 0                        # no sequences: nothing to do
+    assert multi(4, row_stride=580) == -5                # the decode's own checks apply
+    assert multi(4, seq_stride=4095) == -2
+
+
+@no_gpu
 def test_absorb_combine_outproj_argument_errors(L):
     d = ctypes.byref(DSV2)
     assert L.mla_absorb_q(None, 1, P, P, P, P, mla.BF16, None) == -1
