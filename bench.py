@@ -284,6 +284,25 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def read_probe_gbps(nbytes=1 << 30, reps=20):
+        """Read bandwidth of a plain streaming read (mla_read_probe) of a
+        1 GiB buffer, 20 back-to-back launches between two events."""
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        sink = torch.zeros(4, dtype=torch.float32, device=dev)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                mla.mla_read_probe(buf, sink, stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                mla.mla_read_probe(buf, sink, stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        del buf, sink
+        return nbytes / (ms * 1e-3) / 1e9
+
     def in_step_kernel_times(n):
         """The decode kernel's execution time, and that of the rest of the step
         (split merge and out-projection, one fused call where the pipeline uses
@@ -324,6 +343,7 @@ def main():
         return sum(decs) / n, rest, pct
 
     torch.cuda.synchronize()
+    probe_gbps = read_probe_gbps()
     ms_step, nsteps = timed("step", step, args.steps, args.warmup)
     ms_dec, ms_rest, dec_pct = in_step_kernel_times(max(args.steps, 100))
 
@@ -364,6 +384,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps_dec / HBM_PEAK_GBPS, 4),
+            "achievable_read_GBps": round(probe_gbps, 1),
+            "frac_of_measured": round(gbps_dec / probe_gbps, 4),
+            "achievable_read_probe": "mla_read_probe: streaming 16-byte nontemporal loads over a 1 GiB buffer, "
+                                     "20 back-to-back launches between two events",
             "traffic": hbm_traffic(inp.name) if S == 8 else None,
             "us_per_launch": round(ms_dec * 1e3, 3),
             "us_per_launch_p10_p50_p90": [round(dec_pct[q] * 1e3, 3) for q in (10, 50, 90)],

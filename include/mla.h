@@ -384,6 +384,19 @@ int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tok
  */
 mla_status mla_time_next_launch(void* start_event, void* stop_event);
 
+/*
+ * Measurement helper, not part of the decode path: one streaming read of
+ * `bytes` of device memory at `buf` with plain 16-byte vector loads, so that
+ * a caller can time it (mla_time_next_launch) and report the decode's cache
+ * bandwidth against what a read achieves on this device as well as against
+ * the published peak. bytes: a multiple of 16 (0 is a no-op); buf: 16-byte
+ * aligned; sink: 4 device bytes the kernel writes only if the XOR of all
+ * data equals one fixed constant (so the reads cannot be optimised away).
+ * Errors: NULL buf or sink MLA_ERR_NULL, bytes < 0 or not a multiple of 16
+ * MLA_ERR_SHAPE, misaligned buf MLA_ERR_ALIGN.
+ */
+mla_status mla_read_probe(const void* buf, int64_t bytes, void* sink, mla_stream stream);
+
 /* Static, never-NULL description of a status code. */
 const char* mla_status_string(mla_status status);
 

@@ -22,7 +22,7 @@ _STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DT
 # Every symbol include/mla.h declares.
 EXPORTS = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_combine", "mla_out_proj", "mla_combine_out_proj",
            "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error",
-           "mla_time_next_launch",
+           "mla_time_next_launch", "mla_read_probe",
            "mla_cache_append", "mla_cache_append_workspace", "mla_cache_append_noalloc",
            "mla_o_proj", "mla_o_proj_workspace", "mla_query_proj", "mla_query_proj_workspace")
 
@@ -87,6 +87,7 @@ def lib():
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_last_hip_error.argtypes = []
         L.mla_time_next_launch.argtypes = [vp, vp]
+        L.mla_read_probe.argtypes = [vp, i64, vp, vp]
         L.mla_o_proj.argtypes = [pd, i32, i32, vp, vp, i32, vp, i32, vp, i64, vp]
         L.mla_o_proj.restype = i32
         L.mla_o_proj_workspace.argtypes = [pd, i32, i32]
@@ -106,7 +107,7 @@ def lib():
         L.mla_query_proj.restype = i32
         for name in ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_combine", "mla_out_proj", "mla_split_chunk",
                      "mla_suggest_splits", "mla_last_hip_error", "mla_combine_out_proj",
-                     "mla_time_next_launch"):
+                     "mla_time_next_launch", "mla_read_probe"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -207,6 +208,14 @@ def mla_decode_multi(dims, batch, tokens_per_seq, q_lat, cache, seq_lens, max_se
         _dev(lse, "lse", torch.float32, rows * parts * H),
         out_dtype, _stream(stream))
     _check(st, "mla_decode_multi")
+
+
+def mla_read_probe(buf, sink, stream=None):
+    """One streaming read of the whole device tensor `buf` (a measurement
+    helper: time it to get the read bandwidth this device achieves)."""
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().mla_read_probe(_dev(buf, "buf"), nbytes, _dev(sink, "sink"), _stream(stream))
+    _check(st, "mla_read_probe")
 
 
 def mla_combine(dims, batch, num_splits, o_part, part_dtype, lse_part, out, lse, out_dtype,

@@ -1509,6 +1509,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   }
 }
 
+}  // namespace
+
 // Compute units of the current device, queried once per device (the item
 // order only; any value gives correct results).
 int device_compute_units() {
@@ -1522,6 +1524,8 @@ int device_compute_units() {
   }
   return n;
 }
+
+namespace {
 
 template <class C, bool LF>
 hipError_t launch_order(const DecodeParams& q, int grid, hipStream_t stream) {

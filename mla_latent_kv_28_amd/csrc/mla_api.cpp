@@ -551,6 +551,14 @@ void take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
 }
 }  // namespace mla
 
+extern "C" mla_status mla_read_probe(const void* buf, int64_t bytes, void* sink, mla_stream stream) {
+  if (bytes < 0 || bytes % 16 != 0) return MLA_ERR_SHAPE;
+  if (bytes == 0) return MLA_OK;
+  if (!buf || !sink) return MLA_ERR_NULL;
+  if (!aligned16(buf)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_read_probe(buf, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream)));
+}
+
 extern "C" mla_status mla_time_next_launch(void* start_event, void* stop_event) {
   g_next_start = static_cast<hipEvent_t>(start_event);
   g_next_stop = static_cast<hipEvent_t>(stop_event);

@@ -39,6 +39,13 @@ struct DecodeParams {
   int32_t tokens_per_seq;
 };
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_compute_units();
+
+// Streaming read of `bytes` (a multiple of 16) from src; sink: 4 device bytes,
+// written only in the unlikely case that the XOR of the data equals a constant.
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Decode launchers: return the hipError_t of the launch.
 hipError_t launch_decode_dsv2_bf16(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_dsv2_fp8(const DecodeParams& p, hipStream_t s);

@@ -314,3 +314,13 @@ def test_query_proj_argument_errors(L):
     assert f(nbytes=ws - 4) == -2
     assert f(w_uq=P + 2) == -5 and f(qn=P + 8) == -5
     assert f(batch=0, h=None, w_dq=None, w_uq=None, w_qr=None, pos=None, qn=None, qr=None, work=None) == 0
+
+
+@no_gpu
+def test_read_probe_argument_errors(L):
+    assert L.mla_read_probe(P, 0, P, None) == 0            # nothing to read
+    assert L.mla_read_probe(P, -16, P, None) == -2
+    assert L.mla_read_probe(P, 24, P, None) == -2          # not a multiple of 16
+    assert L.mla_read_probe(None, 1 << 20, P, None) == -1
+    assert L.mla_read_probe(P, 1 << 20, None, None) == -1
+    assert L.mla_read_probe(P + 8, 1 << 20, P, None) == -5

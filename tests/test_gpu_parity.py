@@ -234,7 +234,19 @@ RISING_CASES = {
     "bf16_paged16": ("dsv2_b32_l4096", dict(seq_lens=[200, 77], layout="paged", page_size=16), {}, 1),
     "f32_tiny": ("tiny", dict(), dict(q_mult=6.0), 1),                              # per-row loop, fp32
     "bf16_contiguous_split": ("dsv2_b32_l4096", dict(seq_lens=[700, 300]), dict(period=128), 3),
+    "e4m3_contiguous": ("fp8_b128_l8192", dict(seq_lens=[200, 77]), {}, 1),          # e4m3 streaming loop
+    "e4m3_contiguous_split": ("fp8_b128_l8192", dict(seq_lens=[700, 300]), dict(period=128), 3),
+    "e4m3_paged64": ("fp8_b128_l8192", dict(seq_lens=[200, 77], layout="paged", page_size=64), {}, 1),
 }
+
+# The e4m3 cases are held to the fp8 path's own bound (relative L2 4e-2)
+# against the oracle on the dequantised cache: the streaming loop widens each
+# code times its scale to bf16 (one more rounding, relative 2^-9), and with
+# scores spread over a hundred base-2 units the softmax turns that rounding
+# into about 1e-2 of relative output error. They are not compared with the
+# cache before quantisation: e4m3's own rounding (relative 2^-4) moves such
+# scores by units, which changes the softmax by far more than 4e-2 whatever
+# the kernel does; that comparison is made on the fp8 workload's own inputs.
 
 
 @pytest.mark.parametrize("case", sorted(RISING_CASES))
@@ -254,14 +266,11 @@ def test_rising_scores_recompute_on_every_loop_form(case):
         _check(out, ref, F32_REL)
         _lse_check(lse, ref_lse, 1e-3)
     else:
-        _check(out, ref, BF16_REL)
+        _check(out, ref, FP8_REL if fp8 else BF16_REL)
         _lse_check(lse, ref_lse, 5e-2)
-    if fp8:
-        ref_b, _ = oracle.decode(**oracle_args(inp, "bf16"))
-        _check(out, ref_b, FP8_REL)
 
 
-@pytest.mark.parametrize("kind", ["bf16_contiguous", "bf16_paged64"])
+@pytest.mark.parametrize("kind", ["bf16_contiguous", "bf16_paged64", "e4m3_contiguous"])
 def test_rising_scores_recompute_longest_first_grid(kind):
     # 33 sequences x 8 splits = 264 items, more than the GPU's compute units:
     # the longest-first instance of the kernel; every split's scores rise
@@ -276,7 +285,7 @@ def test_rising_scores_recompute_longest_first_grid(kind):
     assert gap > HEADROOM + 8
     _, out, lse = _run(inp, num_splits=8)
     ref, ref_lse = oracle.decode(**oracle_args(inp, "dequantised"))
-    _check(out, ref, BF16_REL)
+    _check(out, ref, FP8_REL if inp.dtype == "fp8" else BF16_REL)
     _lse_check(lse, ref_lse, 5e-2)
 
 
