@@ -17,6 +17,7 @@ from .mla import (  # noqa: F401
     decode,
     decode_one,
     decode_multi,
+    prefill,
     decode_heads,
     gather_rows,
     lse_merge,

@@ -190,6 +190,47 @@ def decode_multi(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, n):
     return o, lse
 
 
+def prefill(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, n):
+    """Attention of n new tokens per sequence in the non-absorbed form, as a
+    prompt is processed: o [B n, H, d_v], lse [B n, H] (row b n + t = token t).
+
+    DeepSeek-V2 paper, section 2.1.2: keys and values are the up-projections
+    k^C = W_UK c_KV and v^C = W_UV c_KV of the cached latents; section 2.1.3:
+    each head's key is [k^C; k^R]. Here every cached row of a sequence is
+    up-projected once and each head runs causal softmax attention: token t
+    (position L_b - n + t) attends to rows 0 .. L_b - n + t, the same masking
+    as `decode_multi`, which reaches the same values without ever forming
+    per-token key sets. A token with no visible row gives o = 0, lse = -inf.
+    """
+    q_nope, q_rope = _f64(q_nope), _f64(q_rope)
+    w_uk, w_uv = _f64(w_uk), _f64(w_uv)
+    BN, H, d_nope = q_nope.shape
+    d_v, d_c = w_uv.shape[1], w_uv.shape[2]
+    B = BN // n
+    o = np.zeros((BN, H, d_v))
+    lse = np.full((BN, H), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        c_kv, k_rope = gather_rows(cache, b, L)
+        k_c = (c_kv @ w_uk.reshape(H * d_nope, d_c).T).reshape(L, H, d_nope)
+        v_c = (c_kv @ w_uv.reshape(H * d_v, d_c).T).reshape(L, H, d_v)
+        pos = L - n + np.arange(n)                              # position of each new token
+        visible = np.arange(L)[None, :] <= pos[:, None]         # [n, L] causal mask
+        rows = slice(b * n, (b + 1) * n)
+        for h in range(H):
+            k = np.concatenate([k_c[:, h, :], k_rope], axis=1)                     # [L, d_nope + d_r]
+            q = np.concatenate([q_nope[rows, h, :], q_rope[rows, h, :]], axis=1)   # [n, d_nope + d_r]
+            s = np.where(visible, sm_scale * (q @ k.T), -np.inf)                   # [n, L]
+            m = s.max(axis=1, initial=-np.inf)
+            has = np.isfinite(m)
+            e = np.where(visible, np.exp(s - np.where(has, m, 0.0)[:, None]), 0.0)
+            z = e.sum(axis=1)
+            zs = np.where(has, z, 1.0)
+            o[rows, h] = (e / zs[:, None]) @ v_c[:, h, :]
+            lse[rows, h] = np.where(has, m + np.log(zs), -np.inf)
+    return o, lse
+
+
 def decode_one(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, h):
     """One (sequence, head) output of `decode`: (o [d_v], lse)."""
     o, lse = decode_heads(q_nope, q_rope, w_uk, w_uv, cache, seq_lens, sm_scale, b, [h])

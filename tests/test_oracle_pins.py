@@ -695,3 +695,33 @@ def test_multi_token_last_token_and_single_token_equal_decode():
     o_d, l_d = oracle.decode(**args1)
     np.testing.assert_array_equal(o1, o_d)
     np.testing.assert_array_equal(l1, l_d)
+
+
+def test_prefill_equals_multi_token_decode_and_brute_force():
+    # prefill up-projects each sequence once and masks a score matrix; it must
+    # reach the values of decode_multi (pinned above), also when a prefix of
+    # older tokens precedes the n new ones and when a sequence is shorter than n
+    n, lens = 5, [9, 5, 3, 14]
+    args, rows, d_c = _multi_case(np.random.default_rng(45), lens, n, stride=16)
+    o, lse = oracle.prefill(n=n, **args)
+    o_m, l_m = oracle.decode_multi(n=n, **args)
+    np.testing.assert_allclose(o, o_m, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(np.isfinite(lse), np.isfinite(l_m))
+    np.testing.assert_allclose(lse[np.isfinite(lse)], l_m[np.isfinite(l_m)], rtol=1e-13)
+    # brute force, one (row, head): pure-Python sums over the visible rows
+    stride = args["cache"]["seq_stride"]
+    b, t, h = 3, 2, 1
+    L = lens[b]
+    count = L - n + t + 1
+    c = rows[b * stride:b * stride + count, :d_c]
+    kr = rows[b * stride:b * stride + count, d_c:]
+    qn, qr = args["q_nope"][b * n + t, h], args["q_rope"][b * n + t, h]
+    sc = [args["sm_scale"] * (sum(qn[i] * sum(args["w_uk"][h][i][k] * c[j][k] for k in range(d_c))
+                                   for i in range(len(qn))) + sum(qr[i] * kr[j][i] for i in range(len(qr))))
+          for j in range(count)]
+    w = [math.exp(x) for x in sc]
+    z = sum(w)
+    ref = [sum(w[j] / z * sum(args["w_uv"][h][v][k] * c[j][k] for k in range(d_c)) for j in range(count))
+           for v in range(args["w_uv"].shape[1])]
+    np.testing.assert_allclose(o[b * n + t, h], ref, rtol=1e-11, atol=1e-13)
+    assert lse[b * n + t, h] == pytest.approx(math.log(z), rel=1e-12)
