@@ -198,6 +198,42 @@ mla_status mla_decode_multi(const mla_dims* dims, int32_t batch, int32_t tokens_
                             float* lse, int32_t out_dtype, mla_stream stream);
 
 /*
+ * Prefill: the attention of n = tokens_per_seq new tokens per sequence in the
+ * non-absorbed form (DeepSeek-V2 paper, section 2.1.2: keys and values are
+ * the up-projections k^C = W_UK c_KV and v^C = W_UV c_KV; section 2.1.3: a
+ * head's key is [k^C ; k^R]), for scoring a prompt or a long chunk of new
+ * tokens, where up-projecting each cached row once is cheaper than absorbing
+ * W_UK into every query. Same causal rule as mla_decode_multi: the new
+ * tokens' rows are already in the cache and counted in seq_lens[b]; token t
+ * of sequence b sits at position seq_lens[b] - n + t and attends to rows
+ * 0 .. seq_lens[b] - n + t (a whole prompt: seq_lens[b] == n).
+ *   q_nope [B n, H, d_nope], q_rope [B n, H, d_rope] bf16 (RoPE applied;
+ *          row b n + t is token t of sequence b; mla_query_proj's output);
+ *   cache  a bf16 cache (contiguous or paged, any power-of-two page size);
+ *   seq_lens [B], clamped to [0, max_seq_len];
+ *   w_uk, w_uv [H, d_nope, d_latent] and [H, d_v, d_latent] bf16;
+ *   out    [B n, H, d_v] bf16: the per-head attention output o = sum_j p_j v^C_j
+ *          (W_UV already applied); lse [B n, H] f32 (natural log).
+ *   workspace: mla_prefill_workspace(dims, B, max_seq_len) bytes, 16-byte
+ *          aligned: the bf16 keys k^C and values v^C of every cached row
+ *          [2, B, H, ceil(max_seq_len / 128) * 128, d_nope]; its contents on
+ *          return are unspecified.
+ * Every cached row of a sequence (its first seq_lens[b] tokens) is
+ * up-projected by each call. A token that sees no row yields out = 0 and
+ * lse = -inf. Softmax in fp32 with a running maximum; products on bf16 with
+ * fp32 accumulation. Supported: the DeepSeek-V2 head shape with a bf16 cache
+ * (else MLA_ERR_UNSUPPORTED / MLA_ERR_DTYPE). Errors as in mla_decode, plus
+ * tokens_per_seq < 1 or a workspace below the required size (MLA_ERR_SHAPE).
+ * The event pair of mla_time_next_launch brackets both kernels it launches.
+ */
+int64_t mla_prefill_workspace(const mla_dims* dims, int32_t batch, int32_t max_seq_len);
+mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t tokens_per_seq,
+                       const void* q_nope, const void* q_rope, const mla_kv_cache* cache,
+                       const int32_t* seq_lens, int32_t max_seq_len, const void* w_uk,
+                       const void* w_uv, float sm_scale, void* out, float* lse, void* workspace,
+                       int64_t workspace_bytes, mla_stream stream);
+
+/*
  * Log-sum-exp merge of split partials (the split-KV pass of mla_decode):
  *   lse[b,h] = log sum_s exp(lse_part[b,s,h]),
  *   out[b,h] = sum_s exp(lse_part[b,s,h] - lse[b,h]) * o_part[b,s,h,:].

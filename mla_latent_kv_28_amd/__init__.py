@@ -24,7 +24,8 @@ EXPORTS = ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_combine", "mla
            "mla_split_chunk", "mla_suggest_splits", "mla_status_string", "mla_last_hip_error",
            "mla_time_next_launch", "mla_read_probe",
            "mla_cache_append", "mla_cache_append_workspace", "mla_cache_append_noalloc",
-           "mla_o_proj", "mla_o_proj_workspace", "mla_query_proj", "mla_query_proj_workspace")
+           "mla_o_proj", "mla_o_proj_workspace", "mla_query_proj", "mla_query_proj_workspace",
+           "mla_prefill", "mla_prefill_workspace")
 
 
 class MLAError(RuntimeError):
@@ -105,6 +106,11 @@ def lib():
         L.mla_query_proj_workspace.restype = i64
         L.mla_query_proj.argtypes = [pd, i32, i32, i32, vp, vp, vp, vp, vp, i32, f32, pr, vp, vp, vp, vp, i64, vp]
         L.mla_query_proj.restype = i32
+        L.mla_prefill_workspace.argtypes = [pd, i32, i32]
+        L.mla_prefill_workspace.restype = i64
+        L.mla_prefill.argtypes = [pd, i32, i32, vp, vp, ctypes.POINTER(KVCache), vp, i32, vp, vp, f32, vp, vp, vp,
+                                  i64, vp]
+        L.mla_prefill.restype = i32
         for name in ("mla_absorb_q", "mla_decode", "mla_decode_multi", "mla_combine", "mla_out_proj", "mla_split_chunk",
                      "mla_suggest_splits", "mla_last_hip_error", "mla_combine_out_proj",
                      "mla_time_next_launch", "mla_read_probe"):
@@ -208,6 +214,34 @@ def mla_decode_multi(dims, batch, tokens_per_seq, q_lat, cache, seq_lens, max_se
         _dev(lse, "lse", torch.float32, rows * parts * H),
         out_dtype, _stream(stream))
     _check(st, "mla_decode_multi")
+
+
+def mla_prefill_workspace(dims, batch, max_seq_len):
+    return int(lib().mla_prefill_workspace(ctypes.byref(dims_of(dims)), batch, max_seq_len))
+
+
+def mla_prefill(dims, batch, tokens_per_seq, q_nope, q_rope, cache, seq_lens, max_seq_len, w_uk, w_uv,
+                sm_scale, out, lse, workspace, stream=None):
+    """Non-absorbed causal attention of tokens_per_seq new tokens per
+    sequence: q_* [batch * n, H, *] bf16, out [batch * n, H, d_v] bf16,
+    lse [batch * n, H] f32, workspace of mla_prefill_workspace bytes."""
+    d = dims_of(dims)
+    H = d.num_heads
+    rows = batch * max(tokens_per_seq, 0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().mla_prefill(
+        ctypes.byref(d), batch, tokens_per_seq,
+        _dev(q_nope, "q_nope", torch.bfloat16, rows * H * d.d_nope),
+        _dev(q_rope, "q_rope", torch.bfloat16, rows * H * d.d_rope),
+        ctypes.byref(cache),
+        _dev(seq_lens, "seq_lens", torch.int32, batch), max_seq_len,
+        _dev(w_uk, "w_uk", torch.bfloat16, H * d.d_nope * d.d_latent),
+        _dev(w_uv, "w_uv", torch.bfloat16, H * d.d_v * d.d_latent),
+        float(sm_scale),
+        _dev(out, "out", torch.bfloat16, rows * H * d.d_v),
+        _dev(lse, "lse", torch.float32, rows * H),
+        _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st, "mla_prefill")
 
 
 def mla_read_probe(buf, sink, stream=None):

@@ -524,6 +524,72 @@ mla_status mla_query_proj(const mla_dims* dims, int32_t batch, int32_t hidden, i
   return hip_status(mla::launch_query_proj(p, static_cast<hipStream_t>(stream)));
 }
 
+int64_t mla_prefill_workspace(const mla_dims* dims, int32_t batch, int32_t max_seq_len) {
+  if (dims == nullptr || batch <= 0 || max_seq_len <= 0 || shape_of(dims) != Shape::kDsv2) return 0;
+  return mla::prefill_workspace_bytes(batch, dims->num_heads, max_seq_len);
+}
+
+mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t tokens_per_seq, const void* q_nope,
+                       const void* q_rope, const mla_kv_cache* cache, const int32_t* seq_lens, int32_t max_seq_len,
+                       const void* w_uk, const void* w_uv, float sm_scale, void* out, float* lse, void* workspace,
+                       int64_t workspace_bytes, mla_stream stream) {
+  if (dims == nullptr || cache == nullptr) return MLA_ERR_NULL;
+  if (batch < 0 || tokens_per_seq < 1 || max_seq_len < 0) return MLA_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * tokens_per_seq > 0x7fffffff) return MLA_ERR_SHAPE;
+  if (!valid_dtype(cache->dtype)) return MLA_ERR_DTYPE;
+  if (shape_of(dims) != Shape::kDsv2) return MLA_ERR_UNSUPPORTED;   // the DeepSeek-V2 head shape
+  if (cache->dtype != MLA_BF16) return MLA_ERR_DTYPE;               // a bf16 cache
+  if (!std::isfinite(sm_scale)) return MLA_ERR_SHAPE;
+  if ((static_cast<int64_t>(tokens_per_seq) + 127) / 128 > 65535) return MLA_ERR_UNSUPPORTED;
+  if ((static_cast<int64_t>(max_seq_len) + 127) / 128 > 0x7fffffff / 128) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !seq_lens || !w_uk || !w_uv || !out || !lse || !cache->latent) return MLA_ERR_NULL;
+  const bool paged = cache->page_size > 0;
+  if (cache->page_size < 0) return MLA_ERR_SHAPE;
+  if (paged) {
+    if (!cache->block_table) return MLA_ERR_NULL;
+    if (!is_pow2(cache->page_size)) return MLA_ERR_SHAPE;
+    const int64_t need = (static_cast<int64_t>(max_seq_len) + cache->page_size - 1) / cache->page_size;
+    if (cache->max_pages_per_seq < need) return MLA_ERR_SHAPE;
+  } else if (cache->seq_stride < max_seq_len) {
+    return MLA_ERR_SHAPE;
+  }
+  if (cache->row_stride < dims->d_latent + dims->d_rope) return MLA_ERR_SHAPE;
+  if ((cache->row_stride * 2) % 16 != 0) return MLA_ERR_ALIGN;
+  if (max_seq_len > 0) {
+    if (!workspace) return MLA_ERR_NULL;
+    if (workspace_bytes < mla_prefill_workspace(dims, batch, max_seq_len)) return MLA_ERR_SHAPE;
+    if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  }
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(cache->latent) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(out))
+    return MLA_ERR_ALIGN;
+  mla::PrefillParams p{};
+  p.q_nope = q_nope;
+  p.q_rope = q_rope;
+  p.latent = cache->latent;
+  p.row_stride = cache->row_stride;
+  p.seq_stride = cache->seq_stride;
+  p.block_table = cache->block_table;
+  p.max_pages = cache->max_pages_per_seq;
+  p.page_shift = paged ? log2i(cache->page_size) : -1;
+  p.seq_lens = seq_lens;
+  p.batch = batch;
+  p.n = tokens_per_seq;
+  p.heads = dims->num_heads;
+  p.max_seq_len = max_seq_len;
+  p.lpad = (max_seq_len + 127) / 128 * 128;
+  p.w_uk = w_uk;
+  p.w_uv = w_uv;
+  const int64_t half = mla::prefill_workspace_bytes(batch, dims->num_heads, max_seq_len) / 2;
+  p.kc = workspace;
+  p.vc = static_cast<char*>(workspace) + half;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.out = out;
+  p.lse = lse;
+  return hip_status(mla::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
 mla_status mla_cache_append_noalloc(const mla_dims* dims, int32_t batch, int32_t hidden, const void* h,
                                     const void* w_dkv, const void* w_kr, const void* norm_gain, int32_t dtype,
                                     float rms_eps, const mla_rope* rope, const int32_t* positions,

@@ -39,6 +39,30 @@ struct DecodeParams {
   int32_t tokens_per_seq;
 };
 
+// Prefill of n new tokens per sequence, non-absorbed (DeepSeek-V2 shape, bf16).
+struct PrefillParams {
+  const void* q_nope;           // [B n, H, 128] bf16
+  const void* q_rope;           // [B n, H, 64] bf16
+  const void* latent;           // bf16 cache rows [c_KV | k^R]
+  int64_t row_stride;           // elements
+  int64_t seq_stride;           // contiguous only
+  const int32_t* block_table;   // paged only
+  int32_t max_pages;
+  int32_t page_shift;           // -1 = contiguous
+  const int32_t* seq_lens;      // [B], clamped to [0, max_seq_len]
+  int32_t batch, n, heads, max_seq_len;
+  int32_t lpad;                 // max_seq_len rounded up to 128
+  const void* w_uk;             // [H, 128, 512] bf16
+  const void* w_uv;             // [H, 128, 512] bf16
+  void* kc;                     // workspace [B, H, lpad, 128] bf16
+  void* vc;                     // workspace [B, H, lpad, 128] bf16
+  float scale_log2;             // sm_scale * log2(e)
+  void* out;                    // [B n, H, 128] bf16
+  float* lse;                   // [B n, H]
+};
+int64_t prefill_workspace_bytes(int batch, int heads, int max_seq_len);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_compute_units();
 

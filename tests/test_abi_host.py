@@ -324,3 +324,29 @@ def test_read_probe_argument_errors(L):
     assert L.mla_read_probe(None, 1 << 20, P, None) == -1
     assert L.mla_read_probe(P, 1 << 20, None, None) == -1
     assert L.mla_read_probe(P + 8, 1 << 20, P, None) == -5
+
+
+@no_gpu
+def test_prefill_argument_errors(L):
+    def pre(n=4, batch=1, max_len=4096, ws=1 << 40, dims=DSV2, scale=0.07, **kw):
+        cache = _cache(**kw)
+        d = ctypes.byref(dims) if dims is not None else None
+        return L.mla_prefill(d, batch, n, P, P, ctypes.byref(cache), P, max_len, P, P, scale, P, P, P, ws, None)
+    need = L.mla_prefill_workspace(ctypes.byref(DSV2), 2, 1000)
+    assert need == 2 * 2 * 128 * 1024 * 128 * 2          # K^C and V^C, 1000 tokens padded to 1024
+    assert L.mla_prefill_workspace(ctypes.byref(TINY), 2, 1000) == 0
+    assert pre(dims=None) == -1
+    assert pre(n=0) == -2
+    assert pre(batch=-1) == -2
+    assert pre(max_len=-1) == -2
+    assert pre(scale=float("inf")) == -2
+    assert pre(dims=TINY) == -4
+    assert pre(dtype=mla.FP8_E4M3) == -3                 # bf16 caches only
+    assert pre(dtype=mla.F32) == -3
+    assert pre(batch=0) == 0
+    assert pre(ws=need // 2) == -2                       # workspace too small for 1 x 4096 tokens
+    assert pre(max_len=1000, batch=2, ws=need - 16) == -2
+    assert pre(row_stride=580) == -5
+    assert pre(seq_stride=4095) == -2
+    assert pre(page_size=48, block_table=P, max_pages_per_seq=100) == -2
+    assert pre(latent=None) == -1
