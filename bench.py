@@ -160,6 +160,125 @@ def o_proj_time(inp, stream, reps=10, copies=3):
             "timing": "HIP events on the launch stream around graph replays of back-to-back calls"}
 
 
+def _graph_time(stream, call, reps, per_graph):
+    """Microseconds per call: HIP events on `stream` around `reps` replays of
+    a graph of `per_graph` back-to-back calls (call(i), i = 0 .. per_graph-1)."""
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(2):
+            call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(per_graph):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+
+
+def query_proj_time(inp, stream, reps=10, per_graph=20):
+    """mla_query_proj (c_Q = RMSNorm(W_DQ h), q^C = W_UQ c_Q, q^R with YaRN
+    rotation) for the workload's batch, hidden 5120, d'_c 1536, bf16. Not
+    part of the decode step (its output feeds the absorb); reported beside it."""
+    import torch
+    import mla_latent_kv_28_amd as mla
+    from mla_synth import make_query_inputs
+    d, B = inp.dims, inp.batch
+    q = make_query_inputs(d, batch=B, seed=3, max_position=163840)
+    dev = "cuda:0"
+    h, w_dq, w_uq, w_qr = (t.to(dev) for t in (q.h, q.w_dq, q.w_uq, q.w_qr))
+    pos = torch.from_numpy(q.positions).to(dev)
+    qn = torch.empty((B, d.num_heads, d.d_nope), dtype=torch.bfloat16, device=dev)
+    qr = torch.empty((B, d.num_heads, d.d_rope), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.mla_query_proj_workspace(d, B, d.hidden, q.d_qlatent), dtype=torch.uint8, device=dev)
+    rope = mla.Rope(10000.0, 40.0, 1.0, 32.0, 4096)
+
+    def call(i):
+        mla.mla_query_proj(d, B, d.hidden, q.d_qlatent, h, w_dq, None, w_uq, w_qr, mla.BF16, q.eps, rope, pos,
+                           qn, qr, ws)
+
+    us = _graph_time(stream, call, reps, per_graph)
+    n2 = d.num_heads * (d.d_nope + d.d_rope)
+    alg = (q.d_qlatent * d.hidden + n2 * q.d_qlatent) * 2 + B * d.hidden * 2 + B * n2 * 2
+    gbps = alg / (us * 1e-6) / 1e9
+    return {"batch": B, "hidden": d.hidden, "d_qlatent": q.d_qlatent, "us_per_call": round(us, 3),
+            "calls_timed": reps * per_graph, "algorithmic_bytes": alg, "GBps": round(gbps, 1),
+            "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+            "timing": "HIP events on the launch stream around graph replays of back-to-back calls"}
+
+
+def prefill_time(pipe, stream, seqs=4, reps=5, per_graph=2):
+    """mla_prefill over whole 4096-token prompts of the first `seqs`
+    sequences of the workload's cache, queries drawn from torch's seeded
+    generator as N(0, 0.3^2) (their values do not change the work). The path
+    is MFMA-bound: reported against the bf16 dense peak, with the flops of
+    the up-projections and of the causal (query, key) pairs."""
+    import torch
+    import mla_latent_kv_28_amd as mla
+    d = pipe.dims
+    L = pipe.max_seq_len
+    n = L
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev).manual_seed(5)
+    qn = (torch.randn((seqs * n, d.num_heads, d.d_nope), generator=gen, device=dev) * 0.3).to(torch.bfloat16)
+    qr = (torch.randn((seqs * n, d.num_heads, d.d_rope), generator=gen, device=dev) * 0.3).to(torch.bfloat16)
+    lens = torch.full((seqs,), L, dtype=torch.int32, device=dev)
+    out = torch.empty((seqs * n, d.num_heads, d.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((seqs * n, d.num_heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(mla.mla_prefill_workspace(d, seqs, L), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        mla.mla_prefill(d, seqs, n, qn, qr, pipe.cache, lens, L, pipe.w_uk, pipe.w_uv, pipe.sm_scale, out, lse, ws)
+
+    us = _graph_time(stream, call, reps, per_graph)
+    H = d.num_heads
+    up = 2 * 2 * seqs * L * d.d_latent * H * d.d_nope                   # K^C and V^C of every row
+    pairs = seqs * n * (n + 1) // 2                                      # causal (query, key) pairs
+    att = pairs * H * 2 * ((d.d_nope + d.d_rope) + d.d_v)
+    tflops = (up + att) / (us * 1e-6) / 1e12
+    del ws, out, qn, qr
+    return {"sequences": seqs, "prompt_tokens": n, "us_per_call": round(us, 1), "calls_timed": reps * per_graph,
+            "gflop_per_call": round((up + att) / 1e9, 1), "tflops": round(tflops, 1),
+            "frac_of_bf16_dense_peak": round(tflops / 2500.0, 4),
+            "tokens_per_s": round(seqs * n / (us * 1e-6), 1),
+            "timing": "HIP events on the launch stream around graph replays of back-to-back calls"}
+
+
+def multi_token_time(pipe, caches, stream, n=2, reps=20):
+    """mla_decode_multi with n new tokens per sequence over the workload's
+    cache (the absorbed queries of the step, each repeated n times), rotating
+    the cache copies: the decode launch's time, query rows per second and the
+    cache bandwidth counted on the bytes of distinct cached rows."""
+    import torch
+    import mla_latent_kv_28_amd as mla
+    d, B, S = pipe.dims, pipe.seqs, pipe.num_splits
+    q = pipe.q_lat.repeat_interleave(n, dim=0).contiguous()
+    out = torch.empty((B * n, S, d.num_heads, d.d_latent), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty((B * n, S, d.num_heads), dtype=torch.float32, device="cuda:0")
+    nb = len(caches)
+
+    def call(i):
+        mla.mla_decode_multi(d, B, n, q, caches[i % nb], pipe.seq_lens, pipe.max_seq_len, pipe.sm_scale, S, out,
+                             lse, mla.BF16)
+
+    us = _graph_time(stream, call, reps, nb)
+    tokens = int(pipe.seq_lens.to(torch.int64).sum().item())
+    alg = tokens * (d.d_latent + d.d_rope) * 2
+    gbps = alg / (us * 1e-6) / 1e9
+    return {"tokens_per_seq": n, "query_rows": B * n, "splits": S, "us_per_launch": round(us, 3),
+            "query_rows_per_s": round(B * n / (us * 1e-6), 1), "cache_GBps": round(gbps, 1),
+            "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+            "timing": "HIP events on the launch stream around graph replays of decode launches alone"}
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle, as it stands, on whole sequences of the same
     workload until about `budget_s` seconds of CPU work have run."""
@@ -400,6 +519,10 @@ def main():
     if inp.dims.hidden == 5120 and not args.eager:
         result["cache_append"] = cache_append_time(inp, stream)
         result["o_proj"] = o_proj_time(inp, stream)
+        result["query_proj"] = query_proj_time(inp, stream)
+        if inp.dtype == "bf16" and inp.name == "dsv2_b32_l4096":
+            result["multi_token"] = multi_token_time(pipe, caches, stream)
+            result["prefill"] = prefill_time(pipe, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
