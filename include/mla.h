@@ -373,13 +373,14 @@ mla_status mla_cache_append_noalloc(const mla_dims* dims, int32_t batch, int32_t
  *   positions [B] int32 device array (any value; the angle is position * f_i),
  *   q_nope [B, H, d_nope] and q_rope [B, H, d_rope] (outputs), all in `dtype`.
  * MLA_BF16 with the DeepSeek-V2 head shape only (MLA_ERR_UNSUPPORTED for the
- * tiny one); hidden a multiple of 16, d_qlatent a multiple of 256 and at most
- * 4096. Products accumulate in fp32 over slices of 256 of the contraction,
- * added in slice order; the norm runs in fp32 and c_Q is rounded to bf16
- * before the up-projection; rotation angles in fp64.
+ * tiny one); hidden a multiple of 16 and at most 20480, d_qlatent a multiple
+ * of 256 and at most 4096 (MLA_ERR_UNSUPPORTED beyond). Products accumulate
+ * in fp32 over slices of 256 of the contraction, added in slice order; the
+ * norm runs in fp32 and c_Q is rounded to bf16 before the up-projection;
+ * rotation angles in fp64.
  * workspace: device memory of at least mla_query_proj_workspace() bytes,
- * 16-byte aligned, owned by the caller. Four kernels are launched (the
- * timing hook's pair brackets all four). batch == 0 is a no-op.
+ * 16-byte aligned, owned by the caller. Three kernels are launched (the
+ * timing hook's pair brackets all three). batch == 0 is a no-op.
  */
 int64_t mla_query_proj_workspace(const mla_dims* dims, int32_t batch, int32_t hidden, int32_t d_qlatent);
 mla_status mla_query_proj(const mla_dims* dims, int32_t batch, int32_t hidden, int32_t d_qlatent,

@@ -467,9 +467,8 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
 
 int64_t mla_query_proj_workspace(const mla_dims* dims, int32_t batch, int32_t hidden, int32_t d_qlatent) {
   if (dims == nullptr || batch <= 0 || hidden <= 0 || d_qlatent <= 0 || shape_of(dims) != Shape::kDsv2) return 0;
-  int64_t cq_off = 0, part2_off = 0, total = 0;
-  mla::query_workspace_layout(batch, hidden, d_qlatent, dims->num_heads * (dims->d_nope + dims->d_rope), &cq_off,
-                              &part2_off, &total);
+  int64_t cq_off = 0, total = 0;
+  mla::query_workspace_layout(batch, hidden, d_qlatent, &cq_off, &total);
   return total;
 }
 
@@ -485,7 +484,7 @@ mla_status mla_query_proj(const mla_dims* dims, int32_t batch, int32_t hidden, i
   if (sh != Shape::kDsv2) return MLA_ERR_UNSUPPORTED;     // the DeepSeek-V2 head shape, bf16
   if (dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (hidden % 16 != 0 || d_qlatent % 256 != 0) return MLA_ERR_SHAPE;
-  if (d_qlatent > 4096) return MLA_ERR_UNSUPPORTED;
+  if (d_qlatent > 4096 || mla::query_partial_sums(hidden) > 16) return MLA_ERR_UNSUPPORTED;
   mla::QueryParams p{};
   {
     const mla_status rs = rope_frequencies(rope, dims->d_rope, p.freq);
@@ -497,9 +496,8 @@ mla_status mla_query_proj(const mla_dims* dims, int32_t batch, int32_t hidden, i
   if (!aligned16(h) || !aligned16(w_dq) || !aligned16(w_uq) || !aligned16(w_qr) || !aligned16(q_nope) ||
       !aligned16(q_rope) || !aligned16(workspace))
     return MLA_ERR_ALIGN;
-  int64_t cq_off = 0, part2_off = 0, total = 0;
-  const int n2 = dims->num_heads * (dims->d_nope + dims->d_rope);
-  mla::query_workspace_layout(batch, hidden, d_qlatent, n2, &cq_off, &part2_off, &total);
+  int64_t cq_off = 0, total = 0;
+  mla::query_workspace_layout(batch, hidden, d_qlatent, &cq_off, &total);
   char* ws = static_cast<char*>(workspace);
   p.h = h;
   p.w_dq = w_dq;
@@ -511,15 +509,13 @@ mla_status mla_query_proj(const mla_dims* dims, int32_t batch, int32_t hidden, i
   p.q_rope = q_rope;
   p.part1 = reinterpret_cast<float*>(ws);
   p.cq = ws + cq_off;
-  p.part2 = reinterpret_cast<float*>(ws + part2_off);
   p.batch = batch;
   p.hidden = hidden;
   p.dq = d_qlatent;
   p.heads = dims->num_heads;
   p.d_nope = dims->d_nope;
   p.d_rope = dims->d_rope;
-  p.s1 = (hidden + 255) / 256;
-  p.s2 = d_qlatent / 256;
+  p.s1 = mla::query_partial_sums(hidden);
   p.eps = rms_eps;
   return hip_status(mla::launch_query_proj(p, static_cast<hipStream_t>(stream)));
 }

@@ -126,14 +126,15 @@ struct QueryParams {
   void* q_rope;                 // [B, H, d_rope] bf16
   float* part1;                 // [s1, B, dq] fp32 partial sums of W_DQ h
   void* cq;                     // [B, dq] bf16, the normed latent
-  float* part2;                 // [s2, B, H (d_nope + d_rope)] fp32 partial sums
-  int32_t batch, hidden, dq, heads, d_nope, d_rope, s1, s2;
+  int32_t batch, hidden, dq, heads, d_nope, d_rope;
+  int32_t s1;                   // partial sums of W_DQ h (query_partial_sums)
   float eps;
   double freq[kMaxRopePairs];
 };
-// Workspace layout of the query path: byte offsets of cq and part2, total.
-void query_workspace_layout(int batch, int hidden, int dq, int n2, int64_t* cq_off, int64_t* part2_off,
-                            int64_t* total);
+// Partial sums the query path keeps of W_DQ h at this hidden size (at most 16).
+int query_partial_sums(int hidden);
+// Workspace layout of the query path: byte offset of cq, total bytes.
+void query_workspace_layout(int batch, int hidden, int dq, int64_t* cq_off, int64_t* total);
 hipError_t launch_query_proj(const QueryParams& p, hipStream_t s);
 
 // Attention output projection u[b] = W_O o[b] (oproj.hip).

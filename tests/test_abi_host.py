@@ -296,8 +296,8 @@ def test_o_proj_argument_errors(L):
 def test_query_proj_argument_errors(L):
     d = ctypes.byref(DSV2)
     ws = mla.mla_query_proj_workspace(DSV2, 4, 5120, 1536)
-    # partial sums of W_DQ h (20 slices) and of the up-projections (6 slices), plus c_Q in bf16
-    assert ws == 20 * 4 * 1536 * 4 + 4 * 1536 * 2 + 6 * 4 * 128 * 192 * 4
+    # partial sums of W_DQ h (20 slices of 256, added five to a workgroup: 4), plus c_Q in bf16
+    assert ws == 4 * 4 * 1536 * 4 + 4 * 1536 * 2
     assert mla.mla_query_proj_workspace(TINY, 4, 128, 256) == 0
     yarn = mla.Rope(1e4, 40.0, 1.0, 32.0, 4096)
 
@@ -308,6 +308,7 @@ def test_query_proj_argument_errors(L):
     assert f(dims=None) == -1 and f(rope=None) == -1
     assert f(batch=-1) == -2 and f(hidden=5128) == -2 and f(dq=1000) == -2 and f(eps=-1.0) == -2
     assert f(dims=ctypes.byref(TINY)) == -4 and f(dq=8192) == -4
+    assert f(hidden=20496) == -4                           # beyond 16 partial sums of W_DQ h
     assert f(dtype=mla.F32) == -3
     assert f(rope=mla.Rope(1e4, 40.0, 5.0, 5.0, 4096)) == -2
     assert f(h=None) == -1 and f(qr=None) == -1 and f(work=None) == -1 and f(pos=None) == -1
