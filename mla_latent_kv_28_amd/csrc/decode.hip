@@ -789,10 +789,15 @@ constexpr int kPvEarly = 0;
 // that execute while it runs, and scheduling barriers keep the compiler from
 // regrouping them. The arithmetic is that of softmax_tile in the same order,
 // so contiguous and paged caches give identical bits.
-template <class C>
+// E4M3: rtile holds the tile's per-token factors r (see E4m3Ring): they
+// multiply the scores and, after the denominator has taken the
+// probabilities, the probabilities that enter the latent sum. That path adds
+// the denominator's terms in token-pair order (it shares no bits with the
+// 16-bit cache's paths).
+template <class C, bool E4M3>
 __device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char* __restrict__ pw,
                                                   const Scores<C>& sc, State<C>& s, int nvalid, float scale_log2,
-                                                  bool first) {
+                                                  bool first, const MLA_LDS float* __restrict__ rtile) {
 #pragma clang fp contract(off)
   static_assert(!C::F32 && !C::FP8 && C::NFJ == 4 && C::HB == 4, "32 latent-sum MFMAs, 16 scores per lane");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
@@ -802,12 +807,15 @@ __device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char*
     if (kPvEarly + g < 32) pvs.step(kPvEarly + g);
   };
   float x[16], a[8], pv[16];
-  // scaled scores
+  // scaled scores (e4m3: times the token's r, element i of group g being
+  // token 8 g + 4 hh + i)
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     mfma(g);
+    f32x4 rg = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (E4M3) rg = *(const MLA_LDS f32x4*)(rtile + 8 * g + 4 * hh);
 #pragma unroll
-    for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = sc.lat[i] * scale_log2;
+    for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = (E4M3 ? sc.lat[i] * rg[i - 4 * g] : sc.lat[i]) * scale_log2;
     sync();
   }
   // maximum over this lane's 16 tokens (exact in any order)
@@ -832,32 +840,59 @@ __device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char*
   s.m_max = fmaxf(s.m_max, mt);
   s.overflow = s.overflow || (mt > s.m_ref + kHeadroom);
   sync();
-  // probabilities, two per MFMA
+  if constexpr (E4M3) {
+    // probabilities, two per MFMA; the denominator takes them as they are,
+    // the latent sum times their tokens' r (read in pairs, tokens
+    // 8 (g / 2) + 4 hh + 2 (g % 2) + 0, 1)
+    float lsum = 0.0f;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    mfma(9 + g);
-    pv[2 * g] = fast_exp2(x[2 * g] - s.m_ref);
-    pv[2 * g + 1] = fast_exp2(x[2 * g + 1] - s.m_ref);
-    sync();
-  }
-  if (nvalid < C::T) {    // partial tile (uniform): tokens past the end weigh nothing
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
-      pv[i] = tok < nvalid ? pv[i] : 0.0f;
+    for (int g = 0; g < 8; ++g) {
+      mfma(9 + g);
+      const int tok = 8 * (g >> 1) + 4 * hh + 2 * (g & 1);
+      float p0 = fast_exp2(x[2 * g] - s.m_ref), p1 = fast_exp2(x[2 * g + 1] - s.m_ref);
+      if (nvalid < C::T) {    // partial tile (uniform): tokens past the end weigh nothing
+        p0 = tok < nvalid ? p0 : 0.0f;
+        p1 = tok + 1 < nvalid ? p1 : 0.0f;
+      }
+      lsum += p0 + p1;
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      const f32x2 rr = *(const MLA_LDS f32x2*)(rtile + tok);
+      pv[2 * g] = p0 * rr[0];
+      pv[2 * g + 1] = p1 * rr[1];
+      sync();
     }
-  }
-  sync();
-  float q4[4];
+    for (int j = 17; j < 21; ++j) mfma(j);
+    mfma(21);
+    s.l += lsum;
+    sync();
+  } else {
+    // probabilities, two per MFMA
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    mfma(17 + j);
-    q4[j] = (pv[4 * j] + pv[4 * j + 1]) + (pv[4 * j + 2] + pv[4 * j + 3]);
+    for (int g = 0; g < 8; ++g) {
+      mfma(9 + g);
+      pv[2 * g] = fast_exp2(x[2 * g] - s.m_ref);
+      pv[2 * g + 1] = fast_exp2(x[2 * g + 1] - s.m_ref);
+      sync();
+    }
+    if (nvalid < C::T) {    // partial tile (uniform): tokens past the end weigh nothing
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
+        pv[i] = tok < nvalid ? pv[i] : 0.0f;
+      }
+    }
+    sync();
+    float q4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mfma(17 + j);
+      q4[j] = (pv[4 * j] + pv[4 * j + 1]) + (pv[4 * j + 2] + pv[4 * j + 3]);
+      sync();
+    }
+    mfma(21);
+    s.l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
     sync();
   }
-  mfma(21);
-  s.l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
-  sync();
   // P^T rows of this wave's heads: element e of k step u is token
   // 16u + 8(e/4) + 4hh + e%4, i.e. pv[8u + e]
   u32x4 pk[2];
@@ -932,11 +967,16 @@ struct StreamTile {
 // An e4m3 cache streamed through the 16-bit tile loop. Each tile's codes and
 // per-token scales land in one of two landing buffers; at the end of the
 // step before the tile is scored, every thread widens the code chunks it
-// loaded itself to bf16 times the token's scale (the dequantised value,
-// rounded to bf16) into one of three 16-bit tile slots; the rotary keys, bf16
-// already, go straight to their slot. LDS: slot, landing, slot, slot,
-// landing, P^T buffers, so that the staged query (from the second slot on)
-// avoids the first slot and the first landing buffer, where tile 0 arrives.
+// loaded itself into one of three 16-bit tile slots. The per-token scale s
+// is split as s = 2^e r with r in [1, 2): the widen multiplies each code by
+// 2^e only (exact in bf16: one conversion instruction per two codes), the
+// rotary key, which lands in the slot in bf16, is divided by r in place, and
+// r itself goes to a 32-float array beside the slot. The score of token j is
+// then r_j times the 16-bit product, and its probability enters the latent
+// sum times r_j, so the latent part carries no rounding beyond the codes'.
+// LDS: slot, landing, slot, slot, landing, P^T buffers, r arrays, so that
+// the staged query (from the second slot on) avoids the first slot and the
+// first landing buffer, where tile 0 arrives.
 template <class C>
 struct E4m3Ring {
   static constexpr int SLOT = C::BUF_BYTES;
@@ -944,7 +984,8 @@ struct E4m3Ring {
   static constexpr int SCALES = C::WAVES * 256;             // one 256-byte scale row per wave
   static constexpr int LAND = CODES + SCALES;
   static constexpr int S0 = 0, L0 = SLOT, S1 = L0 + LAND, S2 = S1 + SLOT, L1 = S2 + SLOT, P = L1 + LAND;
-  static constexpr int BYTES = P + 2 * C::P_BYTES;
+  static constexpr int RS = P + 2 * C::P_BYTES;             // r of each slot's tokens, 3 x 32 floats
+  static constexpr int BYTES = RS + 3 * C::T * 4;
   static constexpr int LPT = 6;                             // per thread: 4 code chunks, scales, rotary
   static_assert(!C::F32 && !C::FP8 && C::WAVES == 4 && C::T == 32, "16-bit DeepSeek-V2 slots");
   static_assert(BYTES <= C::LDS_BYTES, "LDS budget");
@@ -953,7 +994,7 @@ struct E4m3Ring {
 };
 
 struct NoE4m3Ring {   // stands in where no e4m3 ring is used
-  static constexpr int S0 = 0, L0 = 0, S1 = 0, S2 = 0, L1 = 0, P = 0, LPT = 0;
+  static constexpr int S0 = 0, L0 = 0, S1 = 0, S2 = 0, L1 = 0, P = 0, RS = 0, LPT = 0;
 };
 
 // Loads of one e4m3 tile: wave w, lane i loads code chunk i % 32 of rows
@@ -999,32 +1040,48 @@ struct E4m3Tile {
   }
 };
 
+// The significand r in [1, 2) of a normal scale s = 2^e r (a zero scale gives
+// r = 1 and a code times 2^-127, i.e. zero to within bf16's range).
+__device__ __forceinline__ float scale_significand(float s) {
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, s) & 0x007fffffu) | 0x3f800000u);
+}
+
 // Widen this thread's code chunks of one landed tile: 16 codes -> 16 bf16
-// values code * scale, two 16-byte chunks of the slot's latent row.
+// values code * 2^e (exact; the conversion applies the exponent of the scale
+// operand only), two 16-byte chunks of the slot's latent row. Then divide
+// the rotary chunk this thread's own wave loaded (row 8 wave + lane / 8) by
+// its token's r, and record r for the softmax.
 template <class C>
 __device__ __forceinline__ void e4m3_widen(const MLA_LDS char* __restrict__ land, MLA_LDS char* __restrict__ slot,
-                                           int wave) {
+                                           MLA_LDS float* __restrict__ rsl, int wave) {
   // opaque, so that the offsets below are computed here and not kept live
   // across the whole tile loop
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));
+  const MLA_LDS float* scales = (const MLA_LDS float*)(land + E4m3Ring<C>::CODES + wave * 256);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int t = 8 * wave + 2 * k + (lane >> 5), c = lane & 31;
     const u32x4 w = *(const MLA_LDS u32x4*)(land + (4 * wave + k) * 1024 + 16 * lane);
-    const float sc = *(const MLA_LDS float*)(land + E4m3Ring<C>::CODES + wave * 256 + 4 * (2 * k + (lane >> 5)));
+    const float sc = scales[2 * k + (lane >> 5)];
     uint32_t o[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[d], 1.0f, false);
-      const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)w[d], 1.0f, true);
-      const float a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
-      o[2 * d] = pack_bf16x2(a0 * sc, a1 * sc);
-      o[2 * d + 1] = pack_bf16x2(b0 * sc, b1 * sc);
+      o[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[d], sc, false));
+      o[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[d], sc, true));
     }
     *(MLA_LDS u32x4*)(slot + lat_off<C>(t, 32 * c)) = u32x4{o[0], o[1], o[2], o[3]};
     *(MLA_LDS u32x4*)(slot + lat_off<C>(t, 32 * c + 16)) = u32x4{o[4], o[5], o[6], o[7]};
   }
+  const float r = scale_significand(scales[lane >> 3]);
+  const float inv = 1.0f / r;
+  MLA_LDS u32x4* rp = (MLA_LDS u32x4*)(slot + C::LAT_BYTES + wave * 64 * 16 + 16 * lane);
+  u32x4 v = *rp;
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    v[d] = pack_bf16x2(bf16_bits_to_f32(v[d] & 0xffffu) * inv, bf16_bits_to_f32(v[d] >> 16) * inv);
+  *rp = v;
+  if ((lane & 7) == 0) rsl[8 * wave + (lane >> 3)] = r;
 }
 
 // Steady state for a contiguous 16-bit cache: one basic block per tile.
@@ -1043,7 +1100,9 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
                                                  int t, int ntiles, int start, int end, bool first,
                                                  MLA_LDS char* __restrict__ land_fill = nullptr,
                                                  const MLA_LDS char* __restrict__ land_next = nullptr,
-                                                 MLA_LDS char* __restrict__ next = nullptr, int64_t seq_row = 0) {
+                                                 MLA_LDS char* __restrict__ next = nullptr, int64_t seq_row = 0,
+                                                 const MLA_LDS float* __restrict__ r_cur = nullptr,
+                                                 MLA_LDS float* __restrict__ r_next = nullptr) {
   static_assert(!C::F32 && !C::FP8 && C::LAT_CH == 64 && C::WAVES == 4, "16-bit DeepSeek-V2 layout");
   constexpr int LPT = E4M3 ? E4m3Ring<C>::LPT : loads_per_tile<C>();
   static_assert(E4M3 || LPT == C::T / C::WAVES + 1, "nine loads per tile");
@@ -1087,9 +1146,9 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
     ld8.issue_scales(land_fill, wave);
     ld8.issue_rope(dma, fill, wave);
   }
-  softmax_pv_stream<C>(pvs, pw, sc, s, end - (start + t * C::T), p.scale_log2, first);
+  softmax_pv_stream<C, E4M3>(pvs, pw, sc, s, end - (start + t * C::T), p.scale_log2, first, r_cur);
   wait_vmem_le<LPT>();
-  if constexpr (E4M3) e4m3_widen<C>(land_next, next, wave);   // tile t + 1, landed
+  if constexpr (E4M3) e4m3_widen<C>(land_next, next, r_next, wave);   // tile t + 1, landed
   tile_barrier();
 }
 
@@ -1219,6 +1278,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
     }
   };
   auto land = [&](int x) -> MLA_LDS char* { return lds + ((x & 1) ? R8::L1 : R8::L0); };   // e4m3 landing
+  auto rslot = [&](int x) -> MLA_LDS float* { return (MLA_LDS float*)(lds + R8::RS) + (x % 3) * C::T; };
 
   // 16-bit caches, contiguous or with pages of at least 32 tokens (PSTREAM),
   // stream whole tiles and stage the query through LDS (slots 2..3 and the
@@ -1357,7 +1417,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       }
       issue8(1);
       if (pass != 0) wait_vmem_le<R8::LPT>();    // tile 0
-      e4m3_widen<C>(land(0), slot(0), wv);
+      e4m3_widen<C>(land(0), slot(0), rslot(0), wv);
       static_assert(C::P_BYTES == C::THREADS * 32, "two 16-byte zero stores per thread");
       *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32) = u32x4{};
       *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32 + 16) = u32x4{};
@@ -1367,7 +1427,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
         const int tp = max(t - 1, 0), first = pass == 0 && t == 0;
         tile_step_stream<C, false, true>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma,
                                          tbase, t, ntiles, start, end, first != 0, land(t), land(t + 1),
-                                         slot(t + 1), sv.seq_row);
+                                         slot(t + 1), sv.seq_row, rslot(t), rslot(t + 1));
       }
       finish_pass();
     } else if constexpr (STREAM) {
