@@ -10,17 +10,24 @@
 // Three launches, bf16 in and out with fp32 accumulation:
 //  1. qgemm over W_DQ: [B, hidden] x [hidden, d'_c]; a workgroup of five
 //     waves per (32 output features, 1280 contraction features, 32 rows),
-//     each wave one 256-wide slice (MFMA 32x32x16, operands straight from
-//     memory, every load of a slice issued before its products); the five
-//     partial tiles are added through LDS in wave order and stored as one
-//     fp32 partial sum;
+//     each wave one 256-wide slice (MFMA 32x32x16); the five partial tiles
+//     are added through LDS in wave order and stored as one fp32 partial sum;
 //  2. latent_norm: one workgroup per sequence adds those partial sums in
-//     order, takes the RMS norm and writes c_Q in bf16;
+//     order, takes the RMS norm and writes c_Q in bf16, blocked by 16
+//     features ([d'_c / 16][rows][16]) so that the next product's operand
+//     loads are whole 1 KiB rows;
 //  3. qgemm over [W_UQ; W_QR] with the whole d'_c contraction in one
-//     workgroup (up to eight waves, each taking every eighth 256-wide slice,
-//     their tiles added through LDS in wave order), which then turns the rotary pairs (the partner value from the
-//     neighbouring lane, the angle position * f_i in double precision) and
-//     writes q_nope [B, H, d_nope] and q_rope [B, H, d_rope] directly.
+//     workgroup (waves of two 256-wide slices, at most eight, their tiles
+//     added through LDS in wave order), which then turns the
+//     rotary pairs (the partner value from the neighbouring lane, the angle
+//     position * f_i in double precision) and writes q_nope [B, H, d_nope]
+//     and q_rope [B, H, d_rope] directly.
+// A wave's weight slice (32 rows x 512 bytes) goes HBM -> LDS with direct
+// 16-byte loads, two whole rows per instruction, and its MFMA fragments are
+// read back from LDS: loading the fragments straight from memory touched 32
+// rows per instruction, and [W_UQ; W_QR] took 37 us at batch 32 against
+// 29 us staged (three waves of two slices a workgroup; one wave a slice,
+// whose six waves' 96 KB of LDS left one workgroup per compute unit, 36 us).
 // The weights (91 MB at the DeepSeek-V2 shape) are read once per 32 rows.
 #include <hip/hip_runtime.h>
 
@@ -35,9 +42,10 @@ namespace {
 constexpr int kQSlice = 256;     // contraction features per wave and pass
 constexpr int kQMaxWaves = 8;    // waves per workgroup
 constexpr int kQ1Slices = 5;     // slices per workgroup over W_DQ
+constexpr int kQStage = 32 * kQSlice * 2;   // LDS bytes of one wave's weight slice
 
 struct QGemm {
-  const __bf16* a;     // [M, K] row-major activations
+  const __bf16* a;     // activations: [M, K] row-major, or blocked [K / 16][Mpad][16]
   const __bf16* w0;    // rows [0, n0) of the weight, [n0, K]
   const __bf16* w1;    // rows [n0, N), [N - n0, K]
   float* out;          // FINISH == false: [gridDim.y, M, N] partial sums
@@ -47,45 +55,70 @@ struct QGemm {
 
 // Workgroup (x, y, z): columns 32x .. 32x + 31, slices y * slices .. of the
 // contraction, rows 32z .. 32z + 31; wave w takes slices w, w + waves, ...
-// of them. The waves' tiles are added in wave order through LDS; FINISH
-// turns the rotary columns and writes the query.
-template <bool FINISH>
-__global__ __launch_bounds__(64 * kQMaxWaves) void qgemm(QGemm g, QueryParams p) {
-  __shared__ __attribute__((aligned(16))) float red[kQMaxWaves][64 * 16];
+// of them. Weight row j of the tile sits at LDS bytes 512 j .. with its
+// 16-byte chunk c at position c ^ (j & 31), so the 32 rows that one fragment
+// read touches cover every bank group. The waves' tiles are added in wave
+// order through LDS; FINISH turns the rotary columns and writes the query.
+template <bool FINISH, bool A_BLOCKED, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void qgemm(QGemm g, QueryParams p) {
+  __shared__ __attribute__((aligned(16))) char stage[WAVES * kQStage];   // at most blockDim.x / 64 used
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
   const int r = lane & 31, half = lane >> 5;
-  const int n = blockIdx.x * 32 + r;   // B operand column (weight row); N is a multiple of 32
-  const int m = blockIdx.z * 32 + r;   // A operand row
-  const __bf16* w = n < g.n0 ? g.w0 + (int64_t)n * g.K : g.w1 + (int64_t)(n - g.n0) * g.K;
+  const int n0 = blockIdx.x * 32;       // N is a multiple of 32; a tile lies in one weight
+  const int n = n0 + r;                 // B operand column (weight row)
+  const int m = blockIdx.z * 32 + r;    // A operand row
+  const int mpad = gridDim.z * 32;
+  const __bf16* wt = n0 < g.n0 ? g.w0 + (int64_t)n0 * g.K : g.w1 + (int64_t)(n0 - g.n0) * g.K;
+  const auto res = buffer_rsrc(wt, (uint32_t)(32 * g.K * 2));   // reads past the tile return zero
   const bool m_ok = m < g.M;
   const __bf16* a = g.a + (int64_t)(m_ok ? m : 0) * g.K;
+  MLA_LDS char* st = (MLA_LDS char*)stage + wave * kQStage;
   f32x16 acc = {};
   for (int sl = wave; sl < g.slices; sl += waves) {
-    const int k0 = (blockIdx.y * g.slices + sl) * kQSlice, k1 = min(k0 + kQSlice, g.K);
-    bf16x8 av[kQSlice / 16], bv[kQSlice / 16];
+    const int k0 = (blockIdx.y * g.slices + sl) * kQSlice;
+    if (k0 >= g.K) break;              // uniform in the wave
+    const int kn = min(kQSlice, g.K - k0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the previous slice's fragments are read
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 2 * i + half;
+      const int chunk = (lane & 31) ^ (row & 31);
+      buf_load16_to_lds(res, (uint32_t)(row * g.K * 2 + k0 * 2 + 16 * chunk), 0u, st + i * 1024);
+    }
+    bf16x8 av[kQSlice / 16];
 #pragma unroll
     for (int s = 0; s < kQSlice / 16; ++s) {
-      const int k = k0 + 16 * s + 8 * half;
-      if (k0 + 16 * s < k1) {
-        av[s] = m_ok ? *(const bf16x8*)(a + k) : bf16x8{};
-        bv[s] = *(const bf16x8*)(w + k);
+      if (16 * s < kn) {
+        bf16x8 v;
+        if constexpr (A_BLOCKED) v = *(const bf16x8*)(g.a + ((int64_t)(k0 / 16 + s) * mpad + m) * 16 + 8 * half);
+        else v = *(const bf16x8*)(a + k0 + 16 * s + 8 * half);
+        av[s] = m_ok ? v : bf16x8{};
       }
     }
+    wait_vmem();
 #pragma unroll
-    for (int s = 0; s < kQSlice / 16; ++s)
-      if (k0 + 16 * s < k1) acc = mfma32x32x16(av[s], bv[s], acc);
+    for (int s = 0; s < kQSlice / 16; ++s) {
+      if (16 * s < kn) {
+        const bf16x8 bv = *(const MLA_LDS bf16x8*)(st + r * 512 + 16 * ((2 * s + half) ^ r));
+        acc = mfma32x32x16(av[s], bv, acc);
+      }
+    }
   }
   // fixed-order sum of the waves' tiles: lane l of every wave holds the same
-  // 16 positions, so the sum is elementwise
+  // 16 positions, so the sum is elementwise; each wave parks its tile in its
+  // own staging region
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  MLA_LDS float* mine = (MLA_LDS float*)st;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    *(f32x4*)&red[wave][lane * 16 + 4 * i] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+    *(MLA_LDS f32x4*)(mine + lane * 16 + 4 * i) = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
   __syncthreads();
   if (wave != 0) return;
   for (int v = 1; v < waves; ++v) {
+    const MLA_LDS float* other = (const MLA_LDS float*)((MLA_LDS char*)stage + v * kQStage);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4 x = *(const f32x4*)&red[v][lane * 16 + 4 * i];
+      const f32x4 x = *(const MLA_LDS f32x4*)(other + lane * 16 + 4 * i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[4 * i + e] += x[e];
     }
@@ -134,10 +167,12 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
 
 constexpr int kMaxDqPerThread = 16;   // d'_c up to 16 x 256
 constexpr int kMaxParts = 16;         // partial sums of W_DQ h (hidden up to 16 x 1280)
+constexpr int kFastParts = 4;         // hidden up to 4 x 1280: every load issued before any sum
 
 // c_Q[b] = RMSNorm(sum of the partial sums) in bf16; one 256-thread
-// workgroup per sequence, thread t owns features t, t + 256, ...; every load
-// of a feature's partial sums is issued before they are added in order.
+// workgroup per sequence, thread t owns features t, t + 256, ...; the
+// partial sums of a feature are added in order. c_Q is stored blocked:
+// feature c of row b at ((c / 16) * Mpad + b) * 16 + c % 16.
 __global__ __launch_bounds__(256) void latent_norm(QueryParams p) {
   __shared__ float red[4];
   const int b = blockIdx.x, t = threadIdx.x;
@@ -146,28 +181,40 @@ __global__ __launch_bounds__(256) void latent_norm(QueryParams p) {
   const float* src = p.part1 + (int64_t)b * p.dq;
   float x[kMaxDqPerThread];
   float ss = 0.0f;
+  if (p.s1 <= kFastParts) {
+    float v[kMaxDqPerThread][kFastParts];
 #pragma unroll
-  for (int j = 0; j < kMaxDqPerThread; ++j) {
-    if (j < per) {
-      float parts[kMaxParts];
+    for (int j = 0; j < kMaxDqPerThread; ++j)
 #pragma unroll
-      for (int s = 0; s < kMaxParts; ++s) parts[s] = s < p.s1 ? src[s * part + t + 256 * j] : 0.0f;
-      float v = 0.0f;
+      for (int s = 0; s < kFastParts; ++s) v[j][s] = (j < per && s < p.s1) ? src[s * part + t + 256 * j] : 0.0f;
 #pragma unroll
-      for (int s = 0; s < kMaxParts; ++s)
-        if (s < p.s1) v += parts[s];   // in order
-      x[j] = v;
-      ss += v * v;
+    for (int j = 0; j < kMaxDqPerThread; ++j) {
+      float a = 0.0f;
+#pragma unroll
+      for (int s = 0; s < kFastParts; ++s)
+        if (s < p.s1) a += v[j][s];   // in order
+      x[j] = a;
+      if (j < per) ss += a * a;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMaxDqPerThread; ++j) {
+      float a = 0.0f;
+      if (j < per)
+        for (int s = 0; s < p.s1; ++s) a += src[s * part + t + 256 * j];   // in order
+      x[j] = a;
+      if (j < per) ss += a * a;
     }
   }
   const float inv = 1.0f / sqrtf(block_sum256(ss, red) / p.dq + p.eps);
-  __bf16* dst = (__bf16*)p.cq + (int64_t)b * p.dq;
+  const int mpad = (p.batch + 31) / 32 * 32;
+  __bf16* dst = (__bf16*)p.cq;
 #pragma unroll
   for (int j = 0; j < kMaxDqPerThread; ++j) {
     if (j < per) {
       const int c = t + 256 * j;
       const float g = p.gain != nullptr ? (float)((const __bf16*)p.gain)[c] : 1.0f;
-      dst[c] = (__bf16)(x[j] * inv * g);
+      dst[((int64_t)(c >> 4) * mpad + b) * 16 + (c & 15)] = (__bf16)(x[j] * inv * g);
     }
   }
 }
@@ -182,7 +229,7 @@ int query_partial_sums(int hidden) {
 void query_workspace_layout(int batch, int hidden, int dq, int64_t* cq_off, int64_t* total) {
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   *cq_off = up((int64_t)query_partial_sums(hidden) * batch * dq * 4);
-  *total = *cq_off + up((int64_t)batch * dq * 2);
+  *total = *cq_off + up((int64_t)(batch + 31) / 32 * 32 * dq * 2);   // c_Q blocked, rows padded to 32
 }
 
 // A pending event pair (mla_time_next_launch) brackets the launches: the start
@@ -195,16 +242,22 @@ hipError_t launch_query_proj(const QueryParams& p, hipStream_t stream) {
   const int rb = (p.batch + 31) / 32;
   QGemm g1{(const __bf16*)p.h, (const __bf16*)p.w_dq, (const __bf16*)p.w_dq, p.part1, p.batch, p.dq, p.hidden,
            p.dq, kQ1Slices};
-  hipError_t e = launch_kernel_events(qgemm<false>, dim3(p.dq / 32, p.s1, rb), dim3(64 * kQ1Slices), stream, e0,
-                                      nullptr, g1, p);
+  hipError_t e = launch_kernel_events(qgemm<false, false, kQ1Slices>, dim3(p.dq / 32, p.s1, rb),
+                                      dim3(64 * kQ1Slices), stream, e0, nullptr, g1, p);
   if (e != hipSuccess) return e;
   e = launch_kernel_events(latent_norm, dim3(p.batch), dim3(256), stream, nullptr, nullptr, p);
   if (e != hipSuccess) return e;
   const int s2 = p.dq / kQSlice;
   QGemm g2{(const __bf16*)p.cq, (const __bf16*)p.w_uq, (const __bf16*)p.w_qr, nullptr, p.batch, n2, p.dq,
            p.heads * p.d_nope, s2};
-  return launch_kernel_events(qgemm<true>, dim3(n2 / 32, 1, rb), dim3(64 * std::min(s2, kQMaxWaves)), stream,
-                              nullptr, e1, g2, p);
+  // two slices a wave: three waves for d'_c = 1536, whose 48 KB of LDS let
+  // three workgroups share a compute unit (one wave a slice: 36 us; three:
+  // 29 us at batch 32)
+  const dim3 grid2(n2 / 32, 1, rb);
+  if (s2 <= 6)
+    return launch_kernel_events(qgemm<true, true, 3>, grid2, dim3(64 * ((s2 + 1) / 2)), stream, nullptr, e1, g2, p);
+  return launch_kernel_events(qgemm<true, true, kQMaxWaves>, grid2, dim3(64 * std::min((s2 + 1) / 2, kQMaxWaves)),
+                              stream, nullptr, e1, g2, p);
 }
 
 }  // namespace mla

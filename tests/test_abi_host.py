@@ -297,7 +297,8 @@ def test_query_proj_argument_errors(L):
     d = ctypes.byref(DSV2)
     ws = mla.mla_query_proj_workspace(DSV2, 4, 5120, 1536)
     # partial sums of W_DQ h (20 slices of 256, added five to a workgroup: 4), plus c_Q in bf16
-    assert ws == 4 * 4 * 1536 * 4 + 4 * 1536 * 2
+    # with its rows padded to 32
+    assert ws == 4 * 4 * 1536 * 4 + 32 * 1536 * 2
     assert mla.mla_query_proj_workspace(TINY, 4, 128, 256) == 0
     yarn = mla.Rope(1e4, 40.0, 1.0, 32.0, 4096)
 
