@@ -158,6 +158,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
   const int pos = L - n + t;                   // its position: it sees keys 0 .. pos
   const int64_t bv = (int64_t)b * n + (valid ? t : 0);
 
+  // every token of this wave valid, and the position of its first token
+  // (the lowest: every lane sees at least keys 0 .. wave_pos0)
+  const bool wave_full = q0 + 32 * wave + 31 < n;
+  const int wave_pos0 = L - n + q0 + 32 * wave;
   // keys the workgroup needs: up to the position of its last valid token
   const int kmax = L - n + min(q0 + kQBlock - 1, n - 1);
   const int nkb = kmax >= 0 ? kmax / kKBlock + 1 : 0;
@@ -239,18 +243,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
         sc[kk] = mfma32x32x16(a, qf[s], sc[kk]);
       }
     }
-    // element 4 jj + ii of sc[kk]: key j0 + 32 kk + 8 jj + 4 hh + ii
+    // element 4 jj + ii of sc[kk]: key j0 + 32 kk + 8 jj + 4 hh + ii; a
+    // block that every token of the wave sees whole takes no mask (uniform)
     float x[2][16];
     float mt = -INFINITY;
+    if (wave_full && j0 + kKBlock - 1 <= wave_pos0) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = j0 + 32 * kk + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const float v = sc[kk][e] * p.scale_log2;
-        x[kk][e] = (valid && key <= pos) ? v : -INFINITY;
-        mt = fmaxf(mt, x[kk][e]);
-      }
+        for (int e = 0; e < 16; ++e) {
+          x[kk][e] = sc[kk][e] * p.scale_log2;
+          mt = fmaxf(mt, x[kk][e]);
+        }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = j0 + 32 * kk + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const float v = sc[kk][e] * p.scale_log2;
+          x[kk][e] = (valid && key <= pos) ? v : -INFINITY;
+          mt = fmaxf(mt, x[kk][e]);
+        }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m, mt);
     const float ref = m_new == -INFINITY ? 0.0f : m_new;   // a token with no key yet
@@ -265,8 +280,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
         psum += x[kk][e];
       }
     l = l * alpha + psum;
+    if (__ballot(alpha != 1.0f)) {   // uniform: no lane's maximum moved, nothing to rescale
 #pragma unroll
-    for (int jb = 0; jb < kDV / 32; ++jb) o[jb] *= alpha;
+      for (int jb = 0; jb < kDV / 32; ++jb) o[jb] *= alpha;
+    }
 
     // O^T += V^T . P^T, four 16-key steps; element e of step u is key
     // 16 u + 8 (e / 4) + 4 hh + e % 4 = accumulator 8 (u & 1) + e of block u / 2
