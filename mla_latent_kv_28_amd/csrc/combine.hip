@@ -157,11 +157,8 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   const int waves = p.batch * p.heads;
   const dim3 grid((waves + kWaves - 1) / kWaves);
-  if (p.part_bf16)
-    launch_kernel(combine_kernel<true>, grid, dim3(64 * kWaves), s, p);
-  else
-    launch_kernel(combine_kernel<false>, grid, dim3(64 * kWaves), s, p);
-  return hipGetLastError();
+  if (p.part_bf16) return launch_kernel(combine_kernel<true>, grid, dim3(64 * kWaves), s, p);
+  return launch_kernel(combine_kernel<false>, grid, dim3(64 * kWaves), s, p);
 }
 
 }  // namespace mla

@@ -584,8 +584,7 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
   using G = GemmCfg<F32, W_KN, K, N>;
   if (p.batch == 0) return hipSuccess;
   dim3 grid(p.heads, N / G::NT, (p.batch + 31) / 32);
-  launch_kernel((head_gemm<F32, W_KN, K, N>), grid, dim3(64), s, p);
-  return hipGetLastError();
+  return launch_kernel((head_gemm<F32, W_KN, K, N>), grid, dim3(64), s, p);
 }
 
 }  // namespace
@@ -593,19 +592,15 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 hipError_t launch_absorb_dsv2_bf16(const GemmParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
   if (p.tail != nullptr && p.n_tail != 64) return hipErrorInvalidValue;   // 64-wide rotary rows
-  launch_kernel(absorb_bf16_kernel, dim3(p.heads, kAbsN / kAbsNT), dim3(256), s, p);
-  return hipGetLastError();
+  return launch_kernel(absorb_bf16_kernel, dim3(p.heads, kAbsN / kAbsNT), dim3(256), s, p);
 }
 hipError_t launch_absorb_tiny_f32(const GemmParams& p, hipStream_t s) {
   return launch<true, true, 32, 32>(p, s);
 }
 hipError_t launch_outproj_dsv2_bf16(const GemmParams& p, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
-  if (p.a_f32)
-    launch_kernel(outproj_bf16_kernel<true>, dim3(p.heads, kOutN / kOutNT), dim3(256), s, p);
-  else
-    launch_kernel(outproj_bf16_kernel<false>, dim3(p.heads, kOutN / kOutNT), dim3(256), s, p);
-  return hipGetLastError();
+  if (p.a_f32) return launch_kernel(outproj_bf16_kernel<true>, dim3(p.heads, kOutN / kOutNT), dim3(256), s, p);
+  return launch_kernel(outproj_bf16_kernel<false>, dim3(p.heads, kOutN / kOutNT), dim3(256), s, p);
 }
 hipError_t launch_outproj_tiny_f32(const GemmParams& p, hipStream_t s) {
   return launch<true, false, 32, 32>(p, s);
@@ -620,13 +615,11 @@ hipError_t launch_combine_outproj_dsv2_bf16(const CombineOutParams& p, hipStream
   q.rows_per_block = p.batch <= 32 ? 16 : (((p.batch + 1) / 2 + 31) / 32) * 32;
   const dim3 grid(p.heads, (p.batch + q.rows_per_block - 1) / q.rows_per_block), block(64 * kCoWaves);
   if (q.rows_per_block == 16) {
-    if (p.out_f32) launch_kernel(combine_outproj_kernel<true, 2>, grid, block, s, q);
-    else launch_kernel(combine_outproj_kernel<false, 2>, grid, block, s, q);
-  } else {
-    if (p.out_f32) launch_kernel(combine_outproj_kernel<true, 4>, grid, block, s, q);
-    else launch_kernel(combine_outproj_kernel<false, 4>, grid, block, s, q);
+    if (p.out_f32) return launch_kernel(combine_outproj_kernel<true, 2>, grid, block, s, q);
+    return launch_kernel(combine_outproj_kernel<false, 2>, grid, block, s, q);
   }
-  return hipGetLastError();
+  if (p.out_f32) return launch_kernel(combine_outproj_kernel<true, 4>, grid, block, s, q);
+  return launch_kernel(combine_outproj_kernel<false, 4>, grid, block, s, q);
 }
 
 }  // namespace mla
