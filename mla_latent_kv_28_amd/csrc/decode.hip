@@ -460,6 +460,10 @@ __device__ __forceinline__ bf16x8 qk_operand(const MLA_LDS char* buf, const Lane
 __device__ __forceinline__ void mfma_vgpr_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("s_nop 5\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+// The same product starting from zero (no accumulator input).
+__device__ __forceinline__ void mfma_vgpr_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 5\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+}
 // More wait states than the longest MFMA needs before VALU reads its result.
 __device__ __forceinline__ void vgpr_acc_drain(f32x16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
@@ -678,6 +682,7 @@ __device__ __forceinline__ void wait_vmem_le() {
   else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
   else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
   else if constexpr (N == 27) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
   else static_assert(N == 0, "add the vmcnt value here");
@@ -753,7 +758,7 @@ __device__ __forceinline__ void swap_lane_halves(uint32_t& lo, uint32_t& hi) {
 // scheduled ahead of use: the P^T operand of head block b + 1 at MFMA 4b, the
 // C_KV^T operands of k step 1 at MFMAs 10..13. va[0] and pb[0] are read by the
 // caller before MFMA 0.
-template <class C>
+template <class C, bool CODES = false>
 struct PvSched {
   State<C>& s;
   bf16x8 (&va)[2][C::NFJ];
@@ -761,18 +766,31 @@ struct PvSched {
   const MLA_LDS char* __restrict__ prev;
   const MLA_LDS char* __restrict__ pr;
   const LaneOffs<C>& lo;
+  i32x2 raw1[C::NFJ];   // e4m3 codes of k step 1, widened at their first use
   __device__ __forceinline__ void read_pb(int blk) {
     pb[blk & 1] = *(const MLA_LDS bf16x8*)(pr + p_rd_off<C>(lo, blk & 3, blk >> 2));
   }
   __device__ __forceinline__ void read_va(int u, int j) {
-    const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
-    const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
-    va[u][j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (CODES) {
+      const i32x2 w = lds_read_tr8(prev + ((lo.pv[0] ^ (32 * j)) + C::DC * 16 * u));
+      if (u == 0) va[0][j] = e4m3x8_to_bf16x8(w);
+      else raw1[j] = w;
+    } else {
+      const bf16x4 v0 = lds_read_tr16(prev + pv_off<C>(lo, 0, j, u));
+      const bf16x4 v1 = lds_read_tr16(prev + pv_off<C>(lo, 1, j, u));
+      va[u][j] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
   }
   __device__ __forceinline__ void step(int m) {
     if (m % 4 == 0 && m / 4 + 1 < 8) read_pb(m / 4 + 1);
     if (m >= 10 && m < 14) read_va(1, m - 10);
-    pv_mfma<C>(s, m & 3, (m >> 2) & 3, va[m >> 4][m & 3], pb[(m >> 2) & 1]);
+    if constexpr (CODES) {
+      // k step 1's operands replace k step 0's, which are dead from MFMA 16 on
+      if (m >= 16 && m < 20) va[0][m - 16] = e4m3x8_to_bf16x8(raw1[m - 16]);
+      pv_mfma<C>(s, m & 3, (m >> 2) & 3, va[0][m & 3], pb[(m >> 2) & 1]);
+    } else {
+      pv_mfma<C>(s, m & 3, (m >> 2) & 3, va[m >> 4][m & 3], pb[(m >> 2) & 1]);
+    }
   }
 };
 
@@ -789,18 +807,14 @@ constexpr int kPvEarly = 0;
 // that execute while it runs, and scheduling barriers keep the compiler from
 // regrouping them. The arithmetic is that of softmax_tile in the same order,
 // so contiguous and paged caches give identical bits.
-// E4M3: rtile holds the tile's per-token factors r (see E4m3Ring): they
-// multiply the scores and, after the denominator has taken the
-// probabilities, the probabilities that enter the latent sum. That path adds
-// the denominator's terms in token-pair order (it shares no bits with the
-// 16-bit cache's paths).
-// tail(g) runs beside latent-sum MFMAs 24 .. 31, which have no softmax work
-// beside them (the e4m3 loop widens the next tile there).
-template <class C, bool E4M3, class Tail>
-__device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char* __restrict__ pw,
-                                                  const Scores<C>& sc, State<C>& s, int nvalid, float scale_log2,
-                                                  bool first, const MLA_LDS float* __restrict__ rtile,
-                                                  Tail&& tail) {
+// E4M3: the scores are fs (s_t lat + rope) (see QF8), with the tile's
+// per-token scales s_t in `scl` (token 8 w + i at float 64 w + i), and the
+// probabilities enter the latent sum times s_t once the denominator has taken
+// them. `scale_log2` is fs there.
+template <class C, bool E4M3, class PS>
+__device__ __forceinline__ void softmax_pv_stream(PS& pvs, MLA_LDS char* __restrict__ pw, const Scores<C>& sc,
+                                                  State<C>& s, int nvalid, float scale_log2, bool first,
+                                                  const MLA_LDS float* __restrict__ scl, f32x4 sg_next = {}) {
 #pragma clang fp contract(off)
   static_assert(!C::F32 && !C::FP8 && C::NFJ == 4 && C::HB == 4, "32 latent-sum MFMAs, 16 scores per lane");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5, r = lane & 31;
@@ -815,10 +829,17 @@ __device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char*
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     mfma(g);
-    f32x4 rg = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (E4M3) rg = *(const MLA_LDS f32x4*)(rtile + 8 * g + 4 * hh);
+    if constexpr (E4M3) {
+      // scales of tokens 8 g + 4 hh + 0..3, read one group ahead (the
+      // caller reads group 0's)
+      const f32x4 sg = sg_next;
+      if (g < 3) sg_next = *(const MLA_LDS f32x4*)(scl + 64 * (g + 1) + 4 * hh);
 #pragma unroll
-    for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = (E4M3 ? sc.lat[i] * rg[i - 4 * g] : sc.lat[i]) * scale_log2;
+      for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = __builtin_fmaf(sc.lat[i], sg[i - 4 * g], sc.rope[i]) * scale_log2;
+    } else {
+#pragma unroll
+      for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = sc.lat[i] * scale_log2;
+    }
     sync();
   }
   // maximum over this lane's 16 tokens (exact in any order)
@@ -843,59 +864,42 @@ __device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char*
   s.m_max = fmaxf(s.m_max, mt);
   s.overflow = s.overflow || (mt > s.m_ref + kHeadroom);
   sync();
-  if constexpr (E4M3) {
-    // probabilities, two per MFMA; the denominator takes them as they are,
-    // the latent sum times their tokens' r (read in pairs, tokens
-    // 8 (g / 2) + 4 hh + 2 (g % 2) + 0, 1)
-    float lsum = 0.0f;
+  // probabilities, two per MFMA
+  f32x4 sj_next = {};
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      mfma(9 + g);
-      const int tok = 8 * (g >> 1) + 4 * hh + 2 * (g & 1);
-      float p0 = fast_exp2(x[2 * g] - s.m_ref), p1 = fast_exp2(x[2 * g + 1] - s.m_ref);
-      if (nvalid < C::T) {    // partial tile (uniform): tokens past the end weigh nothing
-        p0 = tok < nvalid ? p0 : 0.0f;
-        p1 = tok + 1 < nvalid ? p1 : 0.0f;
-      }
-      lsum += p0 + p1;
-      typedef float f32x2 __attribute__((ext_vector_type(2)));
-      const f32x2 rr = *(const MLA_LDS f32x2*)(rtile + tok);
-      pv[2 * g] = p0 * rr[0];
-      pv[2 * g + 1] = p1 * rr[1];
-      sync();
-    }
-    for (int j = 17; j < 21; ++j) mfma(j);
-    mfma(21);
-    s.l += lsum;
-    sync();
-  } else {
-    // probabilities, two per MFMA
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      mfma(9 + g);
-      pv[2 * g] = fast_exp2(x[2 * g] - s.m_ref);
-      pv[2 * g + 1] = fast_exp2(x[2 * g + 1] - s.m_ref);
-      sync();
-    }
-    if (nvalid < C::T) {    // partial tile (uniform): tokens past the end weigh nothing
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
-        pv[i] = tok < nvalid ? pv[i] : 0.0f;
-      }
-    }
-    sync();
-    float q4[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      mfma(17 + j);
-      q4[j] = (pv[4 * j] + pv[4 * j + 1]) + (pv[4 * j + 2] + pv[4 * j + 3]);
-      sync();
-    }
-    mfma(21);
-    s.l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
+  for (int g = 0; g < 8; ++g) {
+    mfma(9 + g);
+    if (E4M3 && g == 6) sj_next = *(const MLA_LDS f32x4*)(scl + 4 * hh);
+    pv[2 * g] = fast_exp2(x[2 * g] - s.m_ref);
+    pv[2 * g + 1] = fast_exp2(x[2 * g + 1] - s.m_ref);
     sync();
   }
+  if (nvalid < C::T) {    // partial tile (uniform): tokens past the end weigh nothing
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tok = 8 * (i >> 2) + 4 * hh + (i & 3);
+      pv[i] = tok < nvalid ? pv[i] : 0.0f;
+    }
+  }
+  sync();
+  float q4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    mfma(17 + j);
+    q4[j] = (pv[4 * j] + pv[4 * j + 1]) + (pv[4 * j + 2] + pv[4 * j + 3]);
+    if constexpr (E4M3) {
+      // the denominator has taken them; the latent sum takes them times
+      // their tokens' scales (tokens 8 j + 4 hh + 0..3, read one group ahead)
+      const f32x4 sj = sj_next;
+      if (j < 3) sj_next = *(const MLA_LDS f32x4*)(scl + 64 * (j + 1) + 4 * hh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[4 * j + i] *= sj[i];
+    }
+    sync();
+  }
+  mfma(21);
+  s.l += (q4[0] + q4[1]) + (q4[2] + q4[3]);
+  sync();
   // P^T rows of this wave's heads: element e of k step u is token
   // 16u + 8(e/4) + 4hh + e%4, i.e. pv[8u + e]
   u32x4 pk[2];
@@ -910,20 +914,9 @@ __device__ __forceinline__ void softmax_pv_stream(PvSched<C>& pvs, MLA_LDS char*
   const int head = 32 * wave + r;
 #pragma unroll
   for (int u = 0; u < 2; ++u) *(MLA_LDS u32x4*)(pw + p_off<C>(head, 2 * u + hh)) = pk[u];
-  if constexpr (E4M3) {
-    tail(24);
-    sync();
+  sync();
 #pragma unroll
-    for (int g = 25; g < 32; ++g) {
-      mfma(g);
-      tail(g);
-      sync();
-    }
-  } else {
-    sync();
-#pragma unroll
-    for (int g = 25; g < 32; ++g) mfma(g);
-  }
+  for (int g = 25; g < 32; ++g) mfma(g);
 }
 
 // Where the streamed tiles of one split start. A contiguous cache adds the
@@ -978,174 +971,254 @@ struct StreamTile {
   }
 };
 
-// An e4m3 cache streamed through the 16-bit tile loop. Each tile's codes and
-// per-token scales land in one of two landing buffers; at the end of the
-// step before the tile is scored, every thread widens the code chunks it
-// loaded itself into one of three 16-bit tile slots. The per-token scale s
-// is split as s = 2^e r with r in [1, 2): the widen multiplies each code by
-// 2^e only (exact in bf16: one conversion instruction per two codes), the
-// rotary key, which lands in the slot in bf16, is divided by r in place, and
-// r itself goes to a 32-float array beside the slot. The score of token j is
-// then r_j times the 16-bit product, and its probability enters the latent
-// sum times r_j, so the latent part carries no rounding beyond the codes'.
-// LDS: slot, landing, slot, slot, landing, P^T buffers, r arrays, so that
-// the staged query (from the second slot on) avoids the first slot and the
-// first landing buffer, where tile 0 arrives.
+// An e4m3 cache streamed as codes (contiguous layout). The codes stay e4m3 in
+// LDS: the scores take them directly as fp8 MFMA operands against an exact
+// two-part e4m3 split of the query (QF8), and the latent sum widens them in
+// registers (exact) after a byte-transposing read. The per-token scale s
+// multiplies each token's latent score and, after the denominator has taken
+// the probabilities, each probability that enters the latent sum.
+// LDS: the two P^T buffers first, then a ring of NSLOT tile slots, each
+//   codes:  32 rows x 512 bytes, 16-byte chunk c of row t at c ^ key8(t);
+//   rotary: the bf16 rows in the 16-bit tile's layout;
+//   scales: one 256-byte row per wave, token 8 w + i at float 64 w + i.
+// The query is staged from the third slot on, clear of tiles 0 and 1, and the
+// bf16 output rows are staged after the P^T buffers (where the denominators
+// are) at the end.
 template <class C>
-struct E4m3Ring {
-  static constexpr int SLOT = C::BUF_BYTES;
-  static constexpr int CODES = C::T * C::DC;                // one byte per code
-  static constexpr int SCALES = C::WAVES * 256;             // one 256-byte scale row per wave
-  static constexpr int LAND = CODES + SCALES;
-  static constexpr int S0 = 0, L0 = SLOT, S1 = L0 + LAND, S2 = S1 + SLOT, L1 = S2 + SLOT, P = L1 + LAND;
-  static constexpr int RS = P + 2 * C::P_BYTES;             // r of each slot's tokens, 3 x 32 floats
-  static constexpr int BYTES = RS + 3 * C::T * 4;
-  static constexpr int LPT = 6;                             // per thread: 4 code chunks, scales, rotary
-  static_assert(!C::F32 && !C::FP8 && C::WAVES == 4 && C::T == 32, "16-bit DeepSeek-V2 slots");
-  static_assert(BYTES <= C::LDS_BYTES, "LDS budget");
-  static_assert(S1 + 4 * QStage<C>::BYTES <= P, "the staged query ends before the P^T buffers");
-  static_assert(CODES == C::THREADS * 4 * 16, "four 16-code chunks per thread");
+struct F8Ring {
+  static constexpr int CODES = C::T * C::DC;                  // one byte per code
+  static constexpr int ROPE = CODES;                          // offset of the rotary rows in a slot
+  static constexpr int SCL = ROPE + C::ROPE_BYTES;            // offset of the scales
+  static constexpr int SLOT = SCL + C::WAVES * 256;
+  static constexpr int NSLOT = 5, AHEAD = NSLOT - 2;          // tiles in flight beyond the next one
+  static constexpr int P = 0, S0 = 2 * C::P_BYTES;            // P^T buffers, first slot
+  static constexpr int LPT = 6;                               // loads per thread and tile
+  static constexpr int QROPE = S0 + NSLOT * SLOT;             // per wave: the query's rotary fragments
+  static constexpr int QROPE_BYTES = C::NKC_ROPE * 64 * 16;
+  static constexpr int STAGE = S0;                            // output staging at the end
+  static_assert(!C::F32 && !C::FP8 && C::WAVES == 4 && C::T == 32 && C::DC == 512, "DeepSeek-V2 shapes");
+  static_assert(QROPE + C::WAVES * QROPE_BYTES <= C::LDS_BYTES, "LDS budget");
+  static_assert(S0 + 2 * SLOT + C::WAVES * QStage<C>::BYTES <= C::LDS_BYTES, "staged query after slots 0, 1");
+  static_assert(CODES == C::THREADS * 4 * 16, "four 16-byte code chunks per thread");
 };
 
-struct NoE4m3Ring {   // stands in where no e4m3 ring is used
-  static constexpr int S0 = 0, L0 = 0, S1 = 0, S2 = 0, L1 = 0, P = 0, RS = 0, LPT = 0;
-};
+// Swizzle key of code row t (512-byte rows, 16-byte chunks): bits (3, 1, 0, 2)
+// of t mod 16. The score reads (16 consecutive rows at one chunk) and the
+// transposing reads of the latent sum (8 rows of one 4-row parity at two
+// neighbouring chunks, or 16 rows at one chunk) all land on distinct slots.
+__device__ __forceinline__ int key8(int t) { return (t & 8) | ((t & 3) << 1) | ((t >> 2) & 1); }
 
 // Loads of one e4m3 tile: wave w, lane i loads code chunk i % 32 of rows
-// 8w + 2k + i / 32 (k = 0..3: two whole 512-byte rows per instruction) and,
-// in one more instruction, the scales of rows 8w .. 8w + 7 (lanes 0..7).
-// Every code and scale a thread widens was loaded by its own wave. Rows past
-// the split's end repeat its last row; tiles past the end repeat the last.
+// 8w + 2k + i / 32 (k = 0..3: two whole 512-byte rows per instruction), the
+// scales of rows 8w .. 8w + 7 (lanes 0..7, repeated) and the rotary chunks of
+// rows 8w .. 8w + 7. Rows past the split's end repeat its last row; tiles past
+// the end repeat the last tile.
 template <class C>
-struct E4m3Tile {
+struct F8Tile {
   const DecodeParams& p;
   int64_t row0;         // the tile's first cache row
   int last;
-  __device__ __forceinline__ E4m3Tile(const DecodeParams& p_, int64_t seq_row, int t, int ntiles, int start,
-                                      int end)
+  __device__ __forceinline__ F8Tile(const DecodeParams& p_, int64_t seq_row, int t, int ntiles, int start, int end)
       : p(p_) {
     const int tb = start + min(t, ntiles - 1) * C::T;
     last = min(end - tb, C::T) - 1;
     row0 = seq_row + tb;
   }
-  // rows r0 = 8w + 2k (lanes 0..31) and r0 + 1 (lanes 32..63), both clamped
-  // to `last`: a scalar row address plus a 32-bit lane offset
-  __device__ __forceinline__ void issue_codes(MLA_LDS char* land, int wave, int k) const {
+  __device__ __forceinline__ void codes(MLA_LDS char* slot, int wave, int k) const {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     const int r0 = 8 * wave + 2 * k, rs = (int)p.row_stride;
     const int step = r0 + 1 <= last ? rs : 0;
     const auto res = buffer_rsrc((const char*)p.latent + row0 * p.row_stride, (uint32_t)(C::T * rs));
-    buf_load16_to_lds(res, (uint32_t)((lane >> 5) * step + 16 * (lane & 31)), (uint32_t)(min(r0, last) * rs),
-                      land + (4 * wave + k) * 1024);
+    const int chunk = (lane & 31) ^ key8(r0 + (lane >> 5));   // the destination row's key
+    buf_load16_to_lds(res, (uint32_t)((lane >> 5) * step + 16 * chunk), (uint32_t)(min(r0, last) * rs),
+                      slot + r0 * C::DC);
   }
-  __device__ __forceinline__ void issue_scales(MLA_LDS char* land, int wave) const {
+  __device__ __forceinline__ void scales(MLA_LDS char* slot, int wave) const {
     const int row = min(8 * wave + (int)(threadIdx.x & 7), last);
     const auto res = buffer_rsrc(p.scale + row0, (uint32_t)(C::T * 4));
-    buf_load4_to_lds(res, (uint32_t)(4 * row), 0u, land + E4m3Ring<C>::CODES + wave * 256);
+    buf_load4_to_lds(res, (uint32_t)(4 * row), 0u, slot + F8Ring<C>::SCL + wave * 256);
   }
-  // rotary parts into the slot, as the 16-bit loader places them
-  __device__ __forceinline__ void issue_rope(const DmaOffs& dma, MLA_LDS char* slot, int wave) const {
+  __device__ __forceinline__ void rope(const DmaOffs& dma, MLA_LDS char* slot, int wave) const {
     const int row = min((int)(threadIdx.x >> 3), last);
     const int rs2 = (int)(p.rope_stride * 2);
     const auto res = buffer_rsrc((const char*)p.rope + row0 * (p.rope_stride * 2), (uint32_t)(C::T * rs2));
     buf_load16_to_lds(res, (uint32_t)(row * rs2 + (dma.rope_chunk - C::DC * C::ESZ)), 0u,
-                      slot + C::LAT_BYTES + wave * 64 * 16);
+                      slot + F8Ring<C>::ROPE + wave * 64 * 16);
+  }
+  __device__ __forceinline__ void all(const DmaOffs& dma, MLA_LDS char* slot, int wave) const {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) codes(slot, wave, k);
+    scales(slot, wave);
+    rope(dma, slot, wave);
   }
 };
 
-// The significand r in [1, 2) of a normal scale s = 2^e r (a zero scale gives
-// r = 1 and a code times 2^-127, i.e. zero to within bf16's range).
-__device__ __forceinline__ float scale_significand(float s) {
-  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, s) & 0x007fffffu) | 0x3f800000u);
+// Per-lane LDS offsets of the e4m3 loop (the LaneOffs fields, reused):
+//  lat:   score operand of latent block b (64 codes), half x: (lat ^ 64 b) ^ 16 x
+//         (lane (g, r): row r, bytes 64 b + 32 g .. + 31);
+//  rope:  rotary score operand of k block kk: rope ^ 32 kk (as the 16-bit tile);
+//  pv[0]: transposing read of C_KV^T fragment j, k step u: (pv[0] ^ 32 j) + 8 KiB u;
+//  p:     P^T reads, as in the 16-bit loop.
+// Transposing reads: source lane (a, k) of 16-lane group G = 2 hh + sub points
+// at token 8 (k / 4) + 4 hh + k % 4 (+ 16 u) and bytes 128 w + 32 j + 16 sub
+// + 8 a .. + 7, so that lane (G, x) receives feature 128 w + 32 j + 16 sub + x
+// of the tokens that element e of the P^T operand of lane half hh stands for.
+template <class C>
+__device__ __forceinline__ LaneOffs<C> lane_offsets_f8(int wave) {
+  LaneOffs<C> o = lane_offsets<C>(wave);
+  const int lane = threadIdx.x & 63, hh = lane >> 5, r = lane & 31;
+  o.lat = r * C::DC + 16 * ((2 * hh) ^ key8(r));
+  o.rope = o.rope - C::LAT_BYTES + F8Ring<C>::ROPE;
+  const int G = lane >> 4, x = lane & 15, sub = G & 1, hg = G >> 1, k = x >> 1, a = x & 1;
+  const int tok = 8 * (k >> 2) + 4 * hg + (k & 3);
+  o.pv[0] = (tok * C::DC + 16 * (sub ^ key8(tok)) + 8 * a) ^ (128 * wave);
+  o.pv[1] = 0;
+  return o;
 }
 
-// Widen this thread's code chunks of one landed tile: 16 codes -> 16 bf16
-// values code * 2^e (exact; the conversion applies the exponent of the scale
-// operand only), two 16-byte chunks of the slot's latent row. Then divide
-// the rotary chunk this thread's own wave loaded (row 8 wave + lane / 8) by
-// its token's r, and record r for the softmax.
-template <class C>
-__device__ __forceinline__ void e4m3_widen(const MLA_LDS char* __restrict__ land, MLA_LDS char* __restrict__ slot,
-                                           MLA_LDS float* __restrict__ rsl, int wave) {
-  // opaque, so that the offsets below are computed here and not kept live
-  // across the whole tile loop
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));
-  const MLA_LDS float* scales = (const MLA_LDS float*)(land + E4m3Ring<C>::CODES + wave * 256);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int t = 8 * wave + 2 * k + (lane >> 5), c = lane & 31;
-    const u32x4 w = *(const MLA_LDS u32x4*)(land + (4 * wave + k) * 1024 + 16 * lane);
-    const float sc = scales[2 * k + (lane >> 5)];
-    uint32_t o[8];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      o[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[d], sc, false));
-      o[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[d], sc, true));
-    }
-    *(MLA_LDS u32x4*)(slot + lat_off<C>(t, 32 * c)) = u32x4{o[0], o[1], o[2], o[3]};
-    *(MLA_LDS u32x4*)(slot + lat_off<C>(t, 32 * c + 16)) = u32x4{o[4], o[5], o[6], o[7]};
-  }
-  const float r = scale_significand(scales[lane >> 3]);
-  const float inv = 1.0f / r;
-  MLA_LDS u32x4* rp = (MLA_LDS u32x4*)(slot + C::LAT_BYTES + wave * 64 * 16 + 16 * lane);
-  u32x4 v = *rp;
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    v[d] = pack_bf16x2(bf16_bits_to_f32(v[d] & 0xffffu) * inv, bf16_bits_to_f32(v[d] >> 16) * inv);
-  *rp = v;
-  if ((lane & 7) == 0) rsl[8 * wave + (lane >> 3)] = r;
+// Block b's chunks sit at base ^ 64 b: the base holds no bit 8 (the key
+// flips chunk bits 0..3), so the high bit of b is an offset of 256 bytes.
+template <class T>
+__device__ __forceinline__ T* opaque_lds(T* p) {
+  uint32_t v = (uint32_t)(size_t)p;
+  asm volatile("" : "+s"(v));
+  return (T*)(size_t)v;
 }
 
-// The same widen in stages, for the free slots at the end of the softmax
-// schedule: load() reads this thread's code chunks, their scales and its
-// rotary chunk; codes(k) converts and stores chunk k; rope() divides the
-// rotary chunk by r and records r.
+__device__ __forceinline__ i32x8 code_operand(const MLA_LDS char* buf, int base, int b) {
+  const int o = (base ^ (64 * (b & 3))) + 256 * (b >> 2);
+  const int o1 = (base ^ (64 * (b & 3)) ^ 16) + 256 * (b >> 2);
+  const u32x4 x0 = *(const MLA_LDS u32x4*)(buf + o);
+  const u32x4 x1 = *(const MLA_LDS u32x4*)(buf + o1);
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <class C>
-struct E4m3Widen {
-  const MLA_LDS char* __restrict__ land;
-  MLA_LDS char* __restrict__ slot;
-  MLA_LDS float* __restrict__ rsl;
-  int wave, lane;
-  u32x4 w[4], rope_v;
-  float sc[4], rs;
-  __device__ __forceinline__ void load() {
-    const MLA_LDS float* scales = (const MLA_LDS float*)(land + E4m3Ring<C>::CODES + wave * 256);
+__device__ __forceinline__ bf16x8 pv_operand_f8(const MLA_LDS char* buf, const LaneOffs<C>& lo, int j, int u) {
+  return e4m3x8_to_bf16x8(lds_read_tr8(buf + ((lo.pv[0] ^ (32 * j)) + C::DC * 16 * u)));
+}
+
+// The absorbed query of this wave's 32 heads as operands of the fp8 score
+// products (the rotary fragments, 16 bytes per lane and k block, go to the
+// wave's F8Ring::QROPE region, lane l's fragment kk at 16 (64 kk + l)). Head n's latent part is split exactly as q = 2^e (hi + 2^-4 lo)
+// with hi, lo e4m3 and e per head (its largest |q| / 2^e in [128, 256)): hi
+// rounds q / 2^e to four significant bits, and what a bf16 value has beyond
+// them, at most four more bits, is lo (exact for values down to 2^13 below
+// the head's largest; smaller ones round to e4m3's subnormal spacing). The
+// rotary part stays bf16, times 2^-e, so that the scaled score of token t is
+// fs (s_t (hi + 2^-4 lo) . codes + 2^-e q_R . k_R) with one factor fs = 2^e
+// scale log2(e) per lane.
+template <class C>
+struct QF8 {
+  i32x8 hi[C::DC / 64], lo[C::DC / 64];   // block b: lane (g, n) holds k = 64 b + 32 g .. + 31 of head n
+  float fs;
+};
+
+// The staged bf16 query as read from LDS: latent block b, 16-byte chunk c of
+// lane (g, n) is chunk 8 b + 4 g + c of head n's row; the rotary fragments as
+// the 16-bit loop reads them.
+template <class C>
+struct QRaw {
+  u32x4 v[C::DC / 64][4];
+  bf16x8 rope[C::NKC_ROPE];
+};
+
+// One staged half (chunks 0 .. 35 or 36 .. 71 of each head row). The block
+// that straddles the halves (b = 4) is chunks 32 .. 35 for lane half g = 0
+// and 36 .. 39 for g = 1: each lane keeps the read from its own half.
+template <class C>
+__device__ __forceinline__ void stage_q_read_f8(QRaw<C>& q, int half, const MLA_LDS char* region) {
+  using Q = QStage<C>;
+  const int lane = threadIdx.x & 63, g = lane >> 5, r = lane & 31;
+  auto rd = [&](int chunk) { return *(const MLA_LDS u32x4*)(region + (r * Q::PITCH + chunk) * 16); };
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      w[k] = *(const MLA_LDS u32x4*)(land + (4 * wave + k) * 1024 + 16 * lane);
-      sc[k] = scales[2 * k + (lane >> 5)];
-    }
-    rope_v = *(const MLA_LDS u32x4*)(slot + C::LAT_BYTES + wave * 64 * 16 + 16 * lane);
-    rs = scales[lane >> 3];
-  }
-  __device__ __forceinline__ void codes(int k) {
-    const int t = 8 * wave + 2 * k + (lane >> 5), c = lane & 31;
-    uint32_t o[8];
+  for (int b = 0; b < C::DC / 64; ++b)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      o[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k][d], sc[k], false));
-      o[2 * d + 1] =
-          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[k][d], sc[k], true));
+    for (int c = 0; c < 4; ++c) {
+      const int ch0 = 8 * b + c;   // chunk of lane half 0; half 1 adds 4
+      if (ch0 + 4 < Q::HALF) {
+        if (half == 0) q.v[b][c] = rd(ch0 + 4 * g);
+      } else if (ch0 >= Q::HALF) {
+        if (half == 1) q.v[b][c] = rd(ch0 + 4 * g - Q::HALF);
+      } else if (half == 0) {
+        const u32x4 x = rd(min(ch0 + 4 * g, Q::HALF - 1));
+        if (g == 0) q.v[b][c] = x;
+      } else {
+        const u32x4 x = rd(max(ch0 + 4 * g - Q::HALF, 0));
+        if (g == 1) q.v[b][c] = x;
+      }
     }
-    *(MLA_LDS u32x4*)(slot + lat_off<C>(t, 32 * c)) = u32x4{o[0], o[1], o[2], o[3]};
-    *(MLA_LDS u32x4*)(slot + lat_off<C>(t, 32 * c + 16)) = u32x4{o[4], o[5], o[6], o[7]};
+  if (half == 1) {
+#pragma unroll
+    for (int kk = 0; kk < C::NKC_ROPE; ++kk)
+      q.rope[kk] = *(const MLA_LDS bf16x8*)(region + (r * Q::PITCH + 2 * (C::NKC_LAT + kk) + g - Q::HALF) * 16);
   }
-  __device__ __forceinline__ void rope() {
-    const float r = scale_significand(rs);
-    const float inv = 1.0f / r;
-    u32x4 v = rope_v;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before the region is refilled
+}
+
+__device__ __forceinline__ float pow2i(int e) {   // 2^e, -126 <= e <= 127
+  return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+template <class C>
+__device__ __forceinline__ void split_query_f8(QF8<C>& q, const QRaw<C>& raw, float scale_log2,
+                                               MLA_LDS char* __restrict__ qrope) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  // largest magnitude of the head (latent and rotary parts): bf16 magnitudes
+  // order as 15-bit integers
+  u16x2 m2 = {0, 0};
+#pragma unroll
+  for (int b = 0; b < C::DC / 64; ++b)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, raw.v[b][c][d] & 0x7fff7fffu));
+#pragma unroll
+  for (int kk = 0; kk < C::NKC_ROPE; ++kk) {
+    const u32x4 w = __builtin_bit_cast(u32x4, raw.rope[kk]);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[d] & 0x7fff7fffu));
+  }
+  uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 32));   // lanes n and n + 32 hold one head
+  // largest / 2^e in [128, 256): e = exponent(largest) - 7
+  const int e = max((int)(m >> 7) - 134, -120);
+  const float sh = pow2i(e), sl = pow2i(e - 4), inv = pow2i(-e);
+#pragma unroll
+  for (int b = 0; b < C::DC / 64; ++b) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t w0 = raw.v[b][d >> 1][2 * (d & 1)], w1 = raw.v[b][d >> 1][2 * (d & 1) + 1];
+      const float x0 = __builtin_bit_cast(float, w0 << 16), x1 = __builtin_bit_cast(float, w0 & 0xffff0000u);
+      const float x2 = __builtin_bit_cast(float, w1 << 16), x3 = __builtin_bit_cast(float, w1 & 0xffff0000u);
+      i16x2v h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2v{0, 0}, x0, x1, sh, false);
+      h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(h, x2, x3, sh, true);
+      const int hw = __builtin_bit_cast(int, h);
+      const f32x2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, sh, false);
+      const f32x2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hw, sh, true);
+      i16x2v l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2v{0, 0}, x0 - b01[0], x1 - b01[1], sl, false);
+      l = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(l, x2 - b23[0], x3 - b23[1], sl, true);
+      q.hi[b][d] = hw;
+      q.lo[b][d] = __builtin_bit_cast(int, l);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < C::NKC_ROPE; ++kk) {
+    const u32x4 w = __builtin_bit_cast(u32x4, raw.rope[kk]);
+    u32x4 o;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
-      v[d] = pack_bf16x2(bf16_bits_to_f32(v[d] & 0xffffu) * inv, bf16_bits_to_f32(v[d] >> 16) * inv);
-    *(MLA_LDS u32x4*)(slot + C::LAT_BYTES + wave * 64 * 16 + 16 * lane) = v;
-    if ((lane & 7) == 0) rsl[8 * wave + (lane >> 3)] = r;
+      o[d] = pack_bf16x2(bf16_bits_to_f32(w[d] & 0xffffu) * inv, bf16_bits_to_f32(w[d] >> 16) * inv);
+    *(MLA_LDS u32x4*)(qrope + (kk * 64 + (threadIdx.x & 63)) * 16) = o;
   }
-};
+  q.fs = sh * scale_log2;
+}
 
-struct NoTailWork {
-  __device__ __forceinline__ void operator()(int) const {}
+struct NoF8Ring {   // stands in where no e4m3 ring is used
+  static constexpr int S0 = 0, P = 0, SLOT = 0, NSLOT = 1, AHEAD = 0, LPT = 0, STAGE = 0, QROPE = 0,
+                       QROPE_BYTES = 0;
 };
 
 // Steady state for a contiguous 16-bit cache: one basic block per tile.
@@ -1155,27 +1228,21 @@ struct NoTailWork {
 // softmax of tile t. Past the end of the split the loads fetch the last tile
 // again (its rows are still in L2 and its slot is not read), which keeps the
 // per-thread load count, and with it the vmcnt wait, the same for every tile.
-template <class C, bool PAGED, bool E4M3>
+template <class C, bool PAGED>
 __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const MLA_LDS char* __restrict__ cur,
                                                  const MLA_LDS char* __restrict__ prev,
                                                  MLA_LDS char* __restrict__ fill, MLA_LDS char* __restrict__ pw,
                                                  const MLA_LDS char* __restrict__ pr, const QFrag<C>& q,
                                                  State<C>& s, LaneOffs<C>& lo, DmaOffs& dma, const TileBase& tbase,
-                                                 int t, int ntiles, int start, int end, bool first,
-                                                 MLA_LDS char* __restrict__ land_fill = nullptr,
-                                                 const MLA_LDS char* __restrict__ land_next = nullptr,
-                                                 MLA_LDS char* __restrict__ next = nullptr, int64_t seq_row = 0,
-                                                 const MLA_LDS float* __restrict__ r_cur = nullptr,
-                                                 MLA_LDS float* __restrict__ r_next = nullptr) {
+                                                 int t, int ntiles, int start, int end, bool first) {
   static_assert(!C::F32 && !C::FP8 && C::LAT_CH == 64 && C::WAVES == 4, "16-bit DeepSeek-V2 layout");
-  constexpr int LPT = E4M3 ? E4m3Ring<C>::LPT : loads_per_tile<C>();
-  static_assert(E4M3 || LPT == C::T / C::WAVES + 1, "nine loads per tile");
+  constexpr int LPT = loads_per_tile<C>();
+  static_assert(LPT == C::T / C::WAVES + 1, "nine loads per tile");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   refresh<C>(lo);
   asm volatile("" : "+v"(dma.lat), "+v"(dma.rope_chunk));
 
   const StreamTile<C> ld(p, tbase, t + 2, ntiles, start, end, std::integral_constant<bool, PAGED>{});   // tile t + 2
-  const E4m3Tile<C> ld8(p, seq_row, t + 2, ntiles, start, end);
   Scores<C> sc;
   sc.lat = f32x16{};
   sc.rope = f32x16{};
@@ -1190,10 +1257,8 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
   bf16x8 a0 = qk_operand<C>(cur, lo, 0), a1 = qk_operand<C>(cur, lo, 1), a2 = qk_operand<C>(cur, lo, 2);
 #pragma unroll
   for (int kc = 0; kc < C::NKC; ++kc) {
-    if constexpr (!E4M3) {
-      if (kc % 4 == 0 && kc / 4 < LAT_LOADS) ld.latent(dma, fill, wave, kc / 4);
-      if (kc == 4 * LAT_LOADS) ld.rope(dma, fill, wave);
-    }
+    if (kc % 4 == 0 && kc / 4 < LAT_LOADS) ld.latent(dma, fill, wave, kc / 4);
+    if (kc == 4 * LAT_LOADS) ld.rope(dma, fill, wave);
     if (kc >= PF + 2 && kc < PF + 6) pvs.read_va(0, kc - (PF + 2));
     if (kc == PF + 6) pvs.read_pb(0);
     const bf16x8 a3 = kc + 3 < C::NKC ? qk_operand<C>(cur, lo, kc + 3) : bf16x8{};
@@ -1202,34 +1267,111 @@ __device__ __forceinline__ void tile_step_stream(const DecodeParams& p, const ML
     if (kc >= PV0) pvs.step(kc - PV0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (E4M3) {
-    // tile t + 2 is requested after the score MFMAs (spread through them,
-    // its address arithmetic made the loop spill; issued before them, the
-    // launch took 4% longer)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) ld8.issue_codes(land_fill, wave, k);
-    ld8.issue_scales(land_fill, wave);
-    ld8.issue_rope(dma, fill, wave);
-    // tile t + 1 (requested one step earlier) has landed once only tile
-    // t + 2's loads are outstanding; it is widened beside the last
-    // latent-sum MFMAs, into a slot nothing reads during this step (4%
-    // faster than widening it after them)
-    wait_vmem_le<LPT>();
-    int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));
-    E4m3Widen<C> wd{land_next, next, r_next, wave, lane};
-    auto tail = [&](int g) {
-      if (g == 24) wd.load();
-      else if (g >= 26 && g < 30) wd.codes(g - 26);
-      else if (g == 30) wd.rope();
-    };
-    softmax_pv_stream<C, true>(pvs, pw, sc, s, end - (start + t * C::T), p.scale_log2, first, r_cur, tail);
-  } else {
-    softmax_pv_stream<C, false>(pvs, pw, sc, s, end - (start + t * C::T), p.scale_log2, first, r_cur,
-                                NoTailWork{});
-    wait_vmem_le<LPT>();
-  }
+  softmax_pv_stream<C, false>(pvs, pw, sc, s, end - (start + t * C::T), p.scale_log2, first, nullptr);
+  wait_vmem_le<LPT>();
   tile_barrier();
+}
+
+// Steady state for a contiguous e4m3 cache (F8Ring), one basic block per
+// tile. Step t requests tile t + AHEAD (its six loads spread through the
+// score products), scores tile t with fp8 products of the codes against the
+// split query (eight latent blocks of 64 codes, hi and lo, then the four
+// rotary blocks in bf16), and runs the softmax of tile t beside the
+// latent-sum MFMAs of tile t - 1, whose operands are widened from the codes
+// in registers. Tile t + 1 is resident once only the loads of tiles
+// t + 2 .. t + AHEAD are outstanding.
+template <class C>
+__device__ __forceinline__ void tile_step_f8(const DecodeParams& p, const MLA_LDS char* __restrict__ cur,
+                                             const MLA_LDS char* __restrict__ prev, MLA_LDS char* __restrict__ fill,
+                                             MLA_LDS char* __restrict__ pw, const MLA_LDS char* __restrict__ pr,
+                                             const QF8<C>& q, const MLA_LDS char* __restrict__ qrope, State<C>& s,
+                                             LaneOffs<C>& lo, DmaOffs& dma, int64_t seq_row, int t, int ntiles,
+                                             int start, int end, bool first) {
+  using R = F8Ring<C>;
+  constexpr int NB = C::DC / 64;
+  static_assert(NB == 8 && C::NKC_ROPE == 4 && R::LPT == 6, "eight latent blocks, six loads");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  asm volatile("" : "+v"(lo.lat), "+v"(lo.rope), "+v"(lo.pv[0]), "+v"(lo.p), "+v"(dma.rope_chunk));
+  // slot addresses as plain scalars: folded back into the ring arithmetic,
+  // they leave offsets that the LDS instructions' immediate field cannot hold
+  cur = opaque_lds(cur);
+  prev = opaque_lds(prev);
+  pr = opaque_lds(pr);
+  const F8Tile<C> ld(p, seq_row, t + R::AHEAD, ntiles, start, end);
+  Scores<C> sc;
+  sc.lat = f32x16{};
+  bf16x8 va[2][C::NFJ], pb[2];
+  PvSched<C, true> pvs{s, va, pb, prev, pr, lo};
+  // the rotary products first, into VGPRs (the AGPRs hold the latent sums
+  // and the latent score)
+  bf16x8 r0 = qk_operand<C>(cur, lo, C::NKC_LAT), r1 = qk_operand<C>(cur, lo, C::NKC_LAT + 1);
+  // the order below is pinned (scheduling barriers): left to itself, the
+  // compiler moves each operand read next to its MFMA, and the chain of
+  // score products then waits out every LDS read
+  auto sync = [] { __builtin_amdgcn_sched_barrier(0); };
+  const int lane = threadIdx.x & 63;
+  f32x4 sg0;    // the softmax's first scales (tokens 4 hh + 0..3)
+  i32x8 a[2];   // code operands, one block ahead
+  a[0] = code_operand(cur, lo.lat, 0);
+  bf16x8 qr[2];
+  qr[0] = *(const MLA_LDS bf16x8*)(qrope);
+  qr[1] = *(const MLA_LDS bf16x8*)(qrope + 64 * 16);
+  sync();
+#pragma unroll
+  for (int kk = 0; kk < C::NKC_ROPE; ++kk) {
+    bf16x8 r2 = {}, q2 = {};
+    if (kk + 2 < C::NKC_ROPE) {
+      r2 = qk_operand<C>(cur, lo, C::NKC_LAT + kk + 2);
+      q2 = *(const MLA_LDS bf16x8*)(qrope + (kk + 2) * 64 * 16);
+    }
+    if (kk == 0) mfma_vgpr_first(sc.rope, r0, qr[0]);
+    else mfma_vgpr_acc(sc.rope, r0, qr[kk & 1]);
+    r0 = r1;
+    r1 = r2;
+    qr[kk & 1] = q2;
+    sync();
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b + 1 < NB) a[(b + 1) & 1] = code_operand(cur, lo.lat, b + 1);
+    if (b < 4) ld.codes(fill, wave, b);
+    else if (b == 4) ld.scales(fill, wave);
+    else if (b == 5) ld.rope(dma, fill, wave);
+    if (b >= 5 && b < 7) {
+      pvs.read_va(0, 2 * (b - 5));
+      pvs.read_va(0, 2 * (b - 5) + 1);
+    }
+    if (b == 7) pvs.read_pb(0);
+    if (b == 7) sg0 = *(const MLA_LDS f32x4*)((const MLA_LDS char*)cur + R::SCL + 16 * (lane >> 5));
+    sc.lat = mfma32x32x64_e4m3<127>(a[b & 1], q.hi[b], sc.lat);
+    sc.lat = mfma32x32x64_e4m3<123>(a[b & 1], q.lo[b], sc.lat);   // lo carries 2^-4
+    sync();
+  }
+  vgpr_acc_drain(sc.rope);
+  __builtin_amdgcn_sched_barrier(0);
+  softmax_pv_stream<C, true>(pvs, pw, sc, s, end - (start + t * C::T), q.fs, first,
+                             (const MLA_LDS float*)(cur + R::SCL), sg0);
+  wait_vmem_le<(R::AHEAD - 1) * R::LPT>();
+  tile_barrier();
+}
+
+// O^T += C_KV^T . P^T for one tile of e4m3 codes (the last tile of a pass).
+template <class C>
+__device__ __forceinline__ void latent_sum_tile_f8(const MLA_LDS char* __restrict__ buf,
+                                                   const MLA_LDS char* __restrict__ pbuf, State<C>& s,
+                                                   const LaneOffs<C>& lo) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    bf16x8 a[C::NFJ];
+#pragma unroll
+    for (int j = 0; j < C::NFJ; ++j) a[j] = pv_operand_f8<C>(buf, lo, j, u);
+#pragma unroll
+    for (int hb = 0; hb < C::HB; ++hb) {
+      const bf16x8 pb = *(const MLA_LDS bf16x8*)(pbuf + p_rd_off<C>(lo, hb, u));
+#pragma unroll
+      for (int j = 0; j < C::NFJ; ++j) pv_mfma<C>(s, j, hb, a[j], pb);
+    }
+  }
 }
 
 // Which (sequence, split) item a workgroup takes. Workgroups reach the XCDs
@@ -1333,7 +1475,7 @@ template <class C, bool PAGED, bool PSTREAM, bool E4M3, bool LONGEST_FIRST>
 __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   static_assert(!E4M3 || (!PAGED && !C::F32 && !C::FP8), "e4m3 tiles stream through the contiguous 16-bit loop");
-  using R8 = typename std::conditional<E4M3, E4m3Ring<C>, NoE4m3Ring>::type;
+  using R8 = typename std::conditional<E4M3, F8Ring<C>, NoF8Ring>::type;
 
   int b, split, len_b;
   if constexpr (LONGEST_FIRST) {
@@ -1350,15 +1492,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   }
   MLA_LDS char* lds = (MLA_LDS char*)smem;
   auto slot = [&](int x) -> MLA_LDS char* {   // x >= 0
-    if constexpr (E4M3) {
-      const int k = x % 3;
-      return lds + (k == 0 ? R8::S0 : k == 1 ? R8::S1 : R8::S2);
-    } else {
-      return lds + (x % C::NBUF) * C::BUF_BYTES;
-    }
+    if constexpr (E4M3) return lds + R8::S0 + (x % R8::NSLOT) * R8::SLOT;
+    else return lds + (x % C::NBUF) * C::BUF_BYTES;
   };
-  auto land = [&](int x) -> MLA_LDS char* { return lds + ((x & 1) ? R8::L1 : R8::L0); };   // e4m3 landing
-  auto rslot = [&](int x) -> MLA_LDS float* { return (MLA_LDS float*)(lds + R8::RS) + (x % 3) * C::T; };
 
   // 16-bit caches, contiguous or with pages of at least 32 tokens (PSTREAM),
   // stream whole tiles and stage the query through LDS (slots 2..3 and the
@@ -1366,8 +1502,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   // it depends on nothing but the sequence. A paged split's page ids follow.
   constexpr bool STREAM = !C::F32 && !C::FP8 && (!PAGED || PSTREAM);
   static_assert(!PSTREAM || PAGED, "PSTREAM is the paged streaming form");
-  MLA_LDS char* qreg =
-      (E4M3 ? lds + R8::S1 : slot(2)) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * QStage<C>::BYTES;
+  MLA_LDS char* qreg = slot(2) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * QStage<C>::BYTES;
   if constexpr (STREAM) stage_q_issue<C>(p, b, 0, qreg);
   TileBase tbase{(const char*)p.latent, 0, 0, 0};
   if constexpr (PAGED && STREAM) {
@@ -1432,7 +1567,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
     }
   };
   Fp8Stage<C> st;
-  LaneOffs<C> lo = lane_offsets<C>(wave);
+  LaneOffs<C> lo;
+  if constexpr (E4M3) lo = lane_offsets_f8<C>(wave);
+  else lo = lane_offsets<C>(wave);
+  typename std::conditional<E4M3, QF8<C>, int>::type q8{};   // the e4m3 loop's split query
   const SeqView sv = seq_view<PAGED>(p, b);
   DmaOffs dma;
   {
@@ -1456,7 +1594,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
     if (hh == 0) ((MLA_LDS float*)fin)[head] = l_tot;
     const bool wave_overflow = __ballot(s.overflow) != 0;
     if (lane == 0) ((MLA_LDS int*)(fin + kFinFlags))[wave] = wave_overflow ? 1 : 0;
-    latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
+    if constexpr (E4M3) latent_sum_tile_f8<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
+    else latent_sum_tile<C>(slot(ntiles - 1), pslot(ntiles - 1), s, lo);
     if constexpr (!C::F32) vgpr_acc_drain(s.o[C::NFJ - 1][C::HB - 1]);
     __syncthreads();
   };
@@ -1475,39 +1614,41 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       s.overflow = false;
     }
     if constexpr (STREAM && E4M3) {
-      // prologue: tile 0 lands beside the staged query; tile 1's rotary
-      // part goes to a slot the query occupies, so tile 1 is requested once
-      // every wave has read the query; tile 0 is widened meanwhile
+      // prologue: tiles 0 and 1 land beside the staged query (first pass:
+      // requested after its first half); tile 2 goes to the slot the query
+      // occupies, so (first pass) it is requested once every wave has read
+      // the query, and the query is split while it loads
       const int wv = __builtin_amdgcn_readfirstlane(wave);
-      auto issue8 = [&](int x) {
-        const E4m3Tile<C> t8(p, sv.seq_row, x, ntiles, start, end);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) t8.issue_codes(land(x), wv, k);
-        t8.issue_scales(land(x), wv);
-        t8.issue_rope(dma, slot(x), wv);
-      };
+      auto issue8 = [&](int x) { F8Tile<C>(p, sv.seq_row, x, ntiles, start, end).all(dma, slot(x), wv); };
+      static_assert(R8::AHEAD == 3, "tiles 0, 1 and 2 in the prologue");
       issue8(0);
-      if (pass == 0) {
-        wait_vmem_le<R8::LPT>();                  // query half 0
-        stage_q_read<C>(q, 0, qreg);
-        stage_q_issue<C>(p, b, 1, qreg);
-        wait_vmem_le<0>();                        // tile 0 and query half 1
-        stage_q_read<C>(q, 1, qreg);
-        tile_barrier();                           // every wave is done with the staged query
-      }
       issue8(1);
-      if (pass != 0) wait_vmem_le<R8::LPT>();    // tile 0
-      e4m3_widen<C>(land(0), slot(0), rslot(0), wv);
+      if (pass == 0) {
+        QRaw<C> raw;
+        wait_vmem_le<2 * R8::LPT>();              // query half 0
+        stage_q_read_f8<C>(raw, 0, qreg);
+        stage_q_issue<C>(p, b, 1, qreg);
+        wait_vmem_le<0>();                        // tiles 0, 1 and query half 1
+        stage_q_read_f8<C>(raw, 1, qreg);
+        tile_barrier();                           // every wave is done with the staged query
+        issue8(2);
+        split_query_f8<C>(q8, raw, p.scale_log2, lds + R8::QROPE + wv * R8::QROPE_BYTES);
+      } else {
+        issue8(2);
+        wait_vmem_le<2 * R8::LPT>();              // tile 0
+      }
       static_assert(C::P_BYTES == C::THREADS * 32, "two 16-byte zero stores per thread");
       *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32) = u32x4{};
       *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32 + 16) = u32x4{};
       tile_barrier();
+      // step 0 runs its latent sum over tile 0's codes with the zeroed P^T
+      // buffer, which adds exactly zero
 #pragma clang loop unroll(disable)
       for (int t = 0; t < ntiles; ++t) {
         const int tp = max(t - 1, 0), first = pass == 0 && t == 0;
-        tile_step_stream<C, false, true>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma,
-                                         tbase, t, ntiles, start, end, first != 0, land(t), land(t + 1),
-                                         slot(t + 1), sv.seq_row, rslot(t), rslot(t + 1));
+        tile_step_f8<C>(p, slot(t), slot(tp), slot(t + R8::AHEAD), pslot(t), pslot(t - 1), q8,
+                        lds + R8::QROPE + wv * R8::QROPE_BYTES + 16 * lane, s, lo, dma, sv.seq_row, t, ntiles,
+                        start, end, first != 0);
       }
       finish_pass();
     } else if constexpr (STREAM) {
@@ -1535,7 +1676,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
 #pragma clang loop unroll(disable)
       for (int t = 0; t < ntiles; ++t) {
         const int tp = max(t - 1, 0), first = pass == 0 && t == 0;
-        tile_step_stream<C, PAGED, false>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma, tbase, t,
+        tile_step_stream<C, PAGED>(p, slot(t), slot(tp), slot(t + 2), pslot(t), pslot(t - 1), q, s, lo, dma, tbase, t,
                             ntiles, start, end, first != 0);
       }
       finish_pass();
@@ -1577,9 +1718,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
   const float l_tot = s.l + __shfl_xor(s.l, 32);   // every lane takes part in the exchange
   if (hh == 0 && head < C::H) p.lse[out_row<C>(p, b, split, head)] = (s.m_ref + fast_log2(l_tot)) * kLn2;
   // staging of the bf16 rows below: one region of H padded rows per wave,
-  // all before the P^T buffers (where the denominators are)
+  // all clear of the P^T buffers (where the denominators are)
   constexpr int SROW = C::FPW * 2 + 16;
-  constexpr bool STAGE = !C::F32 && C::WAVES * C::H * SROW <= (E4M3 ? R8::P : C::NBUF * C::BUF_BYTES);
+  constexpr int STAGE_AT = E4M3 ? R8::STAGE : 0;
+  constexpr bool STAGE = !C::F32 && (E4M3 ? R8::STAGE + C::WAVES * C::H * SROW <= C::LDS_BYTES
+                                          : C::WAVES * C::H * SROW <= C::NBUF * C::BUF_BYTES);
   if constexpr (STAGE) {
     if (!f32_out) {
       // Lanes r and r + 32 hold alternating runs of four features of head
@@ -1591,7 +1734,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       // region of its own, then reads it back so that every 16 lanes hold
       // one head's slice and each store writes whole 256-byte row segments.
       static_assert(C::FPW * 2 == 16 * 16, "16 lanes a row");
-      MLA_LDS char* stage = lds + wave * (C::H * SROW);
+      MLA_LDS char* stage = lds + STAGE_AT + wave * (C::H * SROW);
 #pragma unroll
       for (int hb = 0; hb < C::HB; ++hb) {
         const int h = 32 * hb + r;
@@ -1679,7 +1822,7 @@ hipError_t launch_order(const DecodeParams& q, int grid, hipStream_t stream) {
     return launch_kernel((decode_kernel<C, true, false, false, LF>), dim3(grid), dim3(C::THREADS), stream, q);
   }
   if constexpr (C::FP8 && C::H == 128 && C::DC == 512 && C::DR == 64) {
-    // contiguous e4m3: widened on the fly into the 16-bit streaming loop
+    // contiguous e4m3: codes streamed into fp8 score products (F8Ring)
     using CB = Cfg<C::H, C::DC, C::DR, kBF16>;
     return launch_kernel((decode_kernel<CB, false, false, true, LF>), dim3(grid), dim3(CB::THREADS), stream, q);
   }

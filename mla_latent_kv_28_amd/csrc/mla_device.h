@@ -4,6 +4,8 @@
 //   v_mfma_f32_32x32x16_bf16: A is 32x16, B is 16x32, C is 32x32.
 //     lane l = 32*hh + r holds A[r][8*hh + 0..7] and B[8*hh + 0..7][r];
 //     accumulator i of lane l is C[8*(i/4) + 4*hh + (i%4)][r].
+//   v_mfma_f32_32x32x64_f8f6f4 (e4m3 operands): lane l holds bytes
+//     A[r][32*hh + 0..31] and B[32*hh + 0..31][r] in order; the same C layout.
 //   v_mfma_f32_32x32x2_f32: lane l holds A[r][hh], B[hh][r]; the same C layout.
 //     Eight of them in a row, the e-th fed with element e of an 8-element lane
 //     vector, contract a 16-wide k block where lane half hh owns k = 8*hh + e,
@@ -24,6 +26,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2v __attribute__((vector_size(4)));   // operand type of the fp8 conversions
 
 #define MLA_LDS __attribute__((address_space(3)))
 
@@ -45,9 +51,11 @@ __device__ __forceinline__ f32x16 mfma32x32x16_f32(const float (&a)[8], const fl
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Two floats to a pair of bf16 (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef __bf16 bf16x2_ __attribute__((ext_vector_type(2)));
+  typedef float f32x2_ __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_){lo, hi}, bf16x2_));
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -100,11 +108,34 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const MLA_LDS void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p);
 }
 
+// Transposing LDS read of bytes: within each 16-lane group, lane 8*a + x
+// receives, as byte k (k = 0..7), byte x of the 8 bytes addressed by source
+// lane 2*k + a (measured on gfx950).
+__device__ __forceinline__ i32x2 lds_read_tr8(const MLA_LDS void* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)p);
+}
+
+// 32x32x64 product of e4m3 operands, B scaled by 2^(SCALE_B - 127) (E8M0).
+// Always the scaled instruction: in a chain of dependent products on gfx950
+// the unscaled form (what zero scales select) issued far slower.
+template <int SCALE_B>
+__device__ __forceinline__ f32x16 mfma32x32x64_e4m3(const i32x8& a, const i32x8& b, const f32x16& c) {
+  static_assert(SCALE_B > 0 && SCALE_B < 255, "an E8M0 scale");
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, SCALE_B);
+}
+
 // Two fp8 e4m3 codes (bytes 0,1 or 2,3 of `w`) to two bf16 values (exact).
 template <bool HIGH_WORD>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HIGH_WORD);
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight e4m3 codes (byte k of `w` = element k) to eight bf16 values (exact).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(const i32x2& w) {
+  const uint32_t a = e4m3x2_to_bf16x2<false>((uint32_t)w[0]), b = e4m3x2_to_bf16x2<true>((uint32_t)w[0]);
+  const uint32_t c = e4m3x2_to_bf16x2<false>((uint32_t)w[1]), d = e4m3x2_to_bf16x2<true>((uint32_t)w[1]);
+  return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
 }
 
 __device__ __forceinline__ float wave_max32(float x) {   // max with the lane 32 away
