@@ -1011,48 +1011,68 @@ __device__ __forceinline__ int key8(int t) { return (t & 8) | ((t & 3) << 1) | (
 // Loads of one e4m3 tile: wave w, lane i loads code chunk i % 32 of rows
 // 8w + 2k + i / 32 (k = 0..3: two whole 512-byte rows per instruction), the
 // scales of rows 8w .. 8w + 7 (lanes 0..7, repeated) and the rotary chunks of
-// rows 8w .. 8w + 7. Rows past the split's end repeat its last row; tiles past
-// the end repeat the last tile.
+// rows 8w .. 8w + 7. Rows past the split's end repeat its last row (their
+// scores repeat a valid score, so the maxima are unchanged, and the softmax
+// zeroes their probabilities); a tile past the end has an empty buffer and
+// reads nothing.
 template <class C>
 struct F8Tile {
-  const DecodeParams& p;
-  int64_t row0;         // the tile's first cache row
-  int last;
-  __device__ __forceinline__ F8Tile(const DecodeParams& p_, int64_t seq_row, int t, int ntiles, int start, int end)
-      : p(p_) {
-    const int tb = start + min(t, ntiles - 1) * C::T;
-    last = min(end - tb, C::T) - 1;
-    row0 = seq_row + tb;
+  __amdgpu_buffer_rsrc_t codes_res, scale_res, rope_res;
+  int rs, rs2, last;
+  __device__ __forceinline__ F8Tile(const DecodeParams& p, int64_t seq_row, int t, int start, int end) {
+    // uniform by construction; stated, so that the resources stay scalar
+    // (a resource the compiler takes for divergent costs a loop per load)
+    const int tb = __builtin_amdgcn_readfirstlane(start + t * C::T);
+    const int nv = __builtin_amdgcn_readfirstlane(max(0, min(end - tb, C::T)));   // rows inside the split
+    last = max(nv - 1, 0);
+    const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane((int)seq_row) +
+                         ((int64_t)__builtin_amdgcn_readfirstlane((int)(seq_row >> 32)) << 32) + tb;
+    rs = (int)p.row_stride;
+    rs2 = (int)(p.rope_stride * 2);
+    codes_res = buffer_rsrc((const char*)p.latent + row0 * p.row_stride, (uint32_t)(nv * rs));
+    scale_res = buffer_rsrc(p.scale + row0, (uint32_t)(nv * 4));
+    rope_res = buffer_rsrc((const char*)p.rope + row0 * (p.rope_stride * 2), (uint32_t)(nv * rs2));
   }
-  __device__ __forceinline__ void codes(MLA_LDS char* slot, int wave, int k) const {
-    int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));
-    const int r0 = 8 * wave + 2 * k, rs = (int)p.row_stride;
-    const int step = r0 + 1 <= last ? rs : 0;
-    const auto res = buffer_rsrc((const char*)p.latent + row0 * p.row_stride, (uint32_t)(C::T * rs));
-    const int chunk = (lane & 31) ^ key8(r0 + (lane >> 5));   // the destination row's key
-    buf_load16_to_lds(res, (uint32_t)((lane >> 5) * step + 16 * chunk), (uint32_t)(min(r0, last) * rs),
-                      slot + r0 * C::DC);
+  // lane (h, c) fills LDS row r = 8w + 2k + h, chunk c, with code chunk
+  // c ^ key8(r) = (c ^ 2h) ^ K, K = 8 (w & 1) | 4 (k & 1) | k / 2, of cache
+  // row min(r, last); lo16 = 16 (c ^ 2h) and h come from the caller
+  __device__ __forceinline__ void codes(MLA_LDS char* slot, int wave, int k, int lo16, int h) const {
+    const int K = 8 * (wave & 1) | 4 * (k & 1) | (k >> 1);
+    const int r0 = 8 * wave + 2 * k;
+    const uint32_t row = (uint32_t)min(r0 + h, last);
+    buf_load16_to_lds(codes_res, __umul24(row, (uint32_t)rs) + (uint32_t)(lo16 ^ (16 * K)), 0u, slot + r0 * C::DC);
   }
-  __device__ __forceinline__ void scales(MLA_LDS char* slot, int wave) const {
-    const int row = min(8 * wave + (int)(threadIdx.x & 7), last);
-    const auto res = buffer_rsrc(p.scale + row0, (uint32_t)(C::T * 4));
-    buf_load4_to_lds(res, (uint32_t)(4 * row), 0u, slot + F8Ring<C>::SCL + wave * 256);
+  // row8 = 8w + lane % 8
+  __device__ __forceinline__ void scales(MLA_LDS char* slot, int wave, int row8) const {
+    buf_load4_to_lds(scale_res, (uint32_t)(4 * min(row8, last)), 0u, slot + F8Ring<C>::SCL + wave * 256);
   }
-  __device__ __forceinline__ void rope(const DmaOffs& dma, MLA_LDS char* slot, int wave) const {
-    const int row = min((int)(threadIdx.x >> 3), last);
-    const int rs2 = (int)(p.rope_stride * 2);
-    const auto res = buffer_rsrc((const char*)p.rope + row0 * (p.rope_stride * 2), (uint32_t)(C::T * rs2));
-    buf_load16_to_lds(res, (uint32_t)(row * rs2 + (dma.rope_chunk - C::DC * C::ESZ)), 0u,
+  // row = tid / 8, chunk = this thread's swizzled rotary chunk (bytes)
+  __device__ __forceinline__ void rope(MLA_LDS char* slot, int wave, int row, int chunk) const {
+    buf_load16_to_lds(rope_res, __umul24((uint32_t)min(row, last), (uint32_t)rs2) + (uint32_t)chunk, 0u,
                       slot + F8Ring<C>::ROPE + wave * 64 * 16);
   }
-  __device__ __forceinline__ void all(const DmaOffs& dma, MLA_LDS char* slot, int wave) const {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) codes(slot, wave, k);
-    scales(slot, wave);
-    rope(dma, slot, wave);
-  }
 };
+
+// Per-lane load offsets of the e4m3 tiles (constant over the loop).
+struct F8LoadOffs {
+  int lo16;    // 16 ((lane % 32) ^ 2 (lane / 32))
+  int h;       // lane / 32
+  int row8;    // 8 wave + lane % 8
+  int rrow;    // tid / 8
+  int rchunk;  // this thread's swizzled rotary chunk (bytes)
+};
+
+template <class C>
+__device__ __forceinline__ F8LoadOffs f8_load_offsets(const DmaOffs& dma) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  F8LoadOffs o;
+  o.lo16 = 16 * ((lane & 31) ^ (2 * h));
+  o.h = h;
+  o.row8 = 8 * wave + (lane & 7);
+  o.rrow = tid >> 3;
+  o.rchunk = dma.rope_chunk - C::DC * C::ESZ;
+  return o;
+}
 
 // Per-lane LDS offsets of the e4m3 loop (the LaneOffs fields, reused):
 //  lat:   score operand of latent block b (64 codes), half x: (lat ^ 64 b) ^ 16 x
@@ -1285,19 +1305,20 @@ __device__ __forceinline__ void tile_step_f8(const DecodeParams& p, const MLA_LD
                                              const MLA_LDS char* __restrict__ prev, MLA_LDS char* __restrict__ fill,
                                              MLA_LDS char* __restrict__ pw, const MLA_LDS char* __restrict__ pr,
                                              const QF8<C>& q, const MLA_LDS char* __restrict__ qrope, State<C>& s,
-                                             LaneOffs<C>& lo, DmaOffs& dma, int64_t seq_row, int t, int ntiles,
-                                             int start, int end, bool first) {
+                                             LaneOffs<C>& lo, F8LoadOffs& lof, int64_t seq_row, int t, int start,
+                                             int end, bool first) {
   using R = F8Ring<C>;
   constexpr int NB = C::DC / 64;
   static_assert(NB == 8 && C::NKC_ROPE == 4 && R::LPT == 6, "eight latent blocks, six loads");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  asm volatile("" : "+v"(lo.lat), "+v"(lo.rope), "+v"(lo.pv[0]), "+v"(lo.p), "+v"(dma.rope_chunk));
+  asm volatile("" : "+v"(lo.lat), "+v"(lo.rope), "+v"(lo.pv[0]), "+v"(lo.p));
+  asm volatile("" : "+v"(lof.lo16), "+v"(lof.h), "+v"(lof.row8), "+v"(lof.rrow), "+v"(lof.rchunk));
   // slot addresses as plain scalars: folded back into the ring arithmetic,
   // they leave offsets that the LDS instructions' immediate field cannot hold
   cur = opaque_lds(cur);
   prev = opaque_lds(prev);
   pr = opaque_lds(pr);
-  const F8Tile<C> ld(p, seq_row, t + R::AHEAD, ntiles, start, end);
+  const F8Tile<C> ld(p, seq_row, t + R::AHEAD, start, end);
   Scores<C> sc;
   sc.lat = f32x16{};
   bf16x8 va[2][C::NFJ], pb[2];
@@ -1334,9 +1355,9 @@ __device__ __forceinline__ void tile_step_f8(const DecodeParams& p, const MLA_LD
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     if (b + 1 < NB) a[(b + 1) & 1] = code_operand(cur, lo.lat, b + 1);
-    if (b < 4) ld.codes(fill, wave, b);
-    else if (b == 4) ld.scales(fill, wave);
-    else if (b == 5) ld.rope(dma, fill, wave);
+    if (b < 4) ld.codes(fill, wave, b, lof.lo16, lof.h);
+    else if (b == 4) ld.scales(fill, wave, lof.row8);
+    else if (b == 5) ld.rope(fill, wave, lof.rrow, lof.rchunk);
     if (b >= 5 && b < 7) {
       pvs.read_va(0, 2 * (b - 5));
       pvs.read_va(0, 2 * (b - 5) + 1);
@@ -1619,8 +1640,15 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       // occupies, so (first pass) it is requested once every wave has read
       // the query, and the query is split while it loads
       const int wv = __builtin_amdgcn_readfirstlane(wave);
-      auto issue8 = [&](int x) { F8Tile<C>(p, sv.seq_row, x, ntiles, start, end).all(dma, slot(x), wv); };
-      static_assert(R8::AHEAD == 3, "tiles 0, 1 and 2 in the prologue");
+      F8LoadOffs lof = f8_load_offsets<C>(dma);
+      auto issue8 = [&](int x) {
+        const F8Tile<C> ld(p, sv.seq_row, x, start, end);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ld.codes(slot(x), wv, k, lof.lo16, lof.h);
+        ld.scales(slot(x), wv, lof.row8);
+        ld.rope(slot(x), wv, lof.rrow, lof.rchunk);
+      };
+      static_assert(R8::AHEAD == 2 || R8::AHEAD == 3, "tiles 0 .. AHEAD - 1 in the prologue");
       issue8(0);
       issue8(1);
       if (pass == 0) {
@@ -1631,11 +1659,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
         wait_vmem_le<0>();                        // tiles 0, 1 and query half 1
         stage_q_read_f8<C>(raw, 1, qreg);
         tile_barrier();                           // every wave is done with the staged query
-        issue8(2);
+        if constexpr (R8::AHEAD == 3) issue8(2);
         split_query_f8<C>(q8, raw, p.scale_log2, lds + R8::QROPE + wv * R8::QROPE_BYTES);
       } else {
-        issue8(2);
-        wait_vmem_le<2 * R8::LPT>();              // tile 0
+        if constexpr (R8::AHEAD == 3) issue8(2);
+        wait_vmem_le<(R8::AHEAD - 1) * R8::LPT>();   // tile 0
       }
       static_assert(C::P_BYTES == C::THREADS * 32, "two 16-byte zero stores per thread");
       *(MLA_LDS u32x4*)(pslot(1) + threadIdx.x * 32) = u32x4{};
@@ -1647,8 +1675,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void decode_kernel(DecodeParams p) {
       for (int t = 0; t < ntiles; ++t) {
         const int tp = max(t - 1, 0), first = pass == 0 && t == 0;
         tile_step_f8<C>(p, slot(t), slot(tp), slot(t + R8::AHEAD), pslot(t), pslot(t - 1), q8,
-                        lds + R8::QROPE + wv * R8::QROPE_BYTES + 16 * lane, s, lo, dma, sv.seq_row, t, ntiles,
-                        start, end, first != 0);
+                        lds + R8::QROPE + wv * R8::QROPE_BYTES + 16 * lane, s, lo, lof, sv.seq_row, t, start,
+                        end, first != 0);
       }
       finish_pass();
     } else if constexpr (STREAM) {
