@@ -106,11 +106,11 @@ typedef struct {
  * dtype MLA_FP8_E4M3: `latent` holds rows of d_latent e4m3 codes (`row_stride`
  *   bytes apart); `rope` holds bf16 rows of d_rope elements (`rope_stride`
  *   elements apart); `scale` holds one fp32 per row; c_KV = code * scale.
- *   Scales are zero or normal fp32 numbers (a subnormal scale is read as
- *   zero's power of two). The contiguous decode takes the scale s = 2^e r
- *   apart: codes enter the products as code * 2^e (exact in bf16) and r in
- *   [1, 2) multiplies the score and the probability in fp32, the rotary key
- *   being divided by r (one bf16 rounding) instead.
+ *   Scales are zero or normal fp32 numbers (a subnormal one may flush to
+ *   zero on the way through the products). The decode keeps the codes unscaled in
+ *   its products (the contiguous form scores them as e4m3 against an exact
+ *   two-part e4m3 split of the query) and multiplies each token's latent
+ *   score, and its probability in the latent sum, by the scale in fp32.
  * Only rows of tokens j < seq_lens[b] are read; padding rows and the unused
  * tail of a sequence's last page may hold anything (NaN included).
  * page_size must be a power of two. The decode may load block-table entries
