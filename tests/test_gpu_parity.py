@@ -304,6 +304,33 @@ def test_dsv2_fp8_against_both_oracles(splits):
     _check(out, ref_b, FP8_REL)
 
 
+def test_dsv2_fp8_query_split_extremes():
+    # the contiguous e4m3 loop scores the codes against an e4m3 split of each
+    # head's absorbed query, q = 2^e (hi + 2^-4 lo), with e taken from the
+    # head's largest |q| (latent and rotary parts). Heads scaled across
+    # 2^-30 .. 2^3, an all-zero head, a head whose rotary part outweighs its
+    # latent part by 2^20, one whose elements spread over 13 binades; tokens
+    # with zero scale and scales spread over 2^-6 .. 2^6
+    inp = make_inputs("fp8_b128_l8192", seq_lens=[700, 300, 64])
+    B, H = inp.batch, inp.dims.num_heads
+    g = torch.Generator().manual_seed(11)
+    fac = 2.0 ** torch.randint(-30, 4, (B, H), generator=g).float()
+    qn = inp.q_nope.float() * fac[..., None]
+    qr = inp.q_rope.float() * fac[..., None]
+    qn[0, 5] = 0.0
+    qr[0, 5] = 0.0
+    qn[1, 7] *= 2.0 ** -20
+    qn[2, 9] *= 2.0 ** torch.randint(-12, 1, (qn.shape[-1],), generator=g).float()
+    inp.q_nope, inp.q_rope = qn.to(torch.bfloat16), qr.to(torch.bfloat16)
+    s = inp.scale.clone() * 2.0 ** torch.randint(-6, 7, inp.scale.shape, generator=g).float()
+    s[torch.randperm(s.numel(), generator=g)[: s.numel() // 50]] = 0.0
+    inp.scale = s
+    _, out, lse = _run(inp, num_splits=2)
+    ref, ref_lse = oracle.decode(**oracle_args(inp, "dequantised"))
+    _check(out, ref, BF16_REL, BF16_ABS * float(np.abs(ref).max()))
+    _lse_check(lse, ref_lse, 2e-2)
+
+
 def test_dsv2_fp8_ragged_nan_padding():
     # rows no sequence owns hold NaN codes and scales; tiles past a split's
     # end repeat its last row, so none of them reaches the result
