@@ -460,9 +460,11 @@ __device__ __forceinline__ bf16x8 qk_operand(const MLA_LDS char* buf, const Lane
 __device__ __forceinline__ void mfma_vgpr_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm("s_nop 5\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-// The same product starting from zero (no accumulator input).
+// The same product starting from zero (no accumulator input); the result
+// registers must not overlap the operands, which the product reads over
+// several passes.
 __device__ __forceinline__ void mfma_vgpr_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 5\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  asm("s_nop 5\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 // More wait states than the longest MFMA needs before VALU reads its result.
 __device__ __forceinline__ void vgpr_acc_drain(f32x16& acc) {
