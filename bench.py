@@ -184,17 +184,23 @@ def _graph_time(stream, call, reps, per_graph):
     return e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
 
 
-def query_proj_time(inp, stream, reps=10, per_graph=20):
+def query_proj_time(inp, stream, reps=10, per_graph=20, copies=4):
     """mla_query_proj (c_Q = RMSNorm(W_DQ h), q^C = W_UQ c_Q, q^R with YaRN
-    rotation) for the workload's batch, hidden 5120, d'_c 1536, bf16. Not
-    part of the decode step (its output feeds the absorb); reported beside it."""
+    rotation) for the workload's batch, hidden 5120, d'_c 1536, bf16: HIP
+    events on its stream around replays of a graph of calls that rotate over
+    `copies` copies of the three weights (91 MB a copy, together beyond the
+    256 MB Infinity Cache). Not part of the decode step (its output feeds the
+    absorb); reported beside it."""
     import torch
     import mla_latent_kv_28_amd as mla
     from mla_synth import make_query_inputs
     d, B = inp.dims, inp.batch
     q = make_query_inputs(d, batch=B, seed=3, max_position=163840)
     dev = "cuda:0"
-    h, w_dq, w_uq, w_qr = (t.to(dev) for t in (q.h, q.w_dq, q.w_uq, q.w_qr))
+    h = q.h.to(dev)
+    w = [tuple(t.to(dev) for t in (q.w_dq, q.w_uq, q.w_qr))]
+    for _ in range(copies - 1):
+        w.append(tuple(t.clone() for t in w[0]))
     pos = torch.from_numpy(q.positions).to(dev)
     qn = torch.empty((B, d.num_heads, d.d_nope), dtype=torch.bfloat16, device=dev)
     qr = torch.empty((B, d.num_heads, d.d_rope), dtype=torch.bfloat16, device=dev)
@@ -202,6 +208,7 @@ def query_proj_time(inp, stream, reps=10, per_graph=20):
     rope = mla.Rope(10000.0, 40.0, 1.0, 32.0, 4096)
 
     def call(i):
+        w_dq, w_uq, w_qr = w[i % copies]
         mla.mla_query_proj(d, B, d.hidden, q.d_qlatent, h, w_dq, None, w_uq, w_qr, mla.BF16, q.eps, rope, pos,
                            qn, qr, ws)
 
@@ -209,9 +216,10 @@ def query_proj_time(inp, stream, reps=10, per_graph=20):
     n2 = d.num_heads * (d.d_nope + d.d_rope)
     alg = (q.d_qlatent * d.hidden + n2 * q.d_qlatent) * 2 + B * d.hidden * 2 + B * n2 * 2
     gbps = alg / (us * 1e-6) / 1e9
+    del w
     return {"batch": B, "hidden": d.hidden, "d_qlatent": q.d_qlatent, "us_per_call": round(us, 3),
-            "calls_timed": reps * per_graph, "algorithmic_bytes": alg, "GBps": round(gbps, 1),
-            "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
+            "calls_timed": reps * per_graph, "weight_copies_rotated": copies, "algorithmic_bytes": alg,
+            "GBps": round(gbps, 1), "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4),
             "timing": "HIP events on the launch stream around graph replays of back-to-back calls"}
 
 

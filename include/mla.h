@@ -298,10 +298,12 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
  *   out   [B, hidden] in out_dtype.
  * dtype: MLA_BF16 for the DeepSeek-V2 shape (out MLA_BF16 or MLA_F32; hidden a
  * multiple of 32), MLA_F32 for the tiny shape (out MLA_F32). fp32
- * accumulation, partial sums over 1024-wide K slices added in slice order.
+ * accumulation: within a 2048-wide part of the contraction, four 512-wide
+ * ranges added in order; the parts' partial sums added in part order.
  * workspace: device memory of at least mla_o_proj_workspace() bytes, 16-byte
  * aligned, owned by the caller (the DeepSeek-V2 shape; NULL allowed for the
- * tiny one). batch == 0 is a no-op.
+ * tiny one): the parts' fp32 partial sums and a copy of o in the operand
+ * order of the product. batch == 0 is a no-op.
  */
 int64_t mla_o_proj_workspace(const mla_dims* dims, int32_t batch, int32_t hidden);
 mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const void* o, const void* w_o,
@@ -380,7 +382,9 @@ mla_status mla_cache_append_noalloc(const mla_dims* dims, int32_t batch, int32_t
  * MLA_BF16 with the DeepSeek-V2 head shape only (MLA_ERR_UNSUPPORTED for the
  * tiny one); hidden a multiple of 16 and at most 20480, d_qlatent a multiple
  * of 256 and at most 4096 (MLA_ERR_UNSUPPORTED beyond). Products accumulate
- * in fp32 over slices of 256 of the contraction, added in slice order; the
+ * in fp32: W_DQ h over 1024-wide parts of the contraction (four 256-wide
+ * ranges added in order within a part, the parts' sums added in part order),
+ * the up-projection over four equal ranges of d_qlatent added in order; the
  * norm runs in fp32 and c_Q is rounded to bf16 before the up-projection;
  * rotation angles in fp64.
  * workspace: device memory of at least mla_query_proj_workspace() bytes,
@@ -417,9 +421,10 @@ int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tok
  * executing and `stop_event` when it ends (hipExtLaunchKernel's event pair),
  * so hipEventElapsedTime on the two gives that kernel's own duration, without
  * the gaps that events recorded separately on the stream add. Each entry
- * point launches one kernel, except mla_cache_append and mla_o_proj, which
- * launch two, and mla_query_proj, which launches four: the start event goes
- * with the first and the stop event with the last, so the pair brackets all. The events are hipEvent_t handles created by
+ * point launches one kernel, except mla_cache_append and mla_prefill, which
+ * launch two, and mla_query_proj and mla_o_proj (bf16), which launch three:
+ * the start event goes with the first and the stop event with the last, so
+ * the pair brackets all. The events are hipEvent_t handles created by
  * the caller with timing enabled; either may be NULL. The pair is consumed
  * by that one launch; a call that fails validation launches nothing and
  * leaves it pending. Always returns MLA_OK.

@@ -484,7 +484,7 @@ mla_status mla_query_proj(const mla_dims* dims, int32_t batch, int32_t hidden, i
   if (sh != Shape::kDsv2) return MLA_ERR_UNSUPPORTED;     // the DeepSeek-V2 head shape, bf16
   if (dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (hidden % 16 != 0 || d_qlatent % 256 != 0) return MLA_ERR_SHAPE;
-  if (d_qlatent > 4096 || mla::query_partial_sums(hidden) > 16) return MLA_ERR_UNSUPPORTED;
+  if (d_qlatent > 4096 || mla::query_partial_sums(hidden) > 20) return MLA_ERR_UNSUPPORTED;
   mla::QueryParams p{};
   {
     const mla_status rs = rope_frequencies(rope, dims->d_rope, p.freq);

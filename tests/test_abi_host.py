@@ -275,7 +275,8 @@ def test_cache_append_noalloc_argument_errors(L):
 def test_o_proj_argument_errors(L):
     d = ctypes.byref(DSV2)
     ws = mla.mla_o_proj_workspace(DSV2, 2, 5120)
-    assert ws == 16 * 2 * 5120 * 4                   # 1024-wide K slices
+    # fp32 partial sums of 2048-wide contraction parts, then o in operand order (rows padded to 32)
+    assert ws == 8 * 2 * 5120 * 4 + 32 * 16384 * 2
     assert mla.mla_o_proj_workspace(TINY, 2, 128) == 0
 
     def f(dims=d, batch=2, hidden=5120, o=P, w=P, dtype=mla.BF16, out=P, out_dtype=mla.BF16, work=P, nbytes=ws):
@@ -296,9 +297,9 @@ def test_o_proj_argument_errors(L):
 def test_query_proj_argument_errors(L):
     d = ctypes.byref(DSV2)
     ws = mla.mla_query_proj_workspace(DSV2, 4, 5120, 1536)
-    # partial sums of W_DQ h (20 slices of 256, added five to a workgroup: 4), plus c_Q in bf16
+    # partial sums of W_DQ h (1024-wide contraction parts: 5), plus c_Q in bf16
     # with its rows padded to 32
-    assert ws == 4 * 4 * 1536 * 4 + 32 * 1536 * 2
+    assert ws == 5 * 4 * 1536 * 4 + 32 * 1536 * 2
     assert mla.mla_query_proj_workspace(TINY, 4, 128, 256) == 0
     yarn = mla.Rope(1e4, 40.0, 1.0, 32.0, 4096)
 
