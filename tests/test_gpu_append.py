@@ -185,3 +185,61 @@ def test_append_then_decode_reads_the_new_token():
     rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     print("append then decode: rel_l2 %.3e" % rel, flush=True)
     assert np.all(np.isfinite(got)) and rel <= 1e-2
+
+
+def _integer_latents(rng, n, target, lim=15):
+    """n integers in [-lim, lim] whose squares sum to exactly `target`."""
+    x = rng.integers(-lim, lim + 1, size=n)
+    for _ in range(200000):
+        diff = target - int(np.sum(x * x))
+        if diff == 0:
+            return x
+        i = int(rng.integers(n))
+        a = abs(int(x[i]))
+        step = 1 if diff > 0 else -1
+        b = a + step
+        if 0 <= b <= lim and abs((b * b - a * a)) <= abs(diff):
+            x[i] = b if x[i] >= 0 else -b
+    raise AssertionError("no integer vector with that sum of squares")
+
+
+def test_dsv2_e4m3_codes_bit_exact_on_exact_latents():
+    # Inputs whose fp32 latent equals the oracle's float64 one: each hidden
+    # state is one-hot, so W_DKV h is one weight column exactly; that column
+    # holds integers whose squares sum to 512 * 64 and the norm's epsilon is
+    # 0, so the RMS is 8 and the normed latent x / 8 is exact. Every
+    # latent / scale is checked to lie well away from a rounding midpoint of
+    # e4m3 (the kernel divides in fp32, the oracle in float64), so the codes
+    # must agree bit for bit and the scales to fp32 rounding.
+    import dataclasses
+    rng = np.random.default_rng(11)
+    B = 8
+    base = make_append_inputs(DSV2, batch=B, seed=12, max_position=100)
+    hid = DSV2.hidden
+    cols = rng.choice(hid, size=B, replace=False)
+    h = torch.zeros((B, hid), dtype=torch.bfloat16)
+    w = base.w_dkv.clone()
+    pos_values = oracle.decode_e4m3(np.arange(0x7F, dtype=np.uint8))   # non-negative finite codes
+    mids = (pos_values[1:] + pos_values[:-1]) / 2
+    for b in range(B):
+        while True:
+            x = _integer_latents(rng, DSV2.d_latent, DSV2.d_latent * 64)
+            y = x / 8.0
+            v = np.abs(y) / (np.abs(y).max() / 448.0)
+            gap = np.min(np.abs(v[:, None] - mids[None, :]), axis=1)
+            if np.all(gap > 1e-4 * np.maximum(v, 1e-3)):
+                break
+        h[b, cols[b]] = 1.0
+        w[:, cols[b]] = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    inp = dataclasses.replace(base, h=h, w_dkv=w, eps=0.0)
+    (codes, scale, rope), idx = _run(inp, "fp8", layout="contiguous")
+    c_ref, _ = _reference(inp)
+    assert np.array_equal(c_ref, np.stack([w[:, cols[b]].double().numpy() / 8.0 for b in range(B)]))
+    ref_codes, ref_scale = oracle.quantise_entry(c_ref)
+    codes, scale = codes.numpy(), scale.double().numpy()
+    for b, r in enumerate(idx):
+        assert np.array_equal(codes[r], ref_codes[b]), (b, int(np.sum(codes[r] != ref_codes[b])))
+        assert abs(scale[r] - ref_scale[b]) <= 2.0 ** -23 * ref_scale[b]
+    distinct = len(np.unique(np.concatenate([ref_codes[b] for b in range(B)])))
+    print("codes compared: %d rows, %d distinct codes" % (B, distinct), flush=True)
+    assert distinct >= 20
