@@ -302,8 +302,7 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t num
  * ranges added in order; the parts' partial sums added in part order.
  * workspace: device memory of at least mla_o_proj_workspace() bytes, 16-byte
  * aligned, owned by the caller (the DeepSeek-V2 shape; NULL allowed for the
- * tiny one): the parts' fp32 partial sums and a copy of o in the operand
- * order of the product. batch == 0 is a no-op.
+ * tiny one): the parts' fp32 partial sums. batch == 0 is a no-op.
  */
 int64_t mla_o_proj_workspace(const mla_dims* dims, int32_t batch, int32_t hidden);
 mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const void* o, const void* w_o,
@@ -421,8 +420,8 @@ int32_t mla_suggest_splits(int32_t batch, int32_t max_seq_len, int64_t total_tok
  * executing and `stop_event` when it ends (hipExtLaunchKernel's event pair),
  * so hipEventElapsedTime on the two gives that kernel's own duration, without
  * the gaps that events recorded separately on the stream add. Each entry
- * point launches one kernel, except mla_cache_append and mla_prefill, which
- * launch two, and mla_query_proj and mla_o_proj (bf16), which launch three:
+ * point launches one kernel, except mla_cache_append, mla_prefill and
+ * mla_o_proj (bf16), which launch two, and mla_query_proj, which launches three:
  * the start event goes with the first and the stop event with the last, so
  * the pair brackets all. The events are hipEvent_t handles created by
  * the caller with timing enabled; either may be NULL. The pair is consumed

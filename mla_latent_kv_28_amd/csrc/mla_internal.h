@@ -142,7 +142,7 @@ struct OProjParams {
   const void* o;      // [B, k] (the heads' outputs, concatenated)
   const void* w;      // [n, k]
   void* out;          // [B, n]
-  float* work;        // bf16: fp32 partial sums [parts, B, n], then o fragment-major
+  float* work;        // bf16: fp32 partial sums [parts, B, n]
   int32_t batch, n, k;
 };
 bool oproj_bf16_shape_ok(int n, int k);

@@ -7,15 +7,14 @@
 // library keeps the two products (mla_out_proj / mla_combine_out_proj, then
 // this one).
 //
-// bf16, three kernels:
-//  1. to_frag_major: o copied into the operand order of the product (1 MB at
-//     batch 32; one 1 KiB load per operand fragment afterwards);
-//  2. skinny_gemm (skinny.h): one workgroup of four waves per (32 output
+// bf16, two kernels:
+//  1. skinny_gemm (skinny.h): one workgroup of four waves per (32 output
 //     features, 2048-wide contraction part), 160 x 8 = 1280 at d = 5120 and
 //     H d_v = 16384; each wave streams its 512-wide range of 32 weight rows
-//     in 128-byte row pieces and stores nothing but the part's fp32 tile,
-//     the four waves' tiles added in order, into the caller's workspace;
-//  3. oproj_reduce: adds the parts in order (deterministic) and rounds.
+//     and of the 32 rows of o in 128-byte row pieces, puts both into operand
+//     order through its LDS buffer, and the four waves' tiles, added in
+//     order, go to the caller's workspace as the part's fp32 partial sums;
+//  2. oproj_reduce: adds the parts in order (deterministic) and rounds.
 // W_O dominates the bytes (168 MB at d = 5120, H d_v = 16384); it is read once
 // per 32 batch rows.
 // fp32 (tiny shape): one thread per output feature, plain fma.
@@ -35,24 +34,29 @@ constexpr int kOpPart = kOpWaves * kOpKw;   // contraction features per workgrou
 
 __host__ __device__ int oproj_parts(int k) { return (k + kOpPart - 1) / kOpPart; }
 
-// out[b][n] = the slices' partial sums added in slice order.
+// out[b][n] = the parts' partial sums added in part order; four outputs a
+// thread (n is a multiple of 32), every part's load issued before the sum.
+constexpr int kOpMaxParts = 16;
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void oproj_reduce(OProjParams p) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t e = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
   if (e >= (int64_t)p.batch * p.n) return;
-  const int slices = oproj_parts(p.k);
+  const int parts = oproj_parts(p.k);
   const int64_t stride = (int64_t)p.batch * p.n;
-  float v[16];
+  f32x4 v[kOpMaxParts];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) v[s] = s < slices ? p.work[s * stride + e] : 0.0f;   // loads together
-  float sum = 0.0f;
+  for (int s = 0; s < kOpMaxParts; ++s)
+    if (s < parts) v[s] = *(const f32x4*)(p.work + s * stride + e);
+  f32x4 sum = v[0];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) sum += v[s];
-  for (int s = 16; s < slices; ++s) sum += p.work[s * stride + e];
-  if constexpr (OUT_F32)
-    ((float*)p.out)[e] = sum;
-  else
-    ((__bf16*)p.out)[e] = (__bf16)sum;
+  for (int s = 1; s < kOpMaxParts; ++s)
+    if (s < parts) sum += v[s];
+  for (int s = kOpMaxParts; s < parts; ++s) sum += *(const f32x4*)(p.work + s * stride + e);
+  if constexpr (OUT_F32) {
+    *(f32x4*)((float*)p.out + e) = sum;
+  } else {
+    *(u32x2*)((__bf16*)p.out + e) = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+  }
 }
 
 __global__ __launch_bounds__(128) void oproj_f32(OProjParams p) {
@@ -70,14 +74,8 @@ __global__ __launch_bounds__(128) void oproj_f32(OProjParams p) {
 // bf16: n a multiple of 32, k a multiple of kOpSlice.
 bool oproj_bf16_shape_ok(int n, int k) { return n % 32 == 0 && k % 1024 == 0; }
 
-// Workspace: the parts' fp32 partial sums, then o in the fragment-major
-// layout (rows padded to 32).
-static int64_t oproj_frag_offset(int batch, int n, int k) {
-  return ((int64_t)oproj_parts(k) * batch * n * 4 + 255) / 256 * 256;
-}
-int64_t oproj_workspace_bytes(int batch, int n, int k) {
-  return oproj_frag_offset(batch, n, k) + (int64_t)(batch + 31) / 32 * 32 * k * 2;
-}
+// Workspace: the parts' fp32 partial sums.
+int64_t oproj_workspace_bytes(int batch, int n, int k) { return (int64_t)oproj_parts(k) * batch * n * 4; }
 
 hipError_t launch_oproj(const OProjParams& p, bool bf16, bool out_f32, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
@@ -85,21 +83,17 @@ hipError_t launch_oproj(const OProjParams& p, bool bf16, bool out_f32, hipStream
   hipEvent_t e0 = nullptr, e1 = nullptr;
   take_launch_events(&e0, &e1);      // a pending event pair brackets both kernels
   const int parts = oproj_parts(p.k);
-  __bf16* ofrag = (__bf16*)((char*)p.work + oproj_frag_offset(p.batch, p.n, p.k));
-  const int64_t pieces = (int64_t)(p.batch + 31) / 32 * 32 * p.k / 8;
-  hipError_t e = launch_kernel_events(to_frag_major, dim3((unsigned)((pieces + 255) / 256)), dim3(256), stream, e0,
-                                      nullptr, (const __bf16*)p.o, ofrag, p.batch, p.k);
-  if (e != hipSuccess) return e;
-  const SkParams g{ofrag, p.w, p.w, 0, p.n, p.batch, p.n, p.k, kOpKw, parts};
+  const SkParams g{p.o, p.w, p.w, p.k, p.n, p.batch, p.n, p.k, kOpKw, parts};
   const EpiPartial ep{p.work, p.batch, p.n};
   const dim3 grid0(p.n / (16 * kOpNa) * parts, (p.batch + 31) / 32), block0(64 * kOpWaves);
-  e = parts * kOpPart != p.k
-          ? launch_kernel_events(skinny_gemm<kOpWaves, kOpDepth, kOpNa, true, true, EpiPartial>, grid0, block0, stream,
-                                 nullptr, nullptr, g, ep)
-          : launch_kernel_events(skinny_gemm<kOpWaves, kOpDepth, kOpNa, true, false, EpiPartial>, grid0, block0, stream,
-                                 nullptr, nullptr, g, ep);
+  hipError_t e =
+      parts * kOpPart != p.k
+          ? launch_kernel_events(skinny_gemm<kOpWaves, kOpDepth, kOpNa, kXRowLds, true, EpiPartial>, grid0, block0, stream,
+                                 e0, nullptr, g, ep)
+          : launch_kernel_events(skinny_gemm<kOpWaves, kOpDepth, kOpNa, kXRowLds, false, EpiPartial>, grid0, block0, stream,
+                                 e0, nullptr, g, ep);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)(((int64_t)p.batch * p.n + 255) / 256));
+  const dim3 grid((unsigned)(((int64_t)p.batch * p.n / 4 + 255) / 256));
   if (out_f32) return launch_kernel_events(oproj_reduce<true>, grid, dim3(256), stream, nullptr, e1, p);
   return launch_kernel_events(oproj_reduce<false>, grid, dim3(256), stream, nullptr, e1, p);
 }

@@ -68,65 +68,41 @@ constexpr int kQWaves = 4, kQNa = 2;      // waves per workgroup, 16-row weight 
 constexpr int kQ1Depth = 4, kQ2Depth = 3; // macro steps in flight per wave (W_DQ; [W_UQ; W_QR])
 constexpr int kQ1Kw = 256;                // W_DQ: contraction features per wave
 
-__device__ __forceinline__ float block_sum256(float v, float* red) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
+constexpr int kMaxParts = 20;   // partial sums of W_DQ h (hidden up to 20 x 1024)
 
-constexpr int kMaxDqPerThread = 16;   // d'_c up to 16 x 256
-constexpr int kFastParts = 8;         // hidden up to 8 x 1024: every load issued before any sum
-
-// c_Q[b] = RMSNorm(sum of the partial sums) in bf16; one 256-thread
-// workgroup per sequence, thread t owns features t, t + 256, ...; the
-// partial sums of a feature are added in order. c_Q is stored
+// c_Q[b] = RMSNorm(sum of the partial sums) in bf16; one workgroup of d'_c / 4
+// threads per sequence, thread t owns features 4t .. 4t + 3 and adds their
+// partial sums in order (all loads issued first). c_Q is stored
 // fragment-major (frag_offset), the operand layout of the up-projection.
-__global__ __launch_bounds__(256) void latent_norm(QueryParams p) {
-  __shared__ float red[4];
-  const int b = blockIdx.x, t = threadIdx.x;
-  const int per = p.dq / 256;
+__global__ __launch_bounds__(1024) void latent_norm(QueryParams p) {
+  __shared__ float red[16];
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6, waves = blockDim.x >> 6;
   const int64_t part = (int64_t)p.batch * p.dq;
-  const float* src = p.part1 + (int64_t)b * p.dq;
-  float x[kMaxDqPerThread];
-  float ss = 0.0f;
-  if (p.s1 <= kFastParts) {
-    float v[kMaxDqPerThread][kFastParts];
+  const float* src = p.part1 + (int64_t)b * p.dq + 4 * t;
+  f32x4 v[kMaxParts];
 #pragma unroll
-    for (int j = 0; j < kMaxDqPerThread; ++j)
+  for (int s = 0; s < kMaxParts; ++s)
+    if (s < p.s1) v[s] = *(const f32x4*)(src + s * part);
+  f32x4 x = v[0];
 #pragma unroll
-      for (int s = 0; s < kFastParts; ++s) v[j][s] = (j < per && s < p.s1) ? src[s * part + t + 256 * j] : 0.0f;
+  for (int s = 1; s < kMaxParts; ++s)
+    if (s < p.s1) x += v[s];   // in order
+  float ss = (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
 #pragma unroll
-    for (int j = 0; j < kMaxDqPerThread; ++j) {
-      float a = 0.0f;
+  for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+  for (int w = 0; w < waves; ++w) tot += red[w];   // in wave order
+  const float inv = 1.0f / sqrtf(tot / p.dq + p.eps);
+  float g[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  if (p.gain != nullptr) {
+    const u32x2 gw = *(const u32x2*)((const __bf16*)p.gain + 4 * t);
 #pragma unroll
-      for (int s = 0; s < kFastParts; ++s)
-        if (s < p.s1) a += v[j][s];   // in order
-      x[j] = a;
-      if (j < per) ss += a * a;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kMaxDqPerThread; ++j) {
-      float a = 0.0f;
-      if (j < per)
-        for (int s = 0; s < p.s1; ++s) a += src[s * part + t + 256 * j];   // in order
-      x[j] = a;
-      if (j < per) ss += a * a;
-    }
+    for (int e = 0; e < 4; ++e) g[e] = bf16_bits_to_f32((gw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
   }
-  const float inv = 1.0f / sqrtf(block_sum256(ss, red) / p.dq + p.eps);
-  __bf16* dst = (__bf16*)p.cq;
-#pragma unroll
-  for (int j = 0; j < kMaxDqPerThread; ++j) {
-    if (j < per) {
-      const int c = t + 256 * j;
-      const float g = p.gain != nullptr ? (float)((const __bf16*)p.gain)[c] : 1.0f;
-      dst[frag_offset(b, c, p.dq)] = (__bf16)(x[j] * inv * g);
-    }
-  }
+  *(u32x2*)((__bf16*)p.cq + frag_offset(b, 4 * t, p.dq)) =
+      u32x2{pack_bf16x2(x[0] * inv * g[0], x[1] * inv * g[1]), pack_bf16x2(x[2] * inv * g[2], x[3] * inv * g[3])};
 }
 
 }  // namespace
@@ -155,13 +131,13 @@ hipError_t launch_query_proj(const QueryParams& p, hipStream_t stream) {
   const EpiPartial ep1{p.part1, p.batch, p.dq};
   const bool tail1 = p.s1 * kQWaves * kQ1Kw != p.hidden;
   const dim3 grid1(p.dq / (16 * kQNa) * p.s1, rb);
-  hipError_t e = tail1 ? launch_kernel_events(skinny_gemm<kQWaves, kQ1Depth, kQNa, false, true, EpiPartial>, grid1, block,
+  hipError_t e = tail1 ? launch_kernel_events(skinny_gemm<kQWaves, kQ1Depth, kQNa, kXRowLds, true, EpiPartial>, grid1, block,
                                               stream, e0, nullptr, g1, ep1)
-                       : launch_kernel_events(skinny_gemm<kQWaves, kQ1Depth, kQNa, false, false, EpiPartial>, grid1, block,
+                       : launch_kernel_events(skinny_gemm<kQWaves, kQ1Depth, kQNa, kXRowLds, false, EpiPartial>, grid1, block,
                                               stream, e0, nullptr, g1, ep1);
   if (e != hipSuccess) return e;
   // 2. c_Q = RMSNorm of their sum, blocked by 16 features
-  e = launch_kernel_events(latent_norm, dim3(p.batch), dim3(256), stream, nullptr, nullptr, p);
+  e = launch_kernel_events(latent_norm, dim3(p.batch), dim3(p.dq / 4), stream, nullptr, nullptr, p);
   if (e != hipSuccess) return e;
   // 3. [W_UQ; W_QR] c_Q over the whole d'_c in one workgroup, rotary finish
   const int kw2 = (p.dq / kQWaves + 64 * kQ2Depth - 1) / (64 * kQ2Depth) * (64 * kQ2Depth);
@@ -170,9 +146,9 @@ hipError_t launch_query_proj(const QueryParams& p, hipStream_t stream) {
   for (int i = 0; i < kMaxRopePairs; ++i) ep2.freq[i] = p.freq[i];
   const dim3 grid2(n2 / (16 * kQNa), rb);
   if (kw2 * kQWaves != p.dq)
-    return launch_kernel_events(skinny_gemm<kQWaves, kQ2Depth, kQNa, true, true, EpiQuery>, grid2, block, stream, nullptr,
+    return launch_kernel_events(skinny_gemm<kQWaves, kQ2Depth, kQNa, kXFrag, true, EpiQuery>, grid2, block, stream, nullptr,
                                 e1, g2, ep2);
-  return launch_kernel_events(skinny_gemm<kQWaves, kQ2Depth, kQNa, true, false, EpiQuery>, grid2, block, stream, nullptr, e1,
+  return launch_kernel_events(skinny_gemm<kQWaves, kQ2Depth, kQNa, kXFrag, false, EpiQuery>, grid2, block, stream, nullptr, e1,
                               g2, ep2);
 }
 

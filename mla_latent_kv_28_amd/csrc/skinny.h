@@ -30,8 +30,14 @@
 namespace mla {
 namespace {
 
+// Activation layouts of skinny_gemm: row-major read straight into fragments
+// (16 rows x 64 bytes a load), fragment-major (frag_offset; one 1 KiB load a
+// fragment), or row-major read like the weights (8 rows x 128 bytes a load)
+// and put into fragment order through the wave's LDS buffer.
+constexpr int kXRow = 0, kXFrag = 1, kXRowLds = 2;
+
 struct SkParams {
-  const void* x;       // XFRAG: fragment-major (frag_offset); else row-major [M][ldx]
+  const void* x;       // kXFrag: fragment-major (frag_offset); else row-major [M][ldx]
   const void* w0;      // weight rows [0, n0), [n0][K] row-major
   const void* w1;      // weight rows [n0, N)
   int32_t ldx;         // row-major activations: elements per row
@@ -70,14 +76,17 @@ __device__ __forceinline__ int sk_lds_pos(int r, int p) {
 // TAIL: the contraction parts reach past K; the operands of k >= K are zeroed
 // (reads past either operand's buffer return zero, and reads inside it are
 // discarded). NA: 16-row groups of weight rows per workgroup (2 or 4).
-template <int WAVES, int D, int NA, bool XFRAG, bool TAIL, class EPI>
+template <int WAVES, int D, int NA, int XL, bool TAIL, class EPI>
 __global__ __launch_bounds__(64 * WAVES) void skinny_gemm(SkParams g, EPI epi) {
   constexpr int TILES = 2 * NA;        // 16x16 tiles per wave: (weight group, batch half)
   constexpr int WLD = 2 * NA;          // weight loads per macro step (8 rows each)
   static_assert(WAVES >= 4 && TILES % 4 == 0, "the tiles split evenly over four finishing waves");
-  // a wave's weight buffer, then (after its loop) its tiles for the sum
-  __shared__ __attribute__((aligned(16))) char wbuf[WAVES][16 * NA * 128];
-  static_assert(16 * NA * 128 == TILES * 64 * 16, "a wave's tiles fill its weight buffer");
+  // a wave's weight buffer (and, XL == kXRowLds, its activation rows after
+  // the weight rows), then (after its loop) its tiles for the sum
+  constexpr int XROWS = XL == kXRowLds ? 32 : 0;
+  constexpr int WB = (16 * NA + XROWS) * 128;
+  __shared__ __attribute__((aligned(16))) char wbuf[WAVES][WB];
+  static_assert(WB >= TILES * 64 * 16, "a wave's tiles fit its buffer");
   const int lane = threadIdx.x & 63, c = lane & 15, grp = lane >> 4;
   auto red = [&](int w, int a) -> MLA_LDS f32x4& { return ((MLA_LDS f32x4*)wbuf[w])[a * 64 + lane]; };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,11 +99,19 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_gemm(SkParams g, EPI epi) {
   const uint32_t wv = (uint32_t)((lane >> 3) * g.K * 2 + 16 * (lane & 7));
   MLA_LDS char* wl = (MLA_LDS char*)wbuf[wave];
   __amdgpu_buffer_rsrc_t xres;
-  uint32_t xv0, xv1;
-  if constexpr (XFRAG) {
+  uint32_t xv0, xv1, xvr[4];
+  if constexpr (XL == kXFrag) {
     xres = buffer_rsrc(g.x, (uint32_t)((int64_t)(g.M + 31) / 32 * 32 * g.K * 2));
     xv0 = (uint32_t)(rb * (g.K / 32) * 2048 + 16 * lane);
     xv1 = xv0 + 1024;
+  } else if constexpr (XL == kXRowLds) {
+    // like the weights: load i reads row 8 i + lane / 8 of the row block
+    // (clamped to the batch; rows past it are not stored), piece lane % 8
+    xres = buffer_rsrc(g.x, (uint32_t)((int64_t)g.M * g.ldx * 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xvr[i] = (uint32_t)(min(32 * rb + 8 * i + (lane >> 3), g.M - 1) * g.ldx * 2 + 16 * (lane & 7));
+    xv0 = xv1 = 0;
   } else {
     const int r0 = min(32 * rb + c, g.M - 1), r1 = min(32 * rb + 16 + c, g.M - 1);
     xres = buffer_rsrc(g.x, (uint32_t)((int64_t)g.M * g.ldx * 2));
@@ -109,24 +126,42 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_gemm(SkParams g, EPI epi) {
     const int k = kbeg + 64 * m;
 #pragma unroll
     for (int i = 0; i < WLD; ++i) wr[j][i] = load_b128(wres, wv + (uint32_t)(8 * i * g.K * 2), (uint32_t)(2 * k));
+    if constexpr (XL == kXRowLds) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t xs = XFRAG ? (uint32_t)((k / 32 + t) * 2048) : (uint32_t)(2 * (k + 32 * t));
-      xb[j][t][0] = load_b128(xres, xv0, xs);
-      xb[j][t][1] = load_b128(xres, xv1, xs);
+      for (int i = 0; i < 4; ++i) xb[j][i >> 1][i & 1] = load_b128(xres, xvr[i], (uint32_t)(2 * k));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t xs = XL == kXFrag ? (uint32_t)((k / 32 + t) * 2048) : (uint32_t)(2 * (k + 32 * t));
+        xb[j][t][0] = load_b128(xres, xv0, xs);
+        xb[j][t][1] = load_b128(xres, xv1, xs);
+      }
     }
   };
   f32x4 acc[TILES] = {};
   auto mma = [&](int m, int j) {
-    // weights of this macro step through the wave's buffer into fragment order
+    // weights (and activation rows) of this macro step through the wave's
+    // buffer into fragment order
 #pragma unroll
     for (int i = 0; i < WLD; ++i) *(MLA_LDS bf16x8*)(wl + sk_lds_pos(8 * i + (lane >> 3), lane & 7)) = wr[j][i];
+    if constexpr (XL == kXRowLds) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *(MLA_LDS bf16x8*)(wl + sk_lds_pos(16 * NA + 8 * i + (lane >> 3), lane & 7)) = xb[j][i >> 1][i & 1];
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       bf16x8 a[NA];
 #pragma unroll
       for (int na = 0; na < NA; ++na) a[na] = *(const MLA_LDS bf16x8*)(wl + sk_lds_pos(16 * na + c, 4 * t + grp));
-      bf16x8 b0 = xb[j][t][0], b1 = xb[j][t][1];
+      bf16x8 b0, b1;
+      if constexpr (XL == kXRowLds) {
+        b0 = *(const MLA_LDS bf16x8*)(wl + sk_lds_pos(16 * NA + c, 4 * t + grp));
+        b1 = *(const MLA_LDS bf16x8*)(wl + sk_lds_pos(16 * NA + 16 + c, 4 * t + grp));
+      } else {
+        b0 = xb[j][t][0];
+        b1 = xb[j][t][1];
+      }
       if constexpr (TAIL) {
         if (kbeg + 64 * m + 32 * t + 8 * grp >= g.K) {
           b0 = b1 = bf16x8{};
@@ -182,25 +217,6 @@ struct EpiPartial {
     if (b < M) *(f32x4*)(out + ((int64_t)kpart * M + b) * N + n) = v;
   }
 };
-
-// A row-major [M, K] bf16 matrix copied to the fragment-major layout (rows
-// padded to a multiple of 32 with zeros); one thread per 16-byte piece.
-__global__ __launch_bounds__(256) void to_frag_major(const __bf16* __restrict__ src, __bf16* __restrict__ dst, int M,
-                                                     int K) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // destination piece
-  const int64_t pieces = (int64_t)(M + 31) / 32 * 32 * K / 8;
-  if (q >= pieces) return;
-  // piece q = ((rb * K/32 + t) * 2 + bb) * 64 + 16 g + c
-  const int lane = (int)(q & 63);
-  const int64_t blk = q >> 6;
-  const int bb = (int)(blk & 1);
-  const int64_t rt = blk >> 1;
-  const int t = (int)(rt % (K / 32)), rb = (int)(rt / (K / 32));
-  const int b = 32 * rb + 16 * bb + (lane & 15), k = 32 * t + 8 * (lane >> 4);
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (b < M) v = *(const u32x4*)(src + (int64_t)b * K + k);
-  *(u32x4*)(dst + 8 * q) = v;
-}
 
 }  // namespace
 }  // namespace mla
