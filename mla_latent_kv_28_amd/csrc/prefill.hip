@@ -142,6 +142,11 @@ __global__ __launch_bounds__(256, 2) void upproj_kernel(PrefillParams p) {
   }
 }
 
+// POS_SCALE (a positive softmax scale, the usual case): the running maximum is
+// taken over the raw scores and each probability is exp2(fma(s, scale, -m)),
+// one instruction fewer per score than scaling first; otherwise every score is
+// scaled before the maximum.
+template <bool POS_SCALE>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kKTile + kVTile];
   MLA_LDS char* ktile = (MLA_LDS char*)smem;
@@ -247,7 +252,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
     // block that every token of the wave sees whole takes no mask (uniform)
     float x[2][16];
     float mt = -INFINITY;
-    if (wave_full && j0 + kKBlock - 1 <= wave_pos0) {
+    const bool whole = wave_full && j0 + kKBlock - 1 <= wave_pos0;
+    if (POS_SCALE && whole) {
+      // raw scores
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          x[kk][e] = sc[kk][e];
+          mt = fmaxf(mt, x[kk][e]);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;
+    } else if (POS_SCALE) {
+      // raw scores; masked keys become -inf (exp2(fma(-inf, scale, -ref)) = 0)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = j0 + 32 * kk + 8 * (e >> 2) + 4 * hh + (e & 3);
+          x[kk][e] = (valid && key <= pos) ? sc[kk][e] : -INFINITY;
+          mt = fmaxf(mt, x[kk][e]);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * p.scale_log2;
+    } else if (whole) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -255,6 +282,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
           x[kk][e] = sc[kk][e] * p.scale_log2;
           mt = fmaxf(mt, x[kk][e]);
         }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
     } else {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -265,8 +293,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
           x[kk][e] = (valid && key <= pos) ? v : -INFINITY;
           mt = fmaxf(mt, x[kk][e]);
         }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m, mt);
     const float ref = m_new == -INFINITY ? 0.0f : m_new;   // a token with no key yet
     const float alpha = fast_exp2(m - ref);                 // 0 on the first block that has keys
@@ -276,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        x[kk][e] = fast_exp2(x[kk][e] - ref);
+        x[kk][e] = POS_SCALE ? fast_exp2(__builtin_fmaf(x[kk][e], p.scale_log2, -ref)) : fast_exp2(x[kk][e] - ref);
         psum += x[kk][e];
       }
     l = l * alpha + psum;
@@ -340,7 +368,9 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     e0 = nullptr;
   }
   const int nqb = (p.n + kQBlock - 1) / kQBlock;
-  return launch_kernel_events(prefill_attn_kernel, dim3(nqb, p.heads, p.batch), dim3(256), stream, e0, e1, p);
+  if (p.scale_log2 > 0.0f)
+    return launch_kernel_events(prefill_attn_kernel<true>, dim3(nqb, p.heads, p.batch), dim3(256), stream, e0, e1, p);
+  return launch_kernel_events(prefill_attn_kernel<false>, dim3(nqb, p.heads, p.batch), dim3(256), stream, e0, e1, p);
 }
 
 }  // namespace mla

@@ -94,6 +94,21 @@ def test_prefill_against_oracle(case):
     _lse_check(lse, ref_lse)
 
 
+@pytest.mark.parametrize("factor", [-1.0, 0.0])
+def test_prefill_non_positive_scale(factor):
+    # the kernel instance for scales <= 0 (scores scaled before the maximum):
+    # a negated scale reverses the ranking of the keys, zero makes every
+    # visible key weigh the same
+    import dataclasses
+    lens, n = [300, 129], 129
+    inp = make_inputs("dsv2_b32_l4096", seq_lens=lens, pad_fill=float("nan"), tokens_per_seq=n)
+    inp = dataclasses.replace(inp, sm_scale=factor * inp.sm_scale)
+    out, lse = _prefill(inp, n)
+    ref, ref_lse = oracle.prefill(n=n, **oracle_args(inp))
+    _check(out, ref, BF16_REL, BF16_ABS)
+    _lse_check(lse, ref_lse)
+
+
 def test_prefill_matches_the_absorbed_multi_token_path():
     from mla_latent_kv_28_amd.pipeline import DecodePipeline
     lens, n = [700, 129, 1000], 129
