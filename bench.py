@@ -287,6 +287,97 @@ def multi_token_time(pipe, caches, stream, n=2, reps=20):
             "timing": "HIP events on the launch stream around graph replays of decode launches alone"}
 
 
+def layer_time(inp, pipe, caches, stream, copies=2, reps=5):
+    """One whole MLA layer for one new token per sequence, at the workload's
+    batch and the DeepSeek-V2 hidden size 5120: the query path and the cache
+    append of the new token (at position L - 1, the row the decode then reads),
+    the decode step of the benchmark (absorb, decode, merge + W_UV) and W_O.
+    The append depends only on the hidden state, like the query path, so it
+    can also run on a second stream beside it (default priority; forked from
+    and joined back to the launch stream); both forms are timed, the one-stream
+    form is reported as the layer's time. HIP events around replays of graphs of
+    layers rotating `copies` copies of every weight and the step's cache
+    copies."""
+    import math as _m
+    import torch
+    import mla_latent_kv_28_amd as mla
+    from mla_synth import make_append_inputs, make_oproj_inputs, make_query_inputs
+    d, B, dev = inp.dims, pipe.batch, "cuda:0"
+    lens = pipe.seq_lens.to(torch.int32)
+    q = make_query_inputs(d, batch=B, seed=3)
+    a = make_append_inputs(d, batch=B, seed=4)
+    _, w_o = make_oproj_inputs(d, B, seed=2)
+    h = q.h.to(dev)
+    base = dict(w_dq=q.w_dq, w_uq=q.w_uq, w_qr=q.w_qr, w_dkv=a.w_dkv, w_kr=a.w_kr, w_uk=pipe.w_uk.cpu(),
+                w_uv=pipe.w_uv.cpu(), w_o=w_o)
+    W = [{k: v.to(dev).contiguous() for k, v in base.items()} for _ in range(copies)]
+    qn = torch.empty((B, d.num_heads, d.d_nope), dtype=torch.bfloat16, device=dev)
+    qr = torch.empty((B, d.num_heads, d.d_rope), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((B, d.hidden), dtype=torch.bfloat16, device=dev)
+    pos = (lens - 1).contiguous()
+    ws_q = torch.empty(mla.mla_query_proj_workspace(d, B, d.hidden, q.d_qlatent), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(mla.mla_cache_append_workspace(d, B, d.hidden) // 4, dtype=torch.float32, device=dev)
+    ws_o = torch.empty(mla.mla_o_proj_workspace(d, B, d.hidden) // 4, dtype=torch.float32, device=dev)
+    rope = mla.Rope(10000.0, 40.0, 1.0, 32.0, 4096)
+    saved = (pipe.q_nope, pipe.q_rope, pipe.w_uk, pipe.w_uv, pipe.cache)
+    pipe.q_nope, pipe.q_rope = qn, qr
+    nb = len(caches)
+    per_graph = copies * nb // _m.gcd(copies, nb)
+    side = torch.cuda.Stream()
+
+    def layer(i, overlap):
+        w, cache = W[i % copies], caches[i % nb]
+        main = torch.cuda.current_stream()
+
+        def append():
+            mla.mla_cache_append(d, B, d.hidden, h, w["w_dkv"], w["w_kr"], None, mla.BF16, a.eps, rope, pos,
+                                 cache, ws_a)
+        if overlap:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                append()
+        mla.mla_query_proj(d, B, d.hidden, q.d_qlatent, h, w["w_dq"], None, w["w_uq"], w["w_qr"], mla.BF16, q.eps,
+                           rope, pos, qn, qr, ws_q)
+        if overlap:
+            main.wait_stream(side)
+        else:
+            append()
+        pipe.w_uk, pipe.w_uv, pipe.cache = w["w_uk"], w["w_uv"], cache
+        pipe.run()
+        mla.mla_o_proj(d, B, d.hidden, pipe.out, w["w_o"], mla.BF16, u, mla.BF16, ws_o)
+
+    res = {}
+    try:
+        for overlap in (True, False):
+            with torch.cuda.stream(stream):
+                for i in range(per_graph):
+                    layer(i, overlap)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(per_graph):
+                    layer(i, overlap)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            res[overlap] = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+            del g
+    finally:
+        pipe.q_nope, pipe.q_rope, pipe.w_uk, pipe.w_uv, pipe.cache = saved
+    us = res[False]
+    return {"batch": B, "hidden": d.hidden, "us_per_layer": round(us, 3), "queries_per_s": round(B / (us * 1e-6), 1),
+            "us_per_layer_append_on_second_stream": round(res[True], 3), "layers_timed": reps * per_graph,
+            "weight_copies_rotated": copies,
+            "kernels": "query path, cache append, absorb, decode, merge + W_UV, W_O (one stream)",
+            "timing": "HIP events on the launch stream around graph replays of back-to-back layers"}
+
+
 def cpu_baseline(inp, budget_s):
     """The float64 oracle, as it stands, on whole sequences of the same
     workload until about `budget_s` seconds of CPU work have run."""
@@ -531,6 +622,7 @@ def main():
         if inp.dtype == "bf16" and inp.name == "dsv2_b32_l4096":
             result["multi_token"] = multi_token_time(pipe, caches, stream)
             result["prefill"] = prefill_time(pipe, stream)
+            result["layer"] = layer_time(inp, pipe, caches, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

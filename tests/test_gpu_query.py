@@ -89,6 +89,20 @@ def test_query_path_against_oracle(B, yarn, gain):
     _check(qr.double().cpu().numpy(), ref_r, absb=3e-2 * np.abs(ref_r).max())
 
 
+def test_query_path_contraction_tails():
+    # a hidden size that is not a multiple of the W_DQ product's 1024-wide
+    # contraction parts, and a d'_c whose quarter is not a multiple of the
+    # second product's 192-wide wave steps: both products take the instances
+    # that zero the operands past the contraction's end
+    import dataclasses
+    d = dataclasses.replace(DSV2, hidden=4144)
+    inp = make_query_inputs(d, batch=37, seed=9, d_qlatent=1280, with_gain=True)
+    qn, qr = _gpu_query(inp, False)
+    _, ref_n, ref_r = _oracle_query(inp, False)
+    _check(qn.double().cpu().numpy(), ref_n, absb=3e-2 * np.abs(ref_n).max())
+    _check(qr.double().cpu().numpy(), ref_r, absb=3e-2 * np.abs(ref_r).max())
+
+
 def test_query_rotation_positions_zero_and_wrap():
     # position 0 leaves the rotary query unrotated: equal to the same inputs
     # with YaRN frequencies (frequencies do not matter at 0); a large position
