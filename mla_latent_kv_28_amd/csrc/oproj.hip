@@ -71,7 +71,7 @@ __global__ __launch_bounds__(128) void oproj_f32(OProjParams p) {
 
 }  // namespace
 
-// bf16: n a multiple of 32, k a multiple of kOpSlice.
+// bf16: n a multiple of 32, k a multiple of 1024.
 bool oproj_bf16_shape_ok(int n, int k) { return n % 32 == 0 && k % 1024 == 0; }
 
 // Workspace: the parts' fp32 partial sums.

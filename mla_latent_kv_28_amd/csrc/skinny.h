@@ -14,8 +14,8 @@
 //    at k + 8 g). A wave's LDS operations run in order, so the buffer needs
 //    no barrier, and one buffer serves every macro step.
 //  - Activations: either fragment-major (one 1 KiB load per k step and batch
-//    half, laid out by frag_offset below) or plain row-major (16 rows x 64
-//    bytes per load).
+//    half, laid out by frag_offset below) or row-major, read like the
+//    weights into a second region of the wave's buffer.
 // The loads of the next D macro steps are in flight while one is multiplied.
 // The waves' 2 NA 16x16 tiles are added through LDS in wave order
 // (deterministic) and handed to the epilogue: lane (g, c) of tile (na, bb)
@@ -30,14 +30,15 @@
 namespace mla {
 namespace {
 
-// Activation layouts of skinny_gemm: row-major read straight into fragments
-// (16 rows x 64 bytes a load), fragment-major (frag_offset; one 1 KiB load a
-// fragment), or row-major read like the weights (8 rows x 128 bytes a load)
-// and put into fragment order through the wave's LDS buffer.
-constexpr int kXRow = 0, kXFrag = 1, kXRowLds = 2;
+// Activation layouts of skinny_gemm: fragment-major (frag_offset; one 1 KiB
+// load a fragment), or row-major read like the weights (8 rows x 128 bytes a
+// load) and put into fragment order through the wave's LDS buffer. (Row-major
+// activations read straight into fragments, 16 rows x 64 bytes a load, cost
+// far more than their bytes when the rows lie far apart.)
+constexpr int kXFrag = 1, kXRowLds = 2;
 
 struct SkParams {
-  const void* x;       // kXFrag: fragment-major (frag_offset); else row-major [M][ldx]
+  const void* x;       // kXFrag: fragment-major (frag_offset); kXRowLds: row-major [M][ldx]
   const void* w0;      // weight rows [0, n0), [n0][K] row-major
   const void* w1;      // weight rows [n0, N)
   int32_t ldx;         // row-major activations: elements per row
@@ -98,25 +99,19 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_gemm(SkParams g, EPI epi) {
   // weight load i of a macro step: rows 8 i + lane / 8, piece lane % 8
   const uint32_t wv = (uint32_t)((lane >> 3) * g.K * 2 + 16 * (lane & 7));
   MLA_LDS char* wl = (MLA_LDS char*)wbuf[wave];
+  static_assert(XL == kXFrag || XL == kXRowLds, "activation layout");
   __amdgpu_buffer_rsrc_t xres;
-  uint32_t xv0, xv1, xvr[4];
+  uint32_t xv0 = 0, xvr[4] = {};
   if constexpr (XL == kXFrag) {
     xres = buffer_rsrc(g.x, (uint32_t)((int64_t)(g.M + 31) / 32 * 32 * g.K * 2));
-    xv0 = (uint32_t)(rb * (g.K / 32) * 2048 + 16 * lane);
-    xv1 = xv0 + 1024;
-  } else if constexpr (XL == kXRowLds) {
+    xv0 = (uint32_t)(rb * (g.K / 32) * 2048 + 16 * lane);   // batch half 1: + 1024
+  } else {
     // like the weights: load i reads row 8 i + lane / 8 of the row block
     // (clamped to the batch; rows past it are not stored), piece lane % 8
     xres = buffer_rsrc(g.x, (uint32_t)((int64_t)g.M * g.ldx * 2));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       xvr[i] = (uint32_t)(min(32 * rb + 8 * i + (lane >> 3), g.M - 1) * g.ldx * 2 + 16 * (lane & 7));
-    xv0 = xv1 = 0;
-  } else {
-    const int r0 = min(32 * rb + c, g.M - 1), r1 = min(32 * rb + 16 + c, g.M - 1);
-    xres = buffer_rsrc(g.x, (uint32_t)((int64_t)g.M * g.ldx * 2));
-    xv0 = (uint32_t)(r0 * g.ldx * 2 + 16 * grp);
-    xv1 = (uint32_t)(r1 * g.ldx * 2 + 16 * grp);
   }
   const int kbeg = kpart * (g.kw * WAVES) + wave * g.kw;
   const int nm = g.kw / 64;   // macro steps, a multiple of D
@@ -132,9 +127,9 @@ __global__ __launch_bounds__(64 * WAVES) void skinny_gemm(SkParams g, EPI epi) {
     } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const uint32_t xs = XL == kXFrag ? (uint32_t)((k / 32 + t) * 2048) : (uint32_t)(2 * (k + 32 * t));
+        const uint32_t xs = (uint32_t)((k / 32 + t) * 2048);
         xb[j][t][0] = load_b128(xres, xv0, xs);
-        xb[j][t][1] = load_b128(xres, xv1, xs);
+        xb[j][t][1] = load_b128(xres, xv0 + 1024, xs);
       }
     }
   };
