@@ -332,8 +332,10 @@ mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const
  *               writes nothing for that sequence.
  *   workspace   device memory of at least mla_cache_append_workspace() bytes,
  *               16-byte aligned, owned by the caller (fp32 partial sums).
- * Products accumulate in fp32, the norm and rotation run in fp32 (angles in
- * fp64). hidden a multiple of 16 (bf16) or 4 (f32). batch == 0 is a no-op.
+ * Products accumulate in fp32 (bf16: 1024-wide parts of the hidden size, each
+ * the in-order sum of four 256-wide ranges, the parts added in order; f32:
+ * 256-wide slices added in order), the norm and rotation run in fp32 (angles
+ * in fp64). hidden a multiple of 16 (bf16) or 4 (f32). batch == 0 is a no-op.
  * Errors as for mla_decode; MLA_ERR_SHAPE also for a short workspace.
  */
 int64_t mla_cache_append_workspace(const mla_dims* dims, int32_t batch, int32_t hidden);
@@ -349,7 +351,7 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t batch, int32_t hidden,
  * forbid allocation): the fp32 partial sums go to a scratch array inside the
  * library instead, one copy on each GPU it runs on, 8 MiB, held until the
  * process ends. The call allocates nothing. Limit:
- * mla_cache_append_workspace(dims, batch, hidden) <= 8 MiB (batch up to 182
+ * mla_cache_append_workspace(dims, batch, hidden) <= 8 MiB (batch up to 728
  * at hidden 5120 with the DeepSeek-V2 shape); beyond it the call returns
  * MLA_ERR_UNSUPPORTED and enqueues nothing. Every call on one GPU uses that
  * GPU's array, so calls that can run at the same time on one GPU (on

@@ -9,11 +9,13 @@
 // YaRN, section 3.1.4) computed on the host.
 //
 // Two kernels:
-//  1. append_project: [B, d] x [d, d_c + d_R] in K slices of 256 into fp32
-//     partial sums work[slice][b][n] (bf16: one wave per 32 x 32 output tile
-//     and slice, MFMA 32x32x16 with operands loaded straight from memory;
-//     fp32: one thread per output column, plain fma). The weights are read
-//     once per 32 batch rows; they dominate the bytes.
+//  1. the projection [B, d] x [d, d_c + d_R] into fp32 partial sums
+//     work[part][b][n]: bf16, skinny_gemm (skinny.h) over [W_DKV; W_KR] in
+//     1024-wide contraction parts (four waves of 256 each, weights and hidden
+//     states in 128-byte row pieces through each wave's LDS buffer); fp32
+//     (tiny shape), append_project_f32 in 256-wide slices, one thread per
+//     output column, plain fma. The weights are read once per 32 batch rows;
+//     they dominate the bytes.
 //  2. append_finish: one workgroup per sequence sums the slices in a fixed
 //     order, applies the norm and the rotation in fp32 (angles in fp64), and
 //     writes the row
@@ -26,46 +28,17 @@
 
 #include "mla_device.h"
 #include "mla_internal.h"
+#include "skinny.h"
 
 namespace mla {
 namespace {
 
-constexpr int kSlice = 256;   // hidden features per partial sum
+constexpr int kSlice = 256;   // hidden features per partial sum (fp32 projection)
+constexpr int kApWaves = 4, kApDepth = 4, kApKw = 256;   // bf16 projection: 1024-wide parts
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 // ---- 1. projection -------------------------------------------------------------
-
-__global__ __launch_bounds__(64) void append_project_bf16(AppendParams p) {
-  const int lane = threadIdx.x, r = lane & 31, half = lane >> 5;
-  const int N = p.d_latent + p.d_rope;
-  const int n = blockIdx.x * 32 + r;                    // output column of this lane's B operand
-  const int m = blockIdx.z * 32 + r;                    // batch row of this lane's A operand
-  const int k0 = blockIdx.y * kSlice, k1 = min(k0 + kSlice, p.hidden);
-  const __bf16* w = n < p.d_latent ? (const __bf16*)p.w_dkv + (int64_t)n * p.hidden
-                                   : (const __bf16*)p.w_kr + (int64_t)(n - p.d_latent) * p.hidden;
-  const bool m_ok = m < p.batch;
-  const __bf16* h = (const __bf16*)p.h + (int64_t)(m_ok ? m : 0) * p.hidden;
-  f32x16 acc = {};
-  bf16x8 a[kSlice / 16], b[kSlice / 16];
-#pragma unroll
-  for (int s = 0; s < kSlice / 16; ++s) {               // every load first, then the products
-    const int k = k0 + 16 * s + 8 * half;
-    if (k0 + 16 * s < k1) {
-      a[s] = m_ok ? *(const bf16x8*)(h + k) : bf16x8{};
-      b[s] = *(const bf16x8*)(w + k);
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < kSlice / 16; ++s)
-    if (k0 + 16 * s < k1) acc = mfma32x32x16(a[s], b[s], acc);
-  float* out = p.work + (int64_t)blockIdx.y * p.batch * N;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = blockIdx.z * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (row < p.batch) out[(int64_t)row * N + n] = acc[i];
-  }
-}
 
 __global__ __launch_bounds__(64) void append_project_f32(AppendParams p) {
   const int N = p.d_latent + p.d_rope;
@@ -235,7 +208,10 @@ __global__ __launch_bounds__(64 * kFinishWaves) void append_finish(AppendParams 
 
 }  // namespace
 
-int append_slices(int hidden) { return (hidden + kSlice - 1) / kSlice; }
+int append_slices(int hidden, bool dsv2) {
+  const int part = dsv2 ? kApWaves * kApKw : kSlice;
+  return (hidden + part - 1) / part;
+}
 
 // Scratch of the allocation-free entry point: the fp32 partial sums that
 // mla_cache_append keeps in the caller's workspace, here in a device array of
@@ -280,8 +256,14 @@ hipError_t launch_cache_append(const AppendParams& p, bool dsv2, int cache_kind,
   const int N = p.d_latent + p.d_rope;
   hipError_t e;
   if (dsv2) {
-    e = launch_kernel_events(append_project_bf16, dim3(N / 32, p.ksplits, (p.batch + 31) / 32), dim3(64),
-                             stream, e0, nullptr, p);
+    const SkParams g{p.h, p.w_dkv, p.w_kr, p.hidden, p.d_latent, p.batch, N, p.hidden, kApKw, p.ksplits};
+    const EpiPartial ep{p.work, p.batch, N};
+    const dim3 grid(N / 32 * p.ksplits, (p.batch + 31) / 32), block(64 * kApWaves);
+    e = p.ksplits * kApWaves * kApKw != p.hidden
+            ? launch_kernel_events(skinny_gemm<kApWaves, kApDepth, 2, kXRowLds, true, EpiPartial>, grid, block,
+                                   stream, e0, nullptr, g, ep)
+            : launch_kernel_events(skinny_gemm<kApWaves, kApDepth, 2, kXRowLds, false, EpiPartial>, grid, block,
+                                   stream, e0, nullptr, g, ep);
     if (e != hipSuccess) return e;
     if (cache_kind == kFP8)
       return launch_kernel_events((append_finish<512, 64, kFP8>), dim3(p.batch), dim3(64 * kFinishWaves), stream,

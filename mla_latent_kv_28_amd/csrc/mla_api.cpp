@@ -365,7 +365,8 @@ mla_status mla_o_proj(const mla_dims* dims, int32_t batch, int32_t hidden, const
 
 int64_t mla_cache_append_workspace(const mla_dims* dims, int32_t batch, int32_t hidden) {
   if (dims == nullptr || batch <= 0 || hidden <= 0) return 0;
-  return static_cast<int64_t>(mla::append_slices(hidden)) * batch * (dims->d_latent + dims->d_rope) *
+  return static_cast<int64_t>(mla::append_slices(hidden, shape_of(dims) == Shape::kDsv2)) * batch *
+         (dims->d_latent + dims->d_rope) *
          static_cast<int64_t>(sizeof(float));
 }
 
@@ -432,7 +433,7 @@ mla_status cache_append_params(const mla_dims* dims, int32_t batch, int32_t hidd
   p.work = nullptr;
   p.batch = batch;
   p.hidden = hidden;
-  p.ksplits = mla::append_slices(hidden);
+  p.ksplits = mla::append_slices(hidden, sh == Shape::kDsv2);
   p.d_latent = dims->d_latent;
   p.d_rope = dims->d_rope;
   p.eps = rms_eps;

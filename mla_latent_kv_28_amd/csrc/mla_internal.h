@@ -107,7 +107,7 @@ struct AppendParams {
   float eps;
   double freq[kMaxRopePairs];   // rotation frequency of feature pair i (plain or YaRN)
 };
-int append_slices(int hidden);
+int append_slices(int hidden, bool dsv2);   // partial sums of the projection
 hipError_t launch_cache_append(const AppendParams& p, bool dsv2, int cache_kind, hipStream_t s);
 // The library's own per-GPU scratch for the allocation-free cache append.
 int64_t append_scratch_bytes();

@@ -217,7 +217,7 @@ def test_binding_refuses_host_tensors(L):
 def test_cache_append_argument_errors(L):
     d = ctypes.byref(DSV2)
     ws = mla.mla_cache_append_workspace(DSV2, 4, 5120)
-    assert ws == 20 * 4 * 576 * 4                     # 256-wide slices of the hidden size
+    assert ws == 5 * 4 * 576 * 4                      # 1024-wide contraction parts of the hidden size
 
     def f(dims=d, batch=4, hidden=5120, h=P, w1=P, w2=P, gain=None, dtype=mla.BF16, eps=1e-6, base=1e4,
           pos=P, cache=None, work=P, work_bytes=ws, rope=None):
@@ -266,8 +266,8 @@ def test_cache_append_noalloc_argument_errors(L):
     assert f(dtype=mla.F32) == -3
     assert f(h=None) == -1 and f(pos=None) == -1
     assert f(h=P + 2) == -5
-    assert f(batch=183) == -4                        # 183 x 20 x 576 x 4 bytes > 8 MiB
-    assert mla.mla_cache_append_workspace(DSV2, 182, 5120) <= (8 << 20)
+    assert f(batch=729) == -4                        # 729 x 5 x 576 x 4 bytes > 8 MiB
+    assert mla.mla_cache_append_workspace(DSV2, 728, 5120) <= (8 << 20)
     assert f(batch=0, h=None, w1=None, w2=None, pos=None) == 0
 
 

@@ -61,7 +61,7 @@ def test_noalloc_append_equals_workspace_append(kind):
 
 def test_noalloc_append_refuses_a_batch_beyond_the_scratch():
     import mla_latent_kv_28_amd as mla
-    B = 200                                        # 200 x 20 slices x 576 x 4 bytes > 8 MiB
+    B = 800                                        # 800 x 5 parts x 576 x 4 bytes > 8 MiB
     assert mla.mla_cache_append_workspace(DSV2, B, DSV2.hidden) > (8 << 20)
     inp = make_append_inputs(DSV2, batch=B, seed=3, max_position=4)
     store, cache = _cache(mla, DSV2, B, 4, "bf16")
