@@ -812,7 +812,9 @@ constexpr int kPvEarly = 0;
 // E4M3: the scores are fs (s_t lat + rope) (see QF8), with the tile's
 // per-token scales s_t in `scl` (token 8 w + i at float 64 w + i), and the
 // probabilities enter the latent sum times s_t once the denominator has taken
-// them. `scale_log2` is fs there.
+// them. `scale_log2` is fs there; fs >= 0, so the maximum is taken over the
+// unscaled scores and each probability is exp2(fma(score, fs, -m)), one
+// instruction fewer per score.
 template <class C, bool E4M3, class PS>
 __device__ __forceinline__ void softmax_pv_stream(PS& pvs, MLA_LDS char* __restrict__ pw, const Scores<C>& sc,
                                                   State<C>& s, int nvalid, float scale_log2, bool first,
@@ -837,7 +839,7 @@ __device__ __forceinline__ void softmax_pv_stream(PS& pvs, MLA_LDS char* __restr
       const f32x4 sg = sg_next;
       if (g < 3) sg_next = *(const MLA_LDS f32x4*)(scl + 64 * (g + 1) + 4 * hh);
 #pragma unroll
-      for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = __builtin_fmaf(sc.lat[i], sg[i - 4 * g], sc.rope[i]) * scale_log2;
+      for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = __builtin_fmaf(sc.lat[i], sg[i - 4 * g], sc.rope[i]);
     } else {
 #pragma unroll
       for (int i = 4 * g; i < 4 * g + 4; ++i) x[i] = sc.lat[i] * scale_log2;
@@ -858,7 +860,9 @@ __device__ __forceinline__ void softmax_pv_stream(PS& pvs, MLA_LDS char* __restr
   for (int k = 0; k < 4; ++k) a[k] = fmaxf(a[2 * k], a[2 * k + 1]);
   sync();
   mfma(7);
-  const float mt = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+  // e4m3: the maximum of the unscaled scores times fs >= 0 (see split_query_f8)
+  const float mt = E4M3 ? fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])) * scale_log2
+                       : fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
   sync();
   mfma(8);
   const float m_first = fmaxf(mt, lane32_partner(mt));
@@ -872,8 +876,9 @@ __device__ __forceinline__ void softmax_pv_stream(PS& pvs, MLA_LDS char* __restr
   for (int g = 0; g < 8; ++g) {
     mfma(9 + g);
     if (E4M3 && g == 6) sj_next = *(const MLA_LDS f32x4*)(scl + 4 * hh);
-    pv[2 * g] = fast_exp2(x[2 * g] - s.m_ref);
-    pv[2 * g + 1] = fast_exp2(x[2 * g + 1] - s.m_ref);
+    pv[2 * g] = E4M3 ? fast_exp2(__builtin_fmaf(x[2 * g], scale_log2, -s.m_ref)) : fast_exp2(x[2 * g] - s.m_ref);
+    pv[2 * g + 1] = E4M3 ? fast_exp2(__builtin_fmaf(x[2 * g + 1], scale_log2, -s.m_ref))
+                         : fast_exp2(x[2 * g + 1] - s.m_ref);
     sync();
   }
   if (nvalid < C::T) {    // partial tile (uniform): tokens past the end weigh nothing
@@ -1130,7 +1135,7 @@ __device__ __forceinline__ bf16x8 pv_operand_f8(const MLA_LDS char* buf, const L
 // the head's largest; smaller ones round to e4m3's subnormal spacing). The
 // rotary part stays bf16, times 2^-e, so that the scaled score of token t is
 // fs (s_t (hi + 2^-4 lo) . codes + 2^-e q_R . k_R) with one factor fs = 2^e
-// scale log2(e) per lane.
+// |scale| log2(e) per lane (a negative scale negates the query instead).
 template <class C>
 struct QF8 {
   i32x8 hi[C::DC / 64], lo[C::DC / 64];   // block b: lane (g, n) holds k = 64 b + 32 g .. + 31 of head n
@@ -1207,12 +1212,15 @@ __device__ __forceinline__ void split_query_f8(QF8<C>& q, const QRaw<C>& raw, fl
   m = max(m, (uint32_t)__shfl_xor((int)m, 32));   // lanes n and n + 32 hold one head
   // largest / 2^e in [128, 256): e = exponent(largest) - 7
   const int e = max((int)(m >> 7) - 134, -120);
+  // a negative softmax scale is carried by the query (every sign flipped), so
+  // that fs = 2^e |scale| log2 e is never negative
+  const uint32_t flip = scale_log2 < 0.0f ? 0x80008000u : 0u;
   const float sh = pow2i(e), sl = pow2i(e - 4), inv = pow2i(-e);
 #pragma unroll
   for (int b = 0; b < C::DC / 64; ++b) {
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      const uint32_t w0 = raw.v[b][d >> 1][2 * (d & 1)], w1 = raw.v[b][d >> 1][2 * (d & 1) + 1];
+      const uint32_t w0 = raw.v[b][d >> 1][2 * (d & 1)] ^ flip, w1 = raw.v[b][d >> 1][2 * (d & 1) + 1] ^ flip;
       const float x0 = __builtin_bit_cast(float, w0 << 16), x1 = __builtin_bit_cast(float, w0 & 0xffff0000u);
       const float x2 = __builtin_bit_cast(float, w1 << 16), x3 = __builtin_bit_cast(float, w1 & 0xffff0000u);
       i16x2v h = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2v{0, 0}, x0, x1, sh, false);
@@ -1228,14 +1236,14 @@ __device__ __forceinline__ void split_query_f8(QF8<C>& q, const QRaw<C>& raw, fl
   }
 #pragma unroll
   for (int kk = 0; kk < C::NKC_ROPE; ++kk) {
-    const u32x4 w = __builtin_bit_cast(u32x4, raw.rope[kk]);
+    const u32x4 w = __builtin_bit_cast(u32x4, raw.rope[kk]) ^ flip;
     u32x4 o;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
       o[d] = pack_bf16x2(bf16_bits_to_f32(w[d] & 0xffffu) * inv, bf16_bits_to_f32(w[d] >> 16) * inv);
     *(MLA_LDS u32x4*)(qrope + (kk * 64 + (threadIdx.x & 63)) * 16) = o;
   }
-  q.fs = sh * scale_log2;
+  q.fs = sh * fabsf(scale_log2);
 }
 
 struct NoF8Ring {   // stands in where no e4m3 ring is used

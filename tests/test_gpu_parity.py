@@ -353,6 +353,23 @@ def test_dsv2_fp8_peaked_attention():
     _lse_check(lse, ref_lse, 5e-2)
 
 
+@pytest.mark.parametrize("factor", [-1.0, 0.0])
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "fp8_paged"])
+def test_decode_non_positive_scale(kind, factor):
+    # any finite softmax scale: a negated one reverses the ranking of the
+    # tokens (the contiguous e4m3 loop carries its sign on the split query),
+    # zero weighs every visible token the same
+    import dataclasses
+    name = "dsv2_b32_l4096" if kind == "bf16" else "fp8_b128_l8192"
+    extra = dict(layout="paged", page_size=64) if kind == "fp8_paged" else {}
+    inp = make_inputs(name, seq_lens=[700, 97, 1, 300], pad_fill=float("nan"), q_scale=4.0, **extra)
+    inp = dataclasses.replace(inp, sm_scale=factor * inp.sm_scale)
+    _, out, lse = _run(inp, num_splits=2)
+    ref, ref_lse = oracle.decode(**oracle_args(inp))
+    _check(out, ref, BF16_REL, BF16_ABS)
+    _lse_check(lse, ref_lse, 2e-2)
+
+
 @pytest.mark.parametrize("page_size", [16, 64])
 def test_dsv2_fp8_paged(page_size):
     # paged e4m3 runs the per-row loader (codes staged in registers)
