@@ -606,7 +606,8 @@ def main():
             "frac_of_measured": round(gbps_dec / probe_gbps, 4),
             "achievable_read_probe": "mla_read_probe: streaming 16-byte nontemporal loads over a 1 GiB buffer, "
                                      "20 back-to-back launches between two events",
-            "traffic": hbm_traffic(inp.name) if S == 8 else None,
+            # the byte-counter profiles run each workload at the library's split count
+            "traffic": hbm_traffic(inp.name) if not args.splits else None,
             "us_per_launch": round(ms_dec * 1e3, 3),
             "us_per_launch_p10_p50_p90": [round(dec_pct[q] * 1e3, 3) for q in (10, 50, 90)],
             "timing": "event pair carried by each decode launch (hipExtLaunchKernel) within whole steps",
