@@ -153,7 +153,8 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch,
  *   seq_lens [B] int32 device array; a length outside [0, max_seq_len] is
  *            clamped to that range.
  *   sm_scale multiplies q_lat·row before the softmax (1/sqrt(d_nope + d_rope)
- *            times any length-extension factor).
+ *            times any length-extension factor). Any finite value is taken,
+ *            zero and negative ones included (MLA_ERR_SHAPE otherwise).
  *   num_splits S >= 1 cuts the token range [0, max_seq_len) into S chunks
  *            of mla_split_chunk(max_seq_len, S) tokens; each (b, split) is
  *            computed independently (by one workgroup; when there are more
